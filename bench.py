@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet core on one MI355X.
+
+One step = one chunked-prefill call (front end + chunked rule + final state)
+over the Qwen3.6-27B-shaped layer: B=1, L=16384 tokens, 16 key / 48 value
+heads, head dims 128, chunk 64, bf16 io, fp32 state, synthetic seeded inputs
+resident in HBM.  ``value`` is prefill tokens/s.  The same run also times the
+one-token decode step of the Qwen3.6-27B-shaped decode workload (B=32, 256
+consecutive steps, state ~N(0, 0.05)) and reports its HBM bandwidth, and
+times the fp64 CPU oracle on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s (MFMA % peak) + decode step HBM GB/s (% peak), 1 GPU"
+BF16_PEAK_FLOPS = 2516.6e12      # MI355X dense bf16 MFMA (4096 FLOP/clk/CU x 256 CU x 2.4 GHz)
+HBM_PEAK_BYTES = 8.0e12          # MI355X HBM3E
+
+
+def prefill_flops_per_token_head(C=64, d=128) -> float:
+    """Algorithmic FLOPs of the chunked rule per token per value head with the
+    triangular products at their exact size: K K^T strictly lower, Q K^T, the
+    two T-products and P.Delta lower-inclusive, three C x d x d products
+    (W S, Q S, K^T Delta) and the C^3/3 triangular solve."""
+    return (C * (C - 1) * d + 4 * C * (C + 1) * d + 6 * C * d * d + C ** 3 / 3) / C
+
+
+def prefill_bytes(B, L, Hk, Hv, d=128) -> int:
+    """Fused-path HBM floor: read qkv, a, b, write o, read/write the state."""
+    conv_dim = 2 * Hk * d + Hv * d
+    return B * L * (conv_dim * 2 + Hv * 2 * 2 + Hv * d * 2) + 2 * B * Hv * d * d * 4
+
+
+def decode_bytes(B, Hk, Hv, d=128) -> int:
+    """Per decode step: state read + write, qkv, conv state in + out, o, a, b,
+    conv taps, A_log and dt_bias."""
+    conv_dim = 2 * Hk * d + Hv * d
+    return (2 * B * Hv * d * d * 4 + B * conv_dim * 2 + 2 * B * conv_dim * 3 * 2 + B * Hv * d * 2
+            + 2 * B * Hv * 2 + conv_dim * 4 * 2 + 2 * Hv * 4)
+
+
+def time_events(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / steps   # seconds per call
+
+
+def bench_prefill(args):
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[2]
+    inp = I.generate(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    out = torch.empty(w.batch, w.seq_len, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    conv = torch.empty(w.batch, w.conv_dim, 3, dtype=torch.bfloat16, device="cuda")
+    S = torch.empty(w.batch, w.num_v_heads, 128, 128, device="cuda")
+
+    def step():
+        gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"],
+                            None, None, out=out, conv_state_out=conv, rec_state_out=S)
+
+    torch.cuda.synchronize()
+    t = time_events(step, args.steps, args.warmup)
+    tokens = w.batch * w.seq_len
+    flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
+    byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads)
+    return w, t, tokens, flops, byts, inp
+
+
+def bench_decode(args):
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[1]
+    inp = I.generate(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    S = d["rec_state"].clone()
+    cs = [d["conv_state"].clone(), torch.empty_like(d["conv_state"])]
+    out = torch.empty(w.batch, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    n = w.decode_steps
+    state = {"i": 0}
+
+    def step():
+        i = state["i"]
+        s = i % n
+        gdn.decode_step(cfg, d["dec_qkv"][s], d["dec_a"][s], d["dec_b"][s], d["conv_w"],
+                        d["A_log"], d["dt_bias"], cs[i % 2], S, out=out,
+                        conv_state_out=cs[(i + 1) % 2], rec_state_out=S)
+        state["i"] = i + 1
+
+    t = time_events(step, n, args.warmup * 8)
+    return w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads)
+
+
+def cpu_baseline(inp, tokens):
+    from linear_attention_recurrence_causal_amd import inputs as I
+    from oracle import oracle as O
+    from tests.helpers import oracle_prefill
+    w = I.WORKLOADS[2]
+    O.build()
+    sl = slice(0, tokens)
+    t0 = time.perf_counter()
+    oracle_prefill(w, inp, seq_slice=sl)
+    dt = time.perf_counter() - t0
+    return {"value": tokens * w.batch / dt, "unit": "tokens/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle (front end + per-token rule), first {tokens} tokens of the "
+                      f"B=1 L={w.seq_len} 16/48-head prefill, all 48 heads, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the GDN core shards by (sequence, head) with no "
+              "communication, so a multi-GPU figure is N independent copies of this one; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    print("bench: prefill", file=sys.stderr, flush=True)
+    w, t, tokens, flops, byts, inp = bench_prefill(args)
+    achieved = flops / t
+    rec = {
+        "metric": METRIC,
+        "value": tokens / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill", "batch": w.batch,
+                   "seq_len": w.seq_len, "num_k_heads": w.num_k_heads,
+                   "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk": 64,
+                   "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_FLOPS, "traffic": None,
+                     "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
+                     "hbm_floor_frac": byts / t / HBM_PEAK_BYTES},
+    }
+    if not args.no_decode:
+        print("bench: decode", file=sys.stderr, flush=True)
+        wd, td, bd = bench_decode(args)
+        rec["decode"] = {
+            "workload": "Qwen3.6-27B-shaped GDN layer decode step, B=32, 256 consecutive steps",
+            "us_per_step": td * 1e6, "tokens_per_s": wd.batch / td, "bytes_per_step": bd,
+            "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": bd / td / 1e9,
+                         "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
+                         "frac": bd / td / HBM_PEAK_BYTES, "traffic": None},
+        }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    rec["gpu"] = torch.cuda.get_device_name(0)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

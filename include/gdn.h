@@ -1,0 +1,164 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet core library (libgdn.so).
+ *
+ * The operation ("the GDN core") is the per-head gated delta rule with its
+ * front end, as stated on the cortex commit page "feat(stage-8c):
+ * linear-attention layer (Qwen3-Next GatedDeltaNet)":
+ *   - "Block": depthwise causal Conv1d (kernel 4) over the packed projected
+ *     q|k|v stream, prepending the carried conv state; SiLU; split into
+ *     heads; L2 normalisation of q and k.
+ *   - "Discretisation": g = -exp(A_log) * softplus(a + dt_bias) and
+ *     beta = sigmoid(b), both in fp32.
+ *   - "Delta rule": per token, S <- exp(g) S; kv = S^T k; delta = beta (v - kv);
+ *     S <- S + k delta^T; o = S^T q (with the updated S).
+ *   - "State": the carried conv tail and the d_k x d_v recurrent state per
+ *     value head; a new request starts from cleared (zero) state.
+ *   - "Performance note": prefill evaluates the same rule in chunks of 64.
+ * Checkpoints of the recurrent and conv state at fixed positions make a
+ * prefix resumable ("Add Qwen3.6-27B hybrid DeltaNet/GQA contrib model and
+ * vLLM serving path", "Summary" and "Why this is larger than a normal
+ * contrib model").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is caller-owned device memory (HIP, the current
+ *     device) unless marked "host".  The library never allocates, frees or
+ *     synchronises; it enqueues kernels on `stream` (a hipStream_t, NULL =
+ *     the null stream) and returns.  It keeps no global mutable state.
+ *   - Arguments are validated before anything is enqueued.  On an error
+ *     nothing is enqueued and no output is touched.  No C++ exception crosses
+ *     this boundary.
+ *   - Tensors are dense, row-major, with the shapes given below.  Every
+ *     pointer needs the alignment of its element type; in addition qkv and
+ *     out of gdn_prefill_chunked and both recurrent states of gdn_decode_step
+ *     must be 16-byte aligned, and ckpt_buf 256-byte aligned.
+ *   - Packed channel order (conv_dim = 2*H_k*d_k + H_v*d_v): all q channels
+ *     (key head major), then all k channels, then all v channels (value head
+ *     major).  conv_w rows follow the same order.
+ *   - Value head h reads key head h / (H_v / H_k) (repeat-interleave).
+ *   - io dtype (qkv, a, b, conv_w, conv_state, out): GDN_F32 or GDN_BF16.
+ *     A_log, dt_bias and the recurrent state are always fp32.
+ *   - conv_state [B, conv_dim, K-1]: per channel the last K-1 pre-conv inputs,
+ *     oldest first.  (The cortex state keeps K columns; its oldest is never
+ *     read by a width-K causal conv of the next token, so K-1 are stored.)
+ *   - rec_state [B, H_v, d_k, d_v] fp32, d_v contiguous.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gdn_status;
+enum {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,       /* null / misaligned pointer, bad size or config   */
+    GDN_EUNSUPPORTED = 2, /* valid but no kernel for this shape / dtype      */
+    GDN_EALIAS = 3,       /* forbidden overlap between an output and input   */
+    GDN_ESPACE = 4,       /* checkpoint buffer / entry array / workspace too small */
+    GDN_EHIP = 5          /* the HIP runtime reported a launch error         */
+};
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Layer shape and numerics.  Supported today: conv_kernel 4, chunk 64;
+ * prefill: d_k = d_v = 128, io GDN_BF16; decode: d_k, d_v in {32, 64, 128},
+ * io GDN_F32 or GDN_BF16. */
+typedef struct gdn_config {
+    int32_t batch;        /* B >= 0                                          */
+    int32_t num_k_heads;  /* H_k >= 1                                        */
+    int32_t num_v_heads;  /* H_v, a positive multiple of H_k                 */
+    int32_t head_k_dim;   /* d_k                                             */
+    int32_t head_v_dim;   /* d_v                                             */
+    int32_t conv_kernel;  /* K                                               */
+    int32_t chunk;        /* prefill chunk length C                          */
+    int32_t io_dtype;     /* gdn_dtype                                       */
+    float q_scale;        /* factor on the unit-norm query; 1 = the pages' rule */
+    float l2_eps;         /* epsilon in x * (sum x^2 + eps)^(-1/2), >= 0      */
+} gdn_config;
+
+/* One emitted checkpoint slot.  Slot j holds the state after absolute
+ * position (j+1)*interval; its conv tail sits at ckpt_buf + conv_offset
+ * ([B, conv_dim, K-1], io dtype) and its recurrent state at ckpt_buf +
+ * rec_offset ([B, H_v, d_k, d_v], fp32). */
+typedef struct gdn_ckpt_entry {
+    int64_t slot;
+    int64_t position;
+    uint64_t conv_offset;
+    uint64_t rec_offset;
+} gdn_ckpt_entry;
+
+/* Checkpoint plan of a prefill call (host only, touches no device).
+ *   The call covers absolute positions [start_pos, start_pos + seq_len); it
+ *   emits slot j for every position p = (j+1)*interval in
+ *   (start_pos, start_pos + seq_len].  slot_bytes = align256(B*conv_dim*(K-1)*
+ *   io_size) + align256(B*H_v*d_k*d_v*4); conv_offset = slot*slot_bytes;
+ *   rec_offset = conv_offset + align256(B*conv_dim*(K-1)*io_size).
+ *   *count      (host, required): slots emitted.
+ *   *buffer_bytes (host, required): bytes a ckpt_buf needs for this call,
+ *                 (last emitted slot + 1) * slot_bytes, 0 if none.
+ *   entries     (host, nullable): filled with up to `capacity` entries.
+ * Errors: GDN_EINVAL (bad config, start_pos/seq_len < 0, interval < 0 or not
+ * a multiple of cfg->chunk, null count/buffer_bytes); GDN_ESPACE when
+ * entries != NULL and capacity < *count (count and bytes are still set). */
+gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_t seq_len,
+                                int64_t interval, gdn_ckpt_entry* entries, int64_t capacity,
+                                int64_t* count, uint64_t* buffer_bytes);
+
+/* Workspace a prefill call needs (host only).  Currently always 0: the
+ * prefill is one fused kernel that keeps every intermediate on chip. */
+gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, uint64_t* bytes);
+
+/* Chunked prefill of seq_len tokens per sequence ("Performance note":
+ * chunk 64; the result is that of the per-token rule up to rounding).
+ *   qkv           [B, L, conv_dim] io        pre-conv projected stream
+ *   a, b          [B, L, H_v] io             gate inputs
+ *   conv_w        [conv_dim, K] io           depthwise taps; tap K-1 weights
+ *                                            the current token
+ *   A_log, dt_bias [H_v] fp32
+ *   conv_state_in [B, conv_dim, K-1] io, or NULL for a new request (zeros)
+ *   conv_state_out [B, conv_dim, K-1] io     must not overlap conv_state_in
+ *   rec_state_in  [B, H_v, d_k, d_v] fp32, or NULL for zeros
+ *   rec_state_out [B, H_v, d_k, d_v] fp32    may equal rec_state_in exactly
+ *   out           [B, L, H_v, d_v] io
+ *   start_pos     absolute position of the first token; chunk boundaries
+ *                 sit at absolute multiples of `chunk`, so a call resumed at
+ *                 a checkpoint repeats the uninterrupted call bit for bit
+ *   ckpt_buf, ckpt_buf_bytes, ckpt_interval: see gdn_state_checkpoint;
+ *                 interval 0 = none (ckpt_buf may then be NULL)
+ *   workspace, workspace_bytes: at least gdn_prefill_workspace_bytes (NULL ok
+ *                 when that is 0)
+ * With seq_len == 0 only the states are copied (qkv, a, b, out may be NULL).
+ * The conv+SiLU output is rounded to the io dtype before the L2 norm, as the
+ * stream it comes from is stored in that dtype. */
+gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                               const void* qkv, const void* a, const void* b, const void* conv_w,
+                               const float* A_log, const float* dt_bias,
+                               const void* conv_state_in, void* conv_state_out,
+                               const float* rec_state_in, float* rec_state_out, void* out,
+                               void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                               void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* One recurrent decode step: one new token per sequence ("Delta rule").
+ *   qkv [B, conv_dim], a, b [B, H_v], out [B, H_v, d_v] (io dtype); the
+ *   other arguments as in gdn_prefill_chunked.  conv_state_out must not
+ *   overlap conv_state_in; rec_state_out may equal rec_state_in exactly. */
+gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a, const void* b,
+                           const void* conv_w, const float* A_log, const float* dt_bias,
+                           const void* conv_state_in, void* conv_state_out,
+                           const float* rec_state_in, float* rec_state_out, void* out,
+                           void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

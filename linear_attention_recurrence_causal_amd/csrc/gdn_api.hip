@@ -1,0 +1,265 @@
+// gdn_api.hip -- the C ABI of libgdn: validation, checkpoint plan, dispatch.
+//
+// Every entry point validates all arguments before it enqueues anything, so
+// an error leaves every output untouched.  No allocation, no synchronisation,
+// no global mutable state.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "gdn_launch.h"
+#include "../../include/gdn.h"
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int io_size(int32_t io) { return io == GDN_BF16 ? 2 : 4; }
+
+// Config checks shared by every entry point (shape sanity only; support for
+// a particular shape is checked per path).
+gdn_status check_config(const gdn_config* c) {
+    if (!c) return GDN_EINVAL;
+    if (c->batch < 0 || c->num_k_heads < 1 || c->num_v_heads < 1) return GDN_EINVAL;
+    if (c->num_v_heads % c->num_k_heads != 0) return GDN_EINVAL;
+    if (c->head_k_dim < 1 || c->head_v_dim < 1 || c->conv_kernel < 1 || c->chunk < 1)
+        return GDN_EINVAL;
+    if (c->io_dtype != GDN_F32 && c->io_dtype != GDN_BF16) return GDN_EINVAL;
+    if (!std::isfinite(c->q_scale) || !std::isfinite(c->l2_eps) || c->l2_eps < 0.f) return GDN_EINVAL;
+    return GDN_OK;
+}
+
+int64_t conv_dim_of(const gdn_config* c) {
+    return 2 * (int64_t)c->num_k_heads * c->head_k_dim + (int64_t)c->num_v_heads * c->head_v_dim;
+}
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned_to(p, 16); }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+
+bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi && x.hi > x.lo && y.hi > y.lo; }
+
+struct Plan {
+    int64_t count = 0;
+    int64_t first_slot = 0;
+    uint64_t conv_bytes = 0;   // aligned conv part of a slot
+    uint64_t slot_bytes = 0;
+    uint64_t buffer_bytes = 0;
+};
+
+// The single source of checkpoint indices and offsets.
+Plan checkpoint_plan(const gdn_config* c, int64_t start_pos, int64_t seq_len, int64_t interval) {
+    Plan p;
+    p.conv_bytes = align_up((uint64_t)c->batch * conv_dim_of(c) * (c->conv_kernel - 1) * io_size(c->io_dtype));
+    const uint64_t rec_bytes = align_up((uint64_t)c->batch * c->num_v_heads * c->head_k_dim * c->head_v_dim * 4);
+    p.slot_bytes = p.conv_bytes + rec_bytes;
+    if (interval <= 0) return p;
+    p.first_slot = start_pos / interval;
+    const int64_t end_slot = (start_pos + seq_len) / interval;  // exclusive
+    p.count = end_slot - p.first_slot;
+    p.buffer_bytes = p.count > 0 ? (uint64_t)end_slot * p.slot_bytes : 0;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_EINVAL: return "invalid argument";
+        case GDN_EUNSUPPORTED: return "unsupported shape or dtype";
+        case GDN_EALIAS: return "output overlaps an input";
+        case GDN_ESPACE: return "buffer too small";
+        case GDN_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int32_t gdn_version(void) { return 100; }
+
+gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_t seq_len,
+                                int64_t interval, gdn_ckpt_entry* entries, int64_t capacity,
+                                int64_t* count, uint64_t* buffer_bytes) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (!count || !buffer_bytes || start_pos < 0 || seq_len < 0 || interval < 0) return GDN_EINVAL;
+    if (interval > 0 && interval % cfg->chunk != 0) return GDN_EINVAL;
+    if (entries && capacity < 0) return GDN_EINVAL;
+    const Plan p = checkpoint_plan(cfg, start_pos, seq_len, interval);
+    *count = p.count;
+    *buffer_bytes = p.buffer_bytes;
+    if (!entries) return GDN_OK;
+    const int64_t n = p.count < capacity ? p.count : capacity;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t slot = p.first_slot + i;
+        entries[i].slot = slot;
+        entries[i].position = (slot + 1) * interval;
+        entries[i].conv_offset = (uint64_t)slot * p.slot_bytes;
+        entries[i].rec_offset = entries[i].conv_offset + p.conv_bytes;
+    }
+    return capacity < p.count ? GDN_ESPACE : GDN_OK;
+}
+
+gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, uint64_t* bytes) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (!bytes || seq_len < 0) return GDN_EINVAL;
+    *bytes = 0;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                               const void* qkv, const void* a, const void* b, const void* conv_w,
+                               const float* A_log, const float* dt_bias,
+                               const void* conv_state_in, void* conv_state_out,
+                               const float* rec_state_in, float* rec_state_out, void* out,
+                               void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                               void* workspace, uint64_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (gdn_status s = check_config(cfg)) return s;
+    if (seq_len < 0 || start_pos < 0 || ckpt_interval < 0) return GDN_EINVAL;
+    if (ckpt_interval > 0 && ckpt_interval % cfg->chunk != 0) return GDN_EINVAL;
+    // qkv and out move in 16-byte vectors, ckpt_buf holds 256-byte aligned
+    // slots; everything else needs its element alignment.  With no tokens,
+    // qkv, a, b and out are never touched and may be NULL.
+    const uintptr_t ea = cfg->io_dtype == GDN_BF16 ? 2 : 4;
+    if (!conv_w || !aligned_to(conv_w, ea) || !conv_state_out || !aligned_to(conv_state_out, ea))
+        return GDN_EINVAL;
+    if (!A_log || !dt_bias || !rec_state_out || !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4) ||
+        !aligned_to(rec_state_out, 4))
+        return GDN_EINVAL;
+    if (seq_len > 0 && (!qkv || !a || !b || !out)) return GDN_EINVAL;
+    if (!aligned16(qkv) || !aligned16(out) || !aligned_to(a, ea) || !aligned_to(b, ea)) return GDN_EINVAL;
+    if (!aligned_to(conv_state_in, ea) || !aligned_to(rec_state_in, 4) || !aligned_to(ckpt_buf, 256))
+        return GDN_EINVAL;
+    if (!gdn::prefill_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype, cfg->conv_kernel,
+                                cfg->chunk))
+        return GDN_EUNSUPPORTED;
+
+    const int64_t B = cfg->batch, L = seq_len, Hv = cfg->num_v_heads;
+    const int64_t cd = conv_dim_of(cfg);
+    const int ios = io_size(cfg->io_dtype);
+    const uint64_t conv_state_bytes = (uint64_t)B * cd * (cfg->conv_kernel - 1) * ios;
+    const uint64_t rec_bytes = (uint64_t)B * Hv * cfg->head_k_dim * cfg->head_v_dim * 4;
+    const Range r_qkv = range_of(qkv, (uint64_t)B * L * cd * ios);
+    const Range r_cin = range_of(conv_state_in, conv_state_in ? conv_state_bytes : 0);
+    const Range r_cout = range_of(conv_state_out, conv_state_bytes);
+    const Range r_rin = range_of(rec_state_in, rec_state_in ? rec_bytes : 0);
+    const Range r_rout = range_of(rec_state_out, rec_bytes);
+    const Range r_out = range_of(out, (uint64_t)B * L * Hv * cfg->head_v_dim * ios);
+    if (overlap(r_cout, r_cin) || overlap(r_cout, r_qkv) || overlap(r_cout, r_out)) return GDN_EALIAS;
+    if (rec_state_in && rec_state_in != rec_state_out && overlap(r_rin, r_rout)) return GDN_EALIAS;
+    if (overlap(r_out, r_qkv) || overlap(r_out, r_rout) || overlap(r_out, r_cin) || overlap(r_out, r_rin))
+        return GDN_EALIAS;
+    if (overlap(r_rout, r_qkv) || overlap(r_rout, r_cout)) return GDN_EALIAS;
+
+    const Plan plan = checkpoint_plan(cfg, start_pos, seq_len, ckpt_interval);
+    if (plan.count > 0) {
+        if (!ckpt_buf) return GDN_EINVAL;
+        if (ckpt_buf_bytes < plan.buffer_bytes) return GDN_ESPACE;
+        const Range r_ck = range_of(ckpt_buf, plan.buffer_bytes);
+        if (overlap(r_ck, r_qkv) || overlap(r_ck, r_out) || overlap(r_ck, r_rout) || overlap(r_ck, r_cout) ||
+            overlap(r_ck, r_cin) || overlap(r_ck, r_rin))
+            return GDN_EALIAS;
+    }
+
+    gdn::PrefillParams p{};
+    p.qkv = qkv;
+    p.a = a;
+    p.b = b;
+    p.conv_w = conv_w;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.conv_in = conv_state_in;
+    p.conv_out = conv_state_out;
+    p.rec_in = rec_state_in;
+    p.rec_out = rec_state_out;
+    p.out = out;
+    p.ckpt_buf = plan.count > 0 ? static_cast<char*>(ckpt_buf) : nullptr;
+    p.slot_bytes = plan.slot_bytes;
+    p.conv_slot_bytes = plan.conv_bytes;
+    p.ckpt_interval = plan.count > 0 ? ckpt_interval : 0;
+    p.seq_len = L;
+    p.start_pos = start_pos;
+    p.conv_dim = cd;
+    p.batch = cfg->batch;
+    p.num_k_heads = cfg->num_k_heads;
+    p.num_v_heads = cfg->num_v_heads;
+    p.q_scale = cfg->q_scale;
+    p.l2_eps = cfg->l2_eps;
+    const hipError_t e = gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a, const void* b,
+                           const void* conv_w, const float* A_log, const float* dt_bias,
+                           const void* conv_state_in, void* conv_state_out,
+                           const float* rec_state_in, float* rec_state_out, void* out,
+                           void* stream) {
+    if (gdn_status s = check_config(cfg)) return s;
+    // the recurrent states move in 16-byte vectors; everything else needs its
+    // element alignment
+    const uintptr_t ea = cfg->io_dtype == GDN_BF16 ? 2 : 4;
+    for (const void* p : {qkv, a, b, conv_w, (const void*)conv_state_out, (const void*)out})
+        if (!p || !aligned_to(p, ea)) return GDN_EINVAL;
+    if (!A_log || !dt_bias || !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4)) return GDN_EINVAL;
+    if (!rec_state_out || !aligned16(rec_state_out) || !aligned16(rec_state_in) ||
+        !aligned_to(conv_state_in, ea))
+        return GDN_EINVAL;
+    if (cfg->conv_kernel != 4 || !gdn::decode_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype))
+        return GDN_EUNSUPPORTED;
+
+    const int64_t B = cfg->batch, Hv = cfg->num_v_heads;
+    const int64_t cd = conv_dim_of(cfg);
+    const int ios = io_size(cfg->io_dtype);
+    const uint64_t conv_state_bytes = (uint64_t)B * cd * 3 * ios;
+    const uint64_t rec_bytes = (uint64_t)B * Hv * cfg->head_k_dim * cfg->head_v_dim * 4;
+    const Range r_qkv = range_of(qkv, (uint64_t)B * cd * ios);
+    const Range r_cin = range_of(conv_state_in, conv_state_in ? conv_state_bytes : 0);
+    const Range r_cout = range_of(conv_state_out, conv_state_bytes);
+    const Range r_rin = range_of(rec_state_in, rec_state_in ? rec_bytes : 0);
+    const Range r_rout = range_of(rec_state_out, rec_bytes);
+    const Range r_out = range_of(out, (uint64_t)B * Hv * cfg->head_v_dim * ios);
+    if (overlap(r_cout, r_cin) || overlap(r_cout, r_qkv) || overlap(r_cout, r_out)) return GDN_EALIAS;
+    if (rec_state_in && rec_state_in != rec_state_out && overlap(r_rin, r_rout)) return GDN_EALIAS;
+    if (overlap(r_out, r_qkv) || overlap(r_out, r_rout) || overlap(r_out, r_cin) || overlap(r_out, r_rin))
+        return GDN_EALIAS;
+    if (overlap(r_rout, r_qkv) || overlap(r_rout, r_cout)) return GDN_EALIAS;
+
+    gdn::DecodeParams p{};
+    p.qkv = qkv;
+    p.a = a;
+    p.b = b;
+    p.conv_w = conv_w;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.conv_in = conv_state_in;
+    p.conv_out = conv_state_out;
+    p.rec_in = rec_state_in;
+    p.rec_out = rec_state_out;
+    p.out = out;
+    p.conv_dim = cd;
+    p.batch = cfg->batch;
+    p.num_k_heads = cfg->num_k_heads;
+    p.num_v_heads = cfg->num_v_heads;
+    p.head_k_dim = cfg->head_k_dim;
+    p.head_v_dim = cfg->head_v_dim;
+    p.io_dtype = cfg->io_dtype;
+    p.q_scale = cfg->q_scale;
+    p.l2_eps = cfg->l2_eps;
+    const hipError_t e = gdn::launch_decode_step(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// gdn_decode.hip -- one recurrent decode step of the Gated DeltaNet core (gfx950).
+//
+// Rule (cortex commit "feat(stage-8c): linear-attention layer (Qwen3-Next
+// GatedDeltaNet)", passages "Block", "Discretisation", "Delta rule"): for the
+// new token of sequence b and value head h,
+//   u = SiLU(causal conv over [conv_state_in | x]) rounded to the io dtype,
+//   q = l2norm(u_q) * q_scale, k = l2norm(u_k), v = u_v,
+//   g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b),
+//   S' = exp(g) S; delta = beta (v - S'^T k); S = S' + k delta^T;
+//   o = S^T q = S'^T q + delta (k . q).
+//
+// Memory-bound by design: the fp32 state (d_k x d_v per head, 64 KiB at 128)
+// is read once and written once; everything else is < 3% of the bytes.
+// One workgroup owns a (b, h, NCOL-column slice) of S.  Columns of S are
+// independent given (q, k, beta, g), so slicing d_v multiplies parallelism;
+// each slice recomputes the (cheap) conv of its head's q and k channels.
+//
+// Thread layout (256 threads): thread = (cq, rg), cq = column quad (4
+// consecutive fp32 columns = one 16-byte load), rg = row group; thread owns
+// rows rg, rg + NRG, ... so that for each row step the whole workgroup reads
+// NRG full row segments with 16-byte coalesced loads.  S' lives in registers
+// between the read and the write.  Reductions over rows use a fixed
+// butterfly + fixed cross-wave order (deterministic, no atomics).
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kDecodeThreads = 256;
+
+template <typename IO, int DK, int NCOL>
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParams p) {
+    using T = io_traits<IO>;
+    constexpr int NCQ = NCOL / 4;                 // column quads per slice
+    constexpr int NRG = kDecodeThreads / NCQ;     // row groups
+    constexpr int RPT = DK / NRG;                 // rows per thread
+    static_assert(RPT * NRG == DK && NCQ * NRG == kDecodeThreads, "bad decode tiling");
+    constexpr int NCH = 2 * DK + NCOL;            // conv channels this slice needs
+    constexpr int NWAVES = kDecodeThreads / 64;
+    constexpr int RG_PER_WAVE = 64 / NCQ;
+
+    __shared__ float u_s[NCH];                    // conv+SiLU outputs (io-rounded)
+    __shared__ float red_s[2][NWAVES][NCOL];      // cross-wave partial sums
+    __shared__ __align__(16) float delta_s[NCOL];
+    __shared__ float scal_s[4];                   // n_q, n_k, k.q (unnormalised), g
+    __shared__ float beta_s;
+
+    const int tid = threadIdx.x;
+    const int z = blockIdx.x;                     // column slice
+    const int h = blockIdx.y;                     // value head
+    const int b = blockIdx.z;                     // sequence
+    const int r = p.num_v_heads / p.num_k_heads;
+    const int kh = h / r;
+    const int dv = p.head_v_dim;
+    const int64_t conv_dim = p.conv_dim;
+    const int col0 = z * NCOL;
+
+    const int cq = tid % NCQ;
+    const int rg = tid / NCQ;
+
+    // ---- 1. issue the state loads first (they dominate the bytes)
+    const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * DK * dv + col0 + cq * 4;
+    float4 S[RPT];
+    if (p.rec_in) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            S[i] = *reinterpret_cast<const float4*>(p.rec_in + s_base + (int64_t)(rg + i * NRG) * dv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // ---- 2. front end for the channels of this slice
+    const bool write_qk_tail = (h % r == 0) && (z == 0);
+    for (int i = tid; i < NCH; i += kDecodeThreads) {
+        int64_t c;
+        bool write_tail;
+        if (i < DK) {
+            c = (int64_t)kh * DK + i;
+            write_tail = write_qk_tail;
+        } else if (i < 2 * DK) {
+            c = (int64_t)p.num_k_heads * DK + (int64_t)kh * DK + (i - DK);
+            write_tail = write_qk_tail;
+        } else {
+            c = 2 * (int64_t)p.num_k_heads * DK + (int64_t)h * dv + col0 + (i - 2 * DK);
+            write_tail = true;
+        }
+        const int64_t cs = ((int64_t)b * conv_dim + c) * 3;
+        const float s0 = p.conv_in ? T::load(p.conv_in, cs + 0) : 0.f;
+        const float s1 = p.conv_in ? T::load(p.conv_in, cs + 1) : 0.f;
+        const float s2 = p.conv_in ? T::load(p.conv_in, cs + 2) : 0.f;
+        const float x = T::load(p.qkv, (int64_t)b * conv_dim + c);
+        const float w0 = T::load(p.conv_w, c * 4 + 0), w1 = T::load(p.conv_w, c * 4 + 1);
+        const float w2 = T::load(p.conv_w, c * 4 + 2), w3 = T::load(p.conv_w, c * 4 + 3);
+        const float y = fmaf(w3, x, fmaf(w2, s2, fmaf(w1, s1, w0 * s0)));
+        u_s[i] = T::round(silu_f32(y));
+        if (write_tail) {
+            if (p.conv_in) {
+                T::copy(p.conv_out, cs + 0, p.conv_in, cs + 1);
+                T::copy(p.conv_out, cs + 1, p.conv_in, cs + 2);
+            } else {
+                T::store(p.conv_out, cs + 0, 0.f);
+                T::store(p.conv_out, cs + 1, 0.f);
+            }
+            T::copy(p.conv_out, cs + 2, p.qkv, (int64_t)b * conv_dim + c);
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. norms, k.q and the gates (one wave each, fixed order)
+    const int wave = tid / 64, lane = tid % 64;
+    if (wave < 3) {
+        float acc = 0.f;
+        for (int i = lane; i < DK; i += 64) {
+            const float qv = u_s[i], kv = u_s[DK + i];
+            acc += wave == 0 ? qv * qv : (wave == 1 ? kv * kv : qv * kv);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) scal_s[wave] = acc;
+    } else if (lane == 0) {
+        const int64_t gi = (int64_t)b * p.num_v_heads + h;
+        const float av = T::load(p.a, gi), bv = T::load(p.b, gi);
+        scal_s[3] = -expf(p.A_log[h]) * softplus_f32(av + p.dt_bias[h]);
+        beta_s = sigmoid_f32(bv);
+    }
+    __syncthreads();
+    const float n_q = p.q_scale / sqrtf(scal_s[0] + p.l2_eps);
+    const float n_k = 1.0f / sqrtf(scal_s[1] + p.l2_eps);
+    const float kq = scal_s[2] * n_q * n_k;        // k_hat . q_hat
+    const float decay = expf(scal_s[3]);
+    const float beta = beta_s;
+
+    // ---- 4. S' = exp(g) S; partial S'^T k and S'^T q over this thread's rows
+    float kv[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};
+    float krow[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + i * NRG;
+        const float kk = u_s[DK + row] * n_k;
+        const float qq = u_s[row] * n_q;
+        krow[i] = kk;
+        S[i].x *= decay; S[i].y *= decay; S[i].z *= decay; S[i].w *= decay;
+        kv[0] = fmaf(S[i].x, kk, kv[0]); kv[1] = fmaf(S[i].y, kk, kv[1]);
+        kv[2] = fmaf(S[i].z, kk, kv[2]); kv[3] = fmaf(S[i].w, kk, kv[3]);
+        oq[0] = fmaf(S[i].x, qq, oq[0]); oq[1] = fmaf(S[i].y, qq, oq[1]);
+        oq[2] = fmaf(S[i].z, qq, oq[2]); oq[3] = fmaf(S[i].w, qq, oq[3]);
+    }
+    // reduce over the row groups of this wave (lanes differing in the rg bits)
+#pragma unroll
+    for (int m = NCQ; m < 64; m <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kv[j] += __shfl_xor(kv[j], m, 64);
+            oq[j] += __shfl_xor(oq[j], m, 64);
+        }
+    }
+    if (lane < NCQ) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            red_s[0][wave][cq * 4 + j] = kv[j];
+            red_s[1][wave][cq * 4 + j] = oq[j];
+        }
+    }
+    (void)RG_PER_WAVE;
+    __syncthreads();
+
+    // ---- 5. delta and o per column
+    if (tid < NCOL) {
+        float skv = 0.f, soq = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) { skv += red_s[0][w][tid]; soq += red_s[1][w][tid]; }
+        const float vv = u_s[2 * DK + tid];
+        const float d = beta * (vv - skv);
+        delta_s[tid] = d;
+        const int64_t oi = ((int64_t)b * p.num_v_heads + h) * dv + col0 + tid;
+        T::store(p.out, oi, fmaf(d, kq, soq));
+    }
+    __syncthreads();
+
+    // ---- 6. S = S' + k delta^T, written once
+    const float4 dl = *reinterpret_cast<const float4*>(&delta_s[cq * 4]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        float4 s = S[i];
+        s.x = fmaf(krow[i], dl.x, s.x); s.y = fmaf(krow[i], dl.y, s.y);
+        s.z = fmaf(krow[i], dl.z, s.z); s.w = fmaf(krow[i], dl.w, s.w);
+        *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = s;
+    }
+}
+
+template <typename IO, int DK, int NCOL>
+hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+    dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
+    hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL>), grid, dim3(kDecodeThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename IO, int DK>
+hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
+    switch (p.head_v_dim) {
+        case 32: return launch_typed<IO, DK, 32>(p, stream);
+        case 64: return launch_typed<IO, DK, 64>(p, stream);
+        case 128: return launch_typed<IO, DK, 64>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename IO>
+hipError_t launch_io(const DecodeParams& p, hipStream_t stream) {
+    switch (p.head_k_dim) {
+        case 32: return launch_dk<IO, 32>(p, stream);
+        case 64: return launch_dk<IO, 64>(p, stream);
+        case 128: return launch_dk<IO, 128>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_supported(int head_k_dim, int head_v_dim, int io_dtype) {
+    auto ok = [](int d) { return d == 32 || d == 64 || d == 128; };
+    return ok(head_k_dim) && ok(head_v_dim) && (io_dtype == GDN_F32 || io_dtype == GDN_BF16);
+}
+
+hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    return p.io_dtype == GDN_BF16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+}
+
+}  // namespace gdn

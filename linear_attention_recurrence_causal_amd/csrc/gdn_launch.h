@@ -1,0 +1,53 @@
+// gdn_launch.h -- kernel parameter blocks and launchers (host side of libgdn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeParams {
+    const void* qkv;        // [B, conv_dim] io
+    const void* a;          // [B, H_v] io
+    const void* b;          // [B, H_v] io
+    const void* conv_w;     // [conv_dim, 4] io
+    const float* A_log;     // [H_v]
+    const float* dt_bias;   // [H_v]
+    const void* conv_in;    // [B, conv_dim, 3] io or null (zeros)
+    void* conv_out;         // [B, conv_dim, 3] io
+    const float* rec_in;    // [B, H_v, d_k, d_v] or null (zeros)
+    float* rec_out;         // [B, H_v, d_k, d_v]
+    void* out;              // [B, H_v, d_v] io
+    int64_t conv_dim;
+    int32_t batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, io_dtype;
+    float q_scale, l2_eps;
+};
+
+struct PrefillParams {
+    const void* qkv;        // [B, L, conv_dim] bf16
+    const void* a;          // [B, L, H_v] bf16
+    const void* b;          // [B, L, H_v] bf16
+    const void* conv_w;     // [conv_dim, 4] bf16
+    const float* A_log;     // [H_v]
+    const float* dt_bias;   // [H_v]
+    const void* conv_in;    // [B, conv_dim, 3] bf16 or null
+    void* conv_out;         // [B, conv_dim, 3] bf16
+    const float* rec_in;    // [B, H_v, 128, 128] or null
+    float* rec_out;         // [B, H_v, 128, 128]
+    void* out;              // [B, L, H_v, 128] bf16
+    char* ckpt_buf;         // checkpoint slots or null
+    uint64_t slot_bytes;    // bytes per slot
+    uint64_t conv_slot_bytes;  // aligned bytes of the conv part of a slot
+    int64_t ckpt_interval;  // 0 = none
+    int64_t seq_len, start_pos, conv_dim;
+    int32_t batch, num_k_heads, num_v_heads;
+    float q_scale, l2_eps;
+};
+
+bool decode_supported(int head_k_dim, int head_v_dim, int io_dtype);
+hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
+
+bool prefill_supported(int head_k_dim, int head_v_dim, int io_dtype, int conv_kernel, int chunk);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+}  // namespace gdn

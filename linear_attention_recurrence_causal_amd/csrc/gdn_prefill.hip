@@ -1,0 +1,558 @@
+// gdn_prefill.hip -- fused chunked prefill of the Gated DeltaNet core (gfx950).
+//
+// What is computed: the per-token gated delta rule of the cortex commit page
+// "feat(stage-8c): linear-attention layer (Qwen3-Next GatedDeltaNet)"
+// ("Block", "Discretisation", "Delta rule"), evaluated in chunks of C = 64
+// tokens ("Performance note").  Within a chunk with rows r, incoming state
+// S0, gamma = inclusive cumsum of g and Gamma = exp(gamma), the rule unrolls
+// to (derivation in the design notes; the pages only name the method):
+//   A[r,i] = beta_r exp(gamma_r - gamma_i) (k_r . k_i)      for i < r
+//   T      = (I + A)^-1                       ("direct solve", the stable
+//            variant of the Qwen3.6-27B PR, "Known limitations and follow-ups")
+//   Delta  = T (diag(beta) V - diag(beta Gamma) K S0)
+//   O      = diag(Gamma) Q S0 + (M .* Q K^T) Delta,  M[r,i] = exp(gamma_r - gamma_i), i <= r
+//   S_C    = exp(gamma_C) S0 + (diag(exp(gamma_C - gamma)) K)^T Delta
+// with q, k the unit-norm vectors.  Here they are kept as raw bf16 conv
+// outputs (exact MFMA operands) and the norms are folded into fp32 row scales.
+//
+// One workgroup owns (sequence b, value head h, a slice of N = 16*NW state
+// columns); wave w owns 16 columns and keeps its 128 x 16 fp32 slice of S in
+// MFMA accumulator registers for the whole call.  Per chunk:
+//   A1  front end: raw qkv (+3-token halo, or the carried conv state) ->
+//       depthwise conv (fp32) -> SiLU -> bf16 -> LDS (Q, K, K^T, V)
+//   A2  gates g, beta (fp32), inclusive scan of g; L2 norms of q and k
+//   A3  K K^T and Q K^T lower 16x16 tiles on MFMA (bf16 in, fp32 out),
+//       decay masks -> A (fp32) and P (bf16)
+//   A4  T = (I + A)^-1 by blocked forward substitution in fp32 (16x16
+//       diagonal blocks by substitution, off-diagonal blocks by products)
+//   B   per wave, on MFMA: K S0, Q S0 (S0 as bf16), R, Delta = R + (T-I) R,
+//       O, and S <- exp(gamma_C) S + K^T Delta' with Delta' split into bf16
+//       hi + lo (two MFMAs): the product that builds the state carries ~16
+//       significant bits, everything else bf16 operands with fp32 accumulate.
+//   C   O rows -> HBM (16-byte stores); checkpoint slots when the chunk end is
+//       a multiple of the checkpoint interval.
+// Chunk boundaries sit at absolute multiples of 64, so a partial first or
+// last chunk is padded with rows that have g = 0, beta = 0, q = k = v = 0,
+// which leaves the rule's result unchanged.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout used throughout (lane l, i =
+// l % 16, q = l / 16): A row i and B column i each hold 8 reduction slots of
+// group q; D holds rows 4q..4q+3 of column i.  The reduction index a slot
+// stands for only has to agree between A and B, so the accumulator layout of
+// one product is reused as the B operand of the next without data movement.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kC = 64;              // chunk
+constexpr int kD = 128;             // d_k = d_v
+constexpr int kKsLd = kD + 8;       // bf16 row stride of Q, K (rows = tokens)
+constexpr int kKtLd = kC + 8;       // bf16 row stride of K^T, N, P
+constexpr int kALd = kC + 4;        // fp32 row stride of A, T
+constexpr int kXLd = 17;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 (16 bytes) from LDS
+__device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// two runs of 4 bf16 (8 bytes each): slots 0-3 from p, 4-7 from p + 16
+__device__ __forceinline__ bf16x8 lds_load4x2(const __bf16* p) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {
+    const f32x8 v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ f32x8 to_f32x8(bf16x8 v) { return __builtin_convertvector(v, f32x8); }
+
+template <int NW>
+struct alignas(16) Smem {
+    static constexpr int N = 16 * NW;
+    static constexpr int VLd = N + 8;
+    static constexpr int NCH = 2 * kD + N;
+    __bf16 Ks[kC * kKsLd];
+    __bf16 Qs[kC * kKsLd];
+    __bf16 Kt[kD * kKtLd];
+    __bf16 Vs[kC * VLd];
+    __bf16 Ps[kC * kKtLd];
+    __bf16 Ns[kC * kKtLd];
+    union {
+        float As[kC * kALd];       // A3 -> A4
+        __bf16 Os[kC * VLd];       // B -> C (A is dead by then)
+    };
+    float Ts[kC * kALd];
+    float Xs[3 * 16 * kXLd];
+    float Ws[NCH * 4];
+    float beta[kC], gam[kC], nq[kC], nk[kC], sR[kC], sO[kC], sU[kC];
+    float eC;
+};
+
+// lower 16x16 tile pairs (m, p), p <= m, in a fixed order
+__device__ __forceinline__ void tile_pair(int idx, int& m, int& p) {
+    m = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
+    p = idx - (m * (m + 1)) / 2;
+}
+
+// Global channel of the WG's channel index ch (q: 0..127, k: 128..255, v: 256..)
+__device__ __forceinline__ int64_t global_channel(int ch, int kh, int h, int zcol0, int Hk) {
+    if (ch < kD) return (int64_t)kh * kD + ch;
+    if (ch < 2 * kD) return (int64_t)Hk * kD + (int64_t)kh * kD + (ch - kD);
+    return 2 * (int64_t)Hk * kD + (int64_t)h * kD + zcol0 + (ch - 2 * kD);
+}
+
+// 8 pre-conv inputs of channels gc..gc+7 at call-local token t.  t < 0 reads
+// the carried conv state (zeros for a new request); t >= L reads zeros.
+__device__ __forceinline__ void load_x8(const PrefillParams& p, int b, int64_t t, int64_t gc,
+                                        float x[8]) {
+    if (t >= 0 && t < p.seq_len) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(p.qkv) + ((int64_t)b * p.seq_len + t) * p.conv_dim + gc);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        }
+    } else if (t < 0 && t >= -3 && p.conv_in) {
+        const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            x[i] = bf16_bits_to_f32(cs[((int64_t)b * p.conv_dim + gc + i) * 3 + (3 + t)]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+}
+
+// Copy the conv tail that ends just before call-local token `end` (the last
+// three pre-conv inputs) for channel gc of sequence b into dst[b][gc][0..2].
+__device__ __forceinline__ void write_tail(const PrefillParams& p, int b, int64_t end, int64_t gc,
+                                           uint16_t* dst) {
+    const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
+    const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int64_t t = end - 3 + j;
+        uint16_t v;
+        if (t >= 0) v = qkv[((int64_t)b * p.seq_len + t) * p.conv_dim + gc];
+        else v = cs ? cs[((int64_t)b * p.conv_dim + gc) * 3 + (3 + t)] : uint16_t(0);
+        dst[((int64_t)b * p.conv_dim + gc) * 3 + j] = v;
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
+    constexpr int NT = 64 * NW;
+    constexpr int N = 16 * NW;
+    constexpr int S_SPLIT = kD / N;
+    using SM = Smem<NW>;
+    constexpr int VLd = SM::VLd;
+    constexpr int NCH = SM::NCH;
+    constexpr int CG = NCH / 8;
+    __shared__ SM sm;
+
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int li = lane % 16, lq = lane / 16;
+
+    // ---- workgroup -> (b, key head, member).  The r*S_SPLIT workgroups of one
+    // (b, key head) read the same q/k rows; give them one blockIdx % 8 so that
+    // the round-robin dispatch puts them on one XCD and its L2.
+    const int r = p.num_v_heads / p.num_k_heads;
+    const int M = r * S_SPLIT;
+    const int NG = p.batch * p.num_k_heads;
+    const int bid = blockIdx.x;
+    const int grp = (bid / 8 / M) * 8 + bid % 8;
+    const int mem = (bid / 8) % M;
+    if (grp >= NG) return;
+    const int b = grp / p.num_k_heads, kh = grp % p.num_k_heads;
+    const int h = kh * r + mem / S_SPLIT, z = mem % S_SPLIT;
+    const int zcol0 = z * N;
+    const int64_t L = p.seq_len, sp = p.start_pos;
+    const bool owns_qk_tail = (mem == 0);
+
+    // ---- one-time set-up: zero the upper tiles of N and P, conv taps -> LDS
+    for (int e = tid; e < 6 * 256; e += NT) {
+        const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
+        const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
+        const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
+        sm.Ps[(16 * m + rr) * kKtLd + 16 * pp + cc] = __bf16(0.f);
+        sm.Ns[(16 * m + rr) * kKtLd + 16 * pp + cc] = __bf16(0.f);
+    }
+    for (int e = tid; e < NCH * 4; e += NT) {
+        const int64_t gc = global_channel(e / 4, kh, h, zcol0, p.num_k_heads);
+        sm.Ws[e] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + (e % 4)]);
+    }
+    const float A_log_h = p.A_log[h], dt_h = p.dt_bias[h];
+    const float neg_A = -expf(A_log_h);
+
+    // ---- the state slice of this wave: S[16t + 4lq + e][zcol0 + 16 wave + li]
+    const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * kD * kD + zcol0 + 16 * wave + li;
+    f32x4 S[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[t][e] = p.rec_in ? p.rec_in[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] : 0.f;
+
+    const int64_t k_first = sp / kC;
+    const int64_t k_end = L > 0 ? (sp + L - 1) / kC + 1 : k_first;
+    __syncthreads();
+
+    for (int64_t kc = k_first; kc < k_end; ++kc) {
+        const int64_t local0 = kc * kC - sp;   // call-local index of chunk row 0
+
+        // ================= A1: front end -> Q, K, K^T, V (bf16) in LDS
+        for (int item = tid; item < CG * 8; item += NT) {
+            const int cg = item % CG, seg = item / CG;
+            const int ch0 = cg * 8;
+            const int64_t gc = global_channel(ch0, kh, h, zcol0, p.num_k_heads);
+            const int tau0 = seg * 8;
+            float w[4][8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j][i] = sm.Ws[(ch0 + i) * 4 + j];
+            float h0[8], h1[8], h2[8];
+            load_x8(p, b, local0 + tau0 - 3, gc, h0);
+            load_x8(p, b, local0 + tau0 - 2, gc, h1);
+            load_x8(p, b, local0 + tau0 - 1, gc, h2);
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                const int tau = tau0 + tt;
+                const int64_t t = local0 + tau;
+                float x[8];
+                load_x8(p, b, t, gc, x);
+                const bool valid = t >= 0 && t < L;
+                f32x8 u;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], h2[i], fmaf(w[1][i], h1[i], w[0][i] * h0[i])));
+                    u[i] = valid ? silu_f32(y) : 0.f;
+                    h0[i] = h1[i];
+                    h1[i] = h2[i];
+                    h2[i] = x[i];
+                }
+                const bf16x8 ub = __builtin_convertvector(u, bf16x8);
+                __bf16* dst = ch0 < kD ? &sm.Qs[tau * kKsLd + ch0]
+                            : ch0 < 2 * kD ? &sm.Ks[tau * kKsLd + ch0 - kD]
+                                           : &sm.Vs[tau * VLd + ch0 - 2 * kD];
+                *reinterpret_cast<bf16x8*>(dst) = ub;
+            }
+        }
+        __syncthreads();
+
+        // ================= A2: gates + inclusive scan (wave 0), L2 norms, K^T
+        for (int e = tid; e < kD * (kC / 8); e += NT) {
+            // K^T[d][tau0 .. tau0+7] from eight K rows; lanes walk d, so the
+            // 2-byte LDS reads of one instruction hit consecutive addresses
+            const int d = e % kD, tau0 = (e / kD) * 8;
+            bf16x8 col;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) col[i] = sm.Ks[(tau0 + i) * kKsLd + d];
+            *reinterpret_cast<bf16x8*>(&sm.Kt[d * kKtLd + tau0]) = col;
+        }
+        for (int job = tid; job < 3 * kC; job += NT) {
+            if (job < kC) {
+                const int tau = job;
+                const int64_t t = local0 + tau;
+                const bool valid = t >= 0 && t < L;
+                float gv = 0.f, bv = 0.f;
+                if (valid) {
+                    const int64_t gi = ((int64_t)b * L + t) * p.num_v_heads + h;
+                    const float av = bf16_bits_to_f32(static_cast<const uint16_t*>(p.a)[gi]);
+                    const float bb = bf16_bits_to_f32(static_cast<const uint16_t*>(p.b)[gi]);
+                    gv = neg_A * softplus_f32(av + dt_h);
+                    bv = sigmoid_f32(bb);
+                }
+                float s = gv;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_up(s, off, 64);
+                    if (lane >= off) s += o;
+                }
+                sm.gam[tau] = s;
+                sm.beta[tau] = bv;
+            } else {
+                const bool isq = job < 2 * kC;
+                const int tau = job % kC;
+                const __bf16* row = (isq ? sm.Qs : sm.Ks) + tau * kKsLd;
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < kD; c += 8) {
+                    const f32x8 v = to_f32x8(lds_load8(row + c));
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = fmaf(v[i], v[i], acc);
+                }
+                const float n = (isq ? p.q_scale : 1.0f) / sqrtf(acc + p.l2_eps);
+                (isq ? sm.nq : sm.nk)[tau] = n;
+            }
+        }
+        __syncthreads();
+
+        // ================= A3: derived row scales; K K^T, Q K^T tiles on MFMA
+        if (tid < kC) {
+            const float gl = sm.gam[tid], gC = sm.gam[kC - 1];
+            const float e = expf(gl);
+            sm.sR[tid] = sm.beta[tid] * e * sm.nk[tid];
+            sm.sO[tid] = e * sm.nq[tid];
+            sm.sU[tid] = expf(gC - gl) * sm.nk[tid];
+            if (tid == 0) sm.eC = expf(gC);
+        }
+        for (int pi = wave; pi < 10; pi += NW) {
+            int m, pp;
+            tile_pair(pi, m, pp);
+            f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int col = 32 * ks + 8 * lq;
+                const bf16x8 ak = lds_load8(&sm.Ks[(16 * m + li) * kKsLd + col]);
+                const bf16x8 aq = lds_load8(&sm.Qs[(16 * m + li) * kKsLd + col]);
+                const bf16x8 bk = lds_load8(&sm.Ks[(16 * pp + li) * kKsLd + col]);
+                accG = mfma16(ak, bk, accG);
+                accQ = mfma16(aq, bk, accQ);
+            }
+            const int ii = 16 * pp + li;
+            const float gi = sm.gam[ii], nki = sm.nk[ii];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * m + 4 * lq + e;
+                const float dec = ii <= rr ? expf(sm.gam[rr] - gi) : 0.f;
+                const float av = ii < rr ? sm.beta[rr] * sm.nk[rr] * nki * dec * accG[e] : 0.f;
+                const float pv = ii <= rr ? sm.nq[rr] * nki * dec * accQ[e] : 0.f;
+                sm.As[rr * kALd + ii] = av;
+                sm.Ps[rr * kKtLd + ii] = __bf16(pv);
+            }
+        }
+        __syncthreads();
+
+        // ================= A4: T = (I + A)^-1, blocked forward substitution
+        if (wave == 0) {
+            // diagonal block m, column c: solve (I + A_mm) x = e_c
+            const int m = lane / 16, c = lane % 16;
+            const float* Arow = sm.As + 16 * m * kALd + 16 * m;
+            float x[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < rr; ++i) acc = fmaf(Arow[rr * kALd + i], x[i], acc);
+                x[rr] = rr < c ? 0.f : (rr == c ? 1.f : -acc);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) sm.Ts[(16 * m + rr) * kALd + 16 * m + c] = x[rr];
+        }
+        __syncthreads();
+        for (int mb = 1; mb < 4; ++mb) {
+            // X_p = sum_{k=p}^{mb-1} A_{mb,k} T_{k,p}
+            for (int e = tid; e < mb * 256; e += NT) {
+                const int pb = e / 256, rr = (e / 16) % 16, cc = e % 16;
+                float acc = 0.f;
+                for (int kb = pb; kb < mb; ++kb) {
+                    const float* Ar = sm.As + (16 * mb + rr) * kALd + 16 * kb;
+                    const float* Tc = sm.Ts + (16 * kb) * kALd + 16 * pb + cc;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc = fmaf(Ar[i], Tc[i * kALd], acc);
+                }
+                sm.Xs[(pb * 16 + rr) * kXLd + cc] = acc;
+            }
+            __syncthreads();
+            // T_{mb,p} = -T_{mb,mb} X_p
+            for (int e = tid; e < mb * 256; e += NT) {
+                const int pb = e / 256, rr = (e / 16) % 16, cc = e % 16;
+                const float* Tr = sm.Ts + (16 * mb + rr) * kALd + 16 * mb;
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc = fmaf(Tr[i], sm.Xs[(pb * 16 + i) * kXLd + cc], acc);
+                sm.Ts[(16 * mb + rr) * kALd + 16 * pb + cc] = -acc;
+            }
+            __syncthreads();
+        }
+        // N = T - I (bf16) on the lower tiles
+        for (int e = tid; e < 10 * 256; e += NT) {
+            int m, pp;
+            tile_pair(e / 256, m, pp);
+            const int rr = 16 * m + (e / 16) % 16, cc = 16 * pp + e % 16;
+            const float v = sm.Ts[rr * kALd + cc] - (rr == cc ? 1.f : 0.f);
+            sm.Ns[rr * kKtLd + cc] = __bf16(v);
+        }
+        __syncthreads();
+
+        // ================= B: state-dependent products, per wave
+        {
+            const int cw = 16 * wave + li;   // column inside the slice
+            bf16x8 Bs[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+            f32x4 KS[4], QS[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                KS[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                QS[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int off = (16 * m + li) * kKsLd + 32 * ks + 4 * lq;
+                    KS[m] = mfma16(lds_load4x2(&sm.Ks[off]), Bs[ks], KS[m]);
+                    QS[m] = mfma16(lds_load4x2(&sm.Qs[off]), Bs[ks], QS[m]);
+                }
+            }
+            // R = beta V - beta Gamma n_k (K S0); Delta = R + (T - I) R
+            f32x4 R[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tau = 16 * m + 4 * lq + e;
+                    const float vv = float(sm.Vs[tau * VLd + cw]);
+                    R[m][e] = sm.beta[tau] * vv - sm.sR[tau] * KS[m][e];
+                }
+            const bf16x8 BR[2] = {to_bf16x8(R[0], R[1]), to_bf16x8(R[2], R[3])};
+            f32x4 Dl[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = R[m];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks == 0 || m >= 2)
+                        acc = mfma16(lds_load4x2(&sm.Ns[(16 * m + li) * kKtLd + 32 * ks + 4 * lq]), BR[ks], acc);
+                Dl[m] = acc;
+            }
+            // O = Gamma n_q (Q S0) + P Delta -> LDS staging
+            const bf16x8 BD[2] = {to_bf16x8(Dl[0], Dl[1]), to_bf16x8(Dl[2], Dl[3])};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = sm.sO[16 * m + 4 * lq + e] * QS[m][e];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks == 0 || m >= 2)
+                        acc = mfma16(lds_load4x2(&sm.Ps[(16 * m + li) * kKtLd + 32 * ks + 4 * lq]), BD[ks], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
+            }
+            // S <- exp(gamma_C) S + K^T Delta',  Delta' = exp(gamma_C - gamma) n_k Delta  (hi + lo)
+            f32x4 Dq[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Dq[m][e] = sm.sU[16 * m + 4 * lq + e] * Dl[m][e];
+            bf16x8 BH[2], BL[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                BH[ks] = to_bf16x8(Dq[2 * ks], Dq[2 * ks + 1]);
+                const f32x8 back = to_f32x8(BH[ks]);
+                const f32x4 l0 = {Dq[2 * ks][0] - back[0], Dq[2 * ks][1] - back[1],
+                                  Dq[2 * ks][2] - back[2], Dq[2 * ks][3] - back[3]};
+                const f32x4 l1 = {Dq[2 * ks + 1][0] - back[4], Dq[2 * ks + 1][1] - back[5],
+                                  Dq[2 * ks + 1][2] - back[6], Dq[2 * ks + 1][3] - back[7]};
+                BL[ks] = to_bf16x8(l0, l1);
+            }
+            const float eC = sm.eC;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4 acc = S[t] * eC;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 akt = lds_load4x2(&sm.Kt[(16 * t + li) * kKtLd + 32 * ks + 4 * lq]);
+                    acc = mfma16(akt, BH[ks], acc);
+                    acc = mfma16(akt, BL[ks], acc);
+                }
+                S[t] = acc;
+            }
+        }
+        __syncthreads();
+
+        // ================= C: outputs and checkpoint slots
+        {
+            constexpr int V8 = N / 8;
+            uint16_t* out = static_cast<uint16_t*>(p.out);
+            for (int e = tid; e < kC * V8; e += NT) {
+                const int tau = e / V8, c8 = e % V8;
+                const int64_t t = local0 + tau;
+                if (t >= 0 && t < L)
+                    *reinterpret_cast<uint4*>(out + (((int64_t)b * L + t) * p.num_v_heads + h) * kD + zcol0 + 8 * c8) =
+                        *reinterpret_cast<const uint4*>(&sm.Os[tau * VLd + 8 * c8]);
+            }
+            const int64_t pe = (kc + 1) * kC;   // absolute end of this chunk
+            if (p.ckpt_interval > 0 && pe % p.ckpt_interval == 0 && pe <= sp + L) {
+                char* slot = p.ckpt_buf + (uint64_t)(pe / p.ckpt_interval - 1) * p.slot_bytes;
+                float* rec = reinterpret_cast<float*>(slot + p.conv_slot_bytes);
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rec[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+                uint16_t* ctail = reinterpret_cast<uint16_t*>(slot);
+                for (int ch = tid; ch < NCH; ch += NT)
+                    if (ch >= 2 * kD || owns_qk_tail)
+                        write_tail(p, b, pe - sp, global_channel(ch, kh, h, zcol0, p.num_k_heads), ctail);
+            }
+        }
+    }
+
+    // ---- final state and conv tail
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.rec_out[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+    for (int ch = tid; ch < NCH; ch += NT)
+        if (ch >= 2 * kD || owns_qk_tail)
+            write_tail(p, b, L, global_channel(ch, kh, h, zcol0, p.num_k_heads),
+                       static_cast<uint16_t*>(p.conv_out));
+}
+
+template <int NW>
+hipError_t launch_nw(const PrefillParams& p, hipStream_t stream) {
+    const int s_split = kD / (16 * NW);
+    const int r = p.num_v_heads / p.num_k_heads;
+    const int ng = p.batch * p.num_k_heads;
+    const int blocks = ((ng + 7) / 8) * 8 * r * s_split;
+    hipLaunchKernelGGL((prefill_kernel<NW>), dim3(blocks), dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(int head_k_dim, int head_v_dim, int io_dtype, int conv_kernel, int chunk) {
+    return head_k_dim == kD && head_v_dim == kD && io_dtype == GDN_BF16 && conv_kernel == 4 &&
+           chunk == kC;
+}
+
+// Columns of S per workgroup: the whole head when there are enough (b, head)
+// chains to fill the chip, else split d_v so that more CUs share the chain.
+int prefill_waves(int64_t chains) {
+    if (const char* env = getenv("GDN_PREFILL_WAVES")) {
+        const int v = atoi(env);
+        if (v == 2 || v == 4 || v == 8) return v;
+    }
+    if (chains >= 192) return 8;
+    if (chains >= 96) return 4;
+    return 2;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    switch (prefill_waves((int64_t)p.batch * p.num_v_heads)) {
+        case 8: return launch_nw<8>(p, stream);
+        case 4: return launch_nw<4>(p, stream);
+        default: return launch_nw<2>(p, stream);
+    }
+}
+
+}  // namespace gdn

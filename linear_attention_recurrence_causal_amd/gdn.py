@@ -1,0 +1,220 @@
+"""Thin Python binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the stream.  If
+the library is missing this module raises on import -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                      "`python -m linear_attention_recurrence_causal_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIAS, GDN_ESPACE, GDN_EHIP = range(6)
+GDN_F32, GDN_BF16 = 0, 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.gdn_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_k_heads", ctypes.c_int32),
+                ("num_v_heads", ctypes.c_int32), ("head_k_dim", ctypes.c_int32),
+                ("head_v_dim", ctypes.c_int32), ("conv_kernel", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+
+
+class CkptEntry(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_int64), ("position", ctypes.c_int64),
+                ("conv_offset", ctypes.c_uint64), ("rec_offset", ctypes.c_uint64)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_CFG = ctypes.POINTER(_Config)
+_lib.gdn_status_string.argtypes = [ctypes.c_int32]
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_version.restype = ctypes.c_int32
+_lib.gdn_state_checkpoint.argtypes = [_CFG, _I64, _I64, _I64, ctypes.POINTER(CkptEntry), _I64,
+                                      ctypes.POINTER(_I64), ctypes.POINTER(_U64)]
+_lib.gdn_state_checkpoint.restype = ctypes.c_int32
+_lib.gdn_prefill_workspace_bytes.argtypes = [_CFG, _I64, ctypes.POINTER(_U64)]
+_lib.gdn_prefill_workspace_bytes.restype = ctypes.c_int32
+_lib.gdn_prefill_chunked.argtypes = [_CFG, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _U64, _I64, _P, _U64, _P]
+_lib.gdn_prefill_chunked.restype = ctypes.c_int32
+_lib.gdn_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.gdn_decode_step.restype = ctypes.c_int32
+
+lib = _lib
+
+
+@dataclass(frozen=True)
+class Config:
+    """Mirror of ``gdn_config``."""
+    batch: int
+    num_k_heads: int
+    num_v_heads: int
+    head_k_dim: int = 128
+    head_v_dim: int = 128
+    conv_kernel: int = 4
+    chunk: int = 64
+    io_dtype: int = GDN_BF16
+    q_scale: float = 1.0
+    l2_eps: float = 1e-6
+
+    @property
+    def conv_dim(self) -> int:
+        return 2 * self.num_k_heads * self.head_k_dim + self.num_v_heads * self.head_v_dim
+
+    @property
+    def torch_io(self) -> torch.dtype:
+        return torch.bfloat16 if self.io_dtype == GDN_BF16 else torch.float32
+
+    def c(self) -> _Config:
+        return _Config(self.batch, self.num_k_heads, self.num_v_heads, self.head_k_dim,
+                       self.head_v_dim, self.conv_kernel, self.chunk, self.io_dtype,
+                       self.q_scale, self.l2_eps)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, shape, dtype, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def state_checkpoint(cfg: Config, start_pos: int, seq_len: int, interval: int):
+    """Checkpoint plan: (list of CkptEntry, buffer_bytes)."""
+    count, nbytes = _I64(0), _U64(0)
+    st = _lib.gdn_state_checkpoint(ctypes.byref(cfg.c()), start_pos, seq_len, interval, None, 0,
+                                   ctypes.byref(count), ctypes.byref(nbytes))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_state_checkpoint")
+    arr = (CkptEntry * max(count.value, 1))()
+    st = _lib.gdn_state_checkpoint(ctypes.byref(cfg.c()), start_pos, seq_len, interval, arr,
+                                   count.value, ctypes.byref(count), ctypes.byref(nbytes))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_state_checkpoint")
+    return list(arr)[: count.value], nbytes.value
+
+
+def prefill_workspace_bytes(cfg: Config, seq_len: int) -> int:
+    n = _U64(0)
+    st = _lib.gdn_prefill_workspace_bytes(ctypes.byref(cfg.c()), seq_len, ctypes.byref(n))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_workspace_bytes")
+    return n.value
+
+
+def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
+                    rec_state_in=None, *, start_pos: int = 0, ckpt_interval: int = 0,
+                    ckpt_buf=None, out=None, conv_state_out=None, rec_state_out=None,
+                    stream=None):
+    """Chunked prefill; returns (out, conv_state_out, rec_state_out).
+
+    Outputs not passed in are allocated with torch.  ``ckpt_buf`` is a uint8
+    device tensor of at least ``state_checkpoint(...)[1]`` bytes.
+    """
+    B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
+    L = qkv.shape[1]
+    io = cfg.torch_io
+    _check(qkv, "qkv", (B, L, cfg.conv_dim), io)
+    _check(a, "a", (B, L, Hv), io)
+    _check(b, "b", (B, L, Hv), io)
+    _check(conv_w, "conv_w", (cfg.conv_dim, cfg.conv_kernel), io)
+    _check(A_log, "A_log", (Hv,), torch.float32)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _check(conv_state_in, "conv_state_in", (B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
+    dev = qkv.device
+    if out is None:
+        out = torch.empty((B, L, Hv, dv), dtype=io, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    if rec_state_out is None:
+        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", (B, L, Hv, dv), io)
+    _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
+    _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
+    ck_bytes = 0
+    if ckpt_buf is not None:
+        if not ckpt_buf.is_cuda or not ckpt_buf.is_contiguous():
+            raise ValueError("ckpt_buf must be a contiguous device tensor")
+        ck_bytes = ckpt_buf.numel() * ckpt_buf.element_size()
+    ws = prefill_workspace_bytes(cfg, L)
+    wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    st = _lib.gdn_prefill_chunked(
+        ctypes.byref(cfg.c()), L, start_pos, _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+        _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out),
+        _ptr(rec_state_in), _ptr(rec_state_out), _ptr(out), _ptr(ckpt_buf), ck_bytes,
+        ckpt_interval, _ptr(wsbuf), ws, _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_chunked")
+    return out, conv_state_out, rec_state_out
+
+
+def decode_step(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
+                rec_state_in=None, *, out=None, conv_state_out=None, rec_state_out=None,
+                stream=None):
+    """One recurrent step; returns (out, conv_state_out, rec_state_out).
+
+    ``rec_state_out`` may be ``rec_state_in`` (in-place update)."""
+    B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
+    io = cfg.torch_io
+    _check(qkv, "qkv", (B, cfg.conv_dim), io)
+    _check(a, "a", (B, Hv), io)
+    _check(b, "b", (B, Hv), io)
+    _check(conv_w, "conv_w", (cfg.conv_dim, cfg.conv_kernel), io)
+    _check(A_log, "A_log", (Hv,), torch.float32)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _check(conv_state_in, "conv_state_in", (B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
+    dev = qkv.device
+    if out is None:
+        out = torch.empty((B, Hv, dv), dtype=io, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    if rec_state_out is None:
+        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", (B, Hv, dv), io)
+    _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
+    _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
+    st = _lib.gdn_decode_step(ctypes.byref(cfg.c()), _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+                              _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in),
+                              _ptr(conv_state_out), _ptr(rec_state_in), _ptr(rec_state_out),
+                              _ptr(out), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_step")
+    return out, conv_state_out, rec_state_out

@@ -1,0 +1,152 @@
+"""Host-side tests of libgdn: it loads, exports what include/gdn.h declares,
+plans checkpoints exactly, and rejects bad arguments before touching a GPU.
+
+No call here reaches a kernel launch: every compute call is given an argument
+that validation refuses first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def G():
+    from linear_attention_recurrence_causal_amd import gdn
+    return gdn
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(G):
+    names = declared_functions()
+    assert {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_checkpoint"} <= set(names)
+    for n in names:
+        assert hasattr(G.lib, n), n
+    assert G.lib.gdn_version() >= 100
+    for s in range(6):
+        assert G.lib.gdn_status_string(s)
+    assert G.lib.gdn_status_string(99) == b"unknown status"
+
+
+def cfg(G, **kw):
+    base = dict(batch=1, num_k_heads=16, num_v_heads=48)
+    base.update(kw)
+    return G.Config(**base)
+
+
+def test_checkpoint_plan_exact(G):
+    """Slots, positions and byte offsets follow the formula in gdn.h, and the
+    emitted positions are those the oracle checkpoints (every multiple of the
+    interval in (start, start + L])."""
+    from oracle import oracle as O
+    for B, Hk, Hv, io in ((1, 16, 48, G.GDN_BF16), (8, 16, 32, G.GDN_BF16), (3, 2, 4, G.GDN_F32)):
+        c = cfg(G, batch=B, num_k_heads=Hk, num_v_heads=Hv, io_dtype=io)
+        ios = 2 if io == G.GDN_BF16 else 4
+        al = lambda x: (x + 255) // 256 * 256
+        conv_b = al(B * c.conv_dim * 3 * ios)
+        slot_b = conv_b + al(B * Hv * 128 * 128 * 4)
+        for start, L, iv in ((0, 262144, 4096), (4096, 8192, 4096), (100, 1000, 64),
+                             (0, 63, 64), (64, 0, 64), (5, 300, 0)):
+            ents, nbytes = G.state_checkpoint(c, start, L, iv)
+            want_pos = [p for p in range(start + 1, start + L + 1) if iv and p % iv == 0]
+            assert [e.position for e in ents] == want_pos
+            assert [e.slot for e in ents] == [p // iv - 1 for p in want_pos]
+            assert [e.conv_offset for e in ents] == [(p // iv - 1) * slot_b for p in want_pos]
+            assert [e.rec_offset for e in ents] == [(p // iv - 1) * slot_b + conv_b for p in want_pos]
+            assert nbytes == (want_pos[-1] // iv * slot_b if want_pos else 0)
+            d = O.Dims(B, L, Hk, Hv, 128, 128, start_pos=start, ckpt_interval=iv)
+            assert O.ckpt_count(d) == len(want_pos)
+    # the 256K, every-4096 workload: 64 slots of 61,440 + 3,145,728 bytes
+    ents, nbytes = G.state_checkpoint(cfg(G), 0, 262144, 4096)
+    assert len(ents) == 64 and ents[0].rec_offset == 61440
+    assert nbytes == 64 * (61440 + 3145728)
+
+
+def test_checkpoint_plan_errors(G):
+    c = cfg(G)
+    count, nb = ctypes.c_int64(0), ctypes.c_uint64(0)
+    f = G.lib.gdn_state_checkpoint
+    assert f(ctypes.byref(c.c()), 0, 100, 65, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
+    assert f(ctypes.byref(c.c()), -1, 100, 64, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
+    assert f(None, 0, 100, 64, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
+    assert f(ctypes.byref(c.c()), 0, 100, 64, None, 0, None, ctypes.byref(nb)) == G.GDN_EINVAL
+    arr = (G.CkptEntry * 1)()
+    st = f(ctypes.byref(c.c()), 0, 300, 64, arr, 1, ctypes.byref(count), ctypes.byref(nb))
+    assert st == G.GDN_ESPACE and count.value == 4 and arr[0].position == 64
+    bad = cfg(G, num_v_heads=47)
+    assert f(ctypes.byref(bad.c()), 0, 100, 64, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
+
+
+def test_workspace_is_zero(G):
+    assert G.prefill_workspace_bytes(cfg(G), 16384) == 0
+
+
+FAKE = 1 << 34  # aligned, far-apart addresses that are never dereferenced: every call below fails validation
+
+
+def prefill_args(G, c, **over):
+    P = ctypes.c_void_p
+    args = dict(seq_len=64, start_pos=0, qkv=P(FAKE), a=P(FAKE * 2), b=P(FAKE * 3),
+                conv_w=P(FAKE * 4), A_log=P(FAKE * 5), dt_bias=P(FAKE * 6), cin=None,
+                cout=P(FAKE * 7), rin=None, rout=P(FAKE * 8), out=P(FAKE * 9), ck=None,
+                ck_bytes=0, iv=0, ws=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return [ctypes.byref(c.c())] + list(args.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(qkv=None), "GDN_EINVAL"),
+    (dict(out=ctypes.c_void_p(FAKE * 9 + 2)), "GDN_EINVAL"),     # out needs 16 bytes
+    (dict(a=ctypes.c_void_p(FAKE * 2 + 1)), "GDN_EINVAL"),       # not element-aligned
+    (dict(ck=ctypes.c_void_p(FAKE * 20 + 16), ck_bytes=1 << 30, iv=64), "GDN_EINVAL"),
+    (dict(seq_len=-1), "GDN_EINVAL"),
+    (dict(iv=100), "GDN_EINVAL"),                                # not a multiple of the chunk
+    (dict(iv=64), "GDN_EINVAL"),                                 # slots emitted, no buffer
+])
+def test_prefill_rejects_bad_arguments(G, over, want):
+    assert G.lib.gdn_prefill_chunked(*prefill_args(G, cfg(G), **over)) == getattr(G, want)
+
+
+def test_prefill_rejects_unsupported_and_aliasing(G):
+    f = G.lib.gdn_prefill_chunked
+    assert f(*prefill_args(G, cfg(G, head_k_dim=64, head_v_dim=64))) == G.GDN_EUNSUPPORTED
+    assert f(*prefill_args(G, cfg(G, io_dtype=G.GDN_F32))) == G.GDN_EUNSUPPORTED
+    assert f(*prefill_args(G, cfg(G, conv_kernel=3))) == G.GDN_EUNSUPPORTED
+    # conv_state_out on top of conv_state_in
+    P = ctypes.c_void_p
+    assert f(*prefill_args(G, cfg(G), cin=P(FAKE * 7))) == G.GDN_EALIAS
+    # out overlapping qkv
+    assert f(*prefill_args(G, cfg(G), out=P(FAKE))) == G.GDN_EALIAS
+    # checkpoint buffer too small
+    assert f(*prefill_args(G, cfg(G), iv=64, ck=P(FAKE * 20), ck_bytes=16)) == G.GDN_ESPACE
+    # bad config
+    assert f(*prefill_args(G, cfg(G, num_v_heads=20))) == G.GDN_EINVAL
+    assert f(*prefill_args(G, cfg(G, l2_eps=-1.0))) == G.GDN_EINVAL
+
+
+def test_decode_rejects_bad_arguments(G):
+    P = ctypes.c_void_p
+    f = G.lib.gdn_decode_step
+    def call(c, **over):
+        args = dict(qkv=P(FAKE), a=P(FAKE * 2), b=P(FAKE * 3), conv_w=P(FAKE * 4),
+                    A_log=P(FAKE * 5), dt_bias=P(FAKE * 6), cin=None, cout=P(FAKE * 7),
+                    rin=None, rout=P(FAKE * 8), out=P(FAKE * 9), stream=None)
+        args.update(over)
+        return f(ctypes.byref(c.c()), *args.values())
+    assert call(cfg(G), qkv=None) == G.GDN_EINVAL
+    assert call(cfg(G), a=P(FAKE * 2 + 1)) == G.GDN_EINVAL           # not element-aligned
+    assert call(cfg(G), rout=P(FAKE * 8 + 4)) == G.GDN_EINVAL        # state needs 16 bytes
+    assert call(cfg(G, head_k_dim=96)) == G.GDN_EUNSUPPORTED
+    assert call(cfg(G, conv_kernel=2)) == G.GDN_EUNSUPPORTED
+    assert call(cfg(G), cin=P(FAKE * 7)) == G.GDN_EALIAS
+    # a partial overlap of the recurrent states is refused, exact equality is in place
+    assert call(cfg(G), rin=P(FAKE * 8 + 256)) == G.GDN_EALIAS
