@@ -50,13 +50,13 @@ namespace {
 constexpr int kC = 64;              // chunk
 constexpr int kD = 128;             // d_k = d_v
 constexpr int kKsLd = kD + 8;       // bf16 row stride of Q, K (rows = tokens)
-constexpr int kKtLd = kC + 8;       // bf16 row stride of K^T, N, P
-constexpr int kALd = kC + 4;        // fp32 row stride of A, T
+constexpr int kKtLd = kC + 8;       // bf16 row stride of K^T, P, AN
 constexpr int kXLd = 17;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -69,10 +69,17 @@ __device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
 
 // two runs of 4 bf16 (8 bytes each): slots 0-3 from p, 4-7 from p + 16
 __device__ __forceinline__ bf16x8 lds_load4x2(const __bf16* p) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ bf16x4 lds_load4(const __bf16* p) {
+    return *reinterpret_cast<const bf16x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {
@@ -91,16 +98,13 @@ struct alignas(16) Smem {
     __bf16 Qs[kC * kKsLd];
     __bf16 Kt[kD * kKtLd];
     __bf16 Vs[kC * VLd];
-    __bf16 Ps[kC * kKtLd];
-    __bf16 Ns[kC * kKtLd];
-    union {
-        float As[kC * kALd];       // A3 -> A4
-        __bf16 Os[kC * VLd];       // B -> C (A is dead by then)
-    };
-    float Ts[kC * kALd];
-    float Xs[3 * 16 * kXLd];
+    __bf16 Ps[kC * kKtLd];        // P = M .* (n_q n_k^T) .* Q K^T, lower incl. diagonal
+    __bf16 AN[kC * kKtLd];        // -A below the diagonal blocks, T_mm - I on them
+    __bf16 Os[kC * VLd];          // output staging (B -> C)
+    float Ad[4 * 16 * kXLd];      // the four diagonal 16x16 blocks of A (fp32)
     float Ws[NCH * 4];
-    float beta[kC], gam[kC], nq[kC], nk[kC], sR[kC], sO[kC], sU[kC];
+    float beta[kC], gam[kC], nq[kC], nk[kC];
+    f32x4 tok[kC];                // per row: beta, beta Gamma n_k, Gamma n_q, exp(gamma_C - gamma) n_k
     float eC;
 };
 
@@ -117,28 +121,27 @@ __device__ __forceinline__ int64_t global_channel(int ch, int kh, int h, int zco
     return 2 * (int64_t)Hk * kD + (int64_t)h * kD + zcol0 + (ch - 2 * kD);
 }
 
-// 8 pre-conv inputs of channels gc..gc+7 at call-local token t.  t < 0 reads
-// the carried conv state (zeros for a new request); t >= L reads zeros.
-__device__ __forceinline__ void load_x8(const PrefillParams& p, int b, int64_t t, int64_t gc,
-                                        float x[8]) {
-    if (t >= 0 && t < p.seq_len) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(p.qkv) + ((int64_t)b * p.seq_len + t) * p.conv_dim + gc);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+__device__ __forceinline__ void unpack_bf16x4(uint2 raw, float x[4]) {
+    x[0] = bf16_bits_to_f32(raw.x & 0xffffu);
+    x[1] = bf16_bits_to_f32(raw.x >> 16);
+    x[2] = bf16_bits_to_f32(raw.y & 0xffffu);
+    x[3] = bf16_bits_to_f32(raw.y >> 16);
+}
+
+// SiLU with the hardware exp2 and reciprocal (about 2 ulp of fp32; the
+// result is rounded to bf16 right after).
+__device__ __forceinline__ float silu_fast(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
+
+// Pre-conv inputs of channels gc..gc+3 at call-local token t < 0: the
+// carried conv state for t >= -3 (zeros for a new request), else zeros.
+__device__ __forceinline__ void load_x4_state(const PrefillParams& p, int b, int64_t t, int64_t gc,
+                                              float x[4]) {
+    const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-            x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-        }
-    } else if (t < 0 && t >= -3 && p.conv_in) {
-        const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            x[i] = bf16_bits_to_f32(cs[((int64_t)b * p.conv_dim + gc + i) * 3 + (3 + t)]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    }
+    for (int i = 0; i < 4; ++i)
+        x[i] = (cs && t >= -3) ? bf16_bits_to_f32(cs[((int64_t)b * p.conv_dim + gc + i) * 3 + (3 + t)]) : 0.f;
 }
 
 // Copy the conv tail that ends just before call-local token `end` (the last
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     using SM = Smem<NW>;
     constexpr int VLd = SM::VLd;
     constexpr int NCH = SM::NCH;
-    constexpr int CG = NCH / 8;
+    constexpr int CG4 = NCH / 4;
     __shared__ SM sm;
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -187,13 +190,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const int64_t L = p.seq_len, sp = p.start_pos;
     const bool owns_qk_tail = (mem == 0);
 
-    // ---- one-time set-up: zero the upper tiles of N and P, conv taps -> LDS
+    // ---- one-time set-up: zero the upper tiles of P, conv taps -> LDS
     for (int e = tid; e < 6 * 256; e += NT) {
         const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
         const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
         const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
         sm.Ps[(16 * m + rr) * kKtLd + 16 * pp + cc] = __bf16(0.f);
-        sm.Ns[(16 * m + rr) * kKtLd + 16 * pp + cc] = __bf16(0.f);
     }
     for (int e = tid; e < NCH * 4; e += NT) {
         const int64_t gc = global_channel(e / 4, kh, h, zcol0, p.num_k_heads);
@@ -219,41 +221,58 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         const int64_t local0 = kc * kC - sp;   // call-local index of chunk row 0
 
         // ================= A1: front end -> Q, K, K^T, V (bf16) in LDS
-        for (int item = tid; item < CG * 8; item += NT) {
-            const int cg = item % CG, seg = item / CG;
-            const int ch0 = cg * 8;
+        for (int item = tid; item < CG4 * 8; item += NT) {
+            const int cg = item % CG4, seg = item / CG4;
+            const int ch0 = cg * 4;
             const int64_t gc = global_channel(ch0, kh, h, zcol0, p.num_k_heads);
             const int tau0 = seg * 8;
-            float w[4][8];
+            const int64_t t_first = local0 + tau0 - 3;   // first of the 11 rows this item reads
+            // All eleven 8-byte row loads are issued unconditionally (the token
+            // index is clamped into the call, L >= 1 here), so they are in
+            // flight together; rows before the call are fixed up below.
+            uint2 raw[11];
+            const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * L * p.conv_dim + gc;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 11; ++j) {
+                const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
+                raw[j] = *reinterpret_cast<const uint2*>(src + tc * p.conv_dim);
+            }
+            float w[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) w[j][i] = sm.Ws[(ch0 + i) * 4 + j];
-            float h0[8], h1[8], h2[8];
-            load_x8(p, b, local0 + tau0 - 3, gc, h0);
-            load_x8(p, b, local0 + tau0 - 2, gc, h1);
-            load_x8(p, b, local0 + tau0 - 1, gc, h2);
+            float hist[3][4];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) unpack_bf16x4(raw[j], hist[j]);
+            if (t_first < 0) {
+                // rows before the call: the carried conv state (zeros if none)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    if (t_first + j < 0) load_x4_state(p, b, t_first + j, gc, hist[j]);
+            }
 #pragma unroll
             for (int tt = 0; tt < 8; ++tt) {
                 const int tau = tau0 + tt;
                 const int64_t t = local0 + tau;
-                float x[8];
-                load_x8(p, b, t, gc, x);
+                float x[4];
+                unpack_bf16x4(raw[3 + tt], x);
+                if (t < 0) load_x4_state(p, b, t, gc, x);
                 const bool valid = t >= 0 && t < L;
-                f32x8 u;
+                f32x4 u;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], h2[i], fmaf(w[1][i], h1[i], w[0][i] * h0[i])));
-                    u[i] = valid ? silu_f32(y) : 0.f;
-                    h0[i] = h1[i];
-                    h1[i] = h2[i];
-                    h2[i] = x[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], hist[2][i], fmaf(w[1][i], hist[1][i], w[0][i] * hist[0][i])));
+                    u[i] = valid ? silu_fast(y) : 0.f;
+                    hist[0][i] = hist[1][i];
+                    hist[1][i] = hist[2][i];
+                    hist[2][i] = x[i];
                 }
-                const bf16x8 ub = __builtin_convertvector(u, bf16x8);
+                const bf16x4 ub = __builtin_convertvector(u, bf16x4);
                 __bf16* dst = ch0 < kD ? &sm.Qs[tau * kKsLd + ch0]
                             : ch0 < 2 * kD ? &sm.Ks[tau * kKsLd + ch0 - kD]
                                            : &sm.Vs[tau * VLd + ch0 - 2 * kD];
-                *reinterpret_cast<bf16x8*>(dst) = ub;
+                *reinterpret_cast<bf16x4*>(dst) = ub;
             }
         }
         __syncthreads();
@@ -306,14 +325,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         }
         __syncthreads();
 
-        // ================= A3: derived row scales; K K^T, Q K^T tiles on MFMA
+        // ================= A3: per-row scales; K K^T, Q K^T tiles on MFMA
         if (tid < kC) {
             const float gl = sm.gam[tid], gC = sm.gam[kC - 1];
-            const float e = expf(gl);
-            sm.sR[tid] = sm.beta[tid] * e * sm.nk[tid];
-            sm.sO[tid] = e * sm.nq[tid];
-            sm.sU[tid] = expf(gC - gl) * sm.nk[tid];
-            if (tid == 0) sm.eC = expf(gC);
+            const float e = expf(gl), nkv = sm.nk[tid], bv = sm.beta[tid];
+            sm.tok[tid] = f32x4{bv, bv * e * nkv, e * sm.nq[tid], expf(gC - gl) * nkv};
         }
         for (int pi = wave; pi < 10; pi += NW) {
             int m, pp;
@@ -333,64 +349,34 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 16 * m + 4 * lq + e;
-                const float dec = ii <= rr ? expf(sm.gam[rr] - gi) : 0.f;
+                const float dec = ii <= rr ? __expf(sm.gam[rr] - gi) : 0.f;
                 const float av = ii < rr ? sm.beta[rr] * sm.nk[rr] * nki * dec * accG[e] : 0.f;
                 const float pv = ii <= rr ? sm.nq[rr] * nki * dec * accQ[e] : 0.f;
-                sm.As[rr * kALd + ii] = av;
+                if (m == pp) sm.Ad[(m * 16 + 4 * lq + e) * kXLd + li] = av;
+                else sm.AN[rr * kKtLd + ii] = __bf16(-av);
                 sm.Ps[rr * kKtLd + ii] = __bf16(pv);
             }
         }
         __syncthreads();
 
-        // ================= A4: T = (I + A)^-1, blocked forward substitution
+        // ================= A4: inverses of the four diagonal blocks
+        // (I + A_mm)^-1 = I + N_mm by substitution, one wave, lane = (block m,
+        // column c).  The off-diagonal coupling is applied in B by blocked
+        // forward substitution, so no other part of (I + A)^-1 is formed.
         if (wave == 0) {
-            // diagonal block m, column c: solve (I + A_mm) x = e_c
             const int m = lane / 16, c = lane % 16;
-            const float* Arow = sm.As + 16 * m * kALd + 16 * m;
+            const float* Ab = sm.Ad + m * 16 * kXLd;
             float x[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < rr; ++i) acc = fmaf(Arow[rr * kALd + i], x[i], acc);
+                for (int i = 0; i < rr; ++i) acc = fmaf(Ab[rr * kXLd + i], x[i], acc);
                 x[rr] = rr < c ? 0.f : (rr == c ? 1.f : -acc);
             }
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) sm.Ts[(16 * m + rr) * kALd + 16 * m + c] = x[rr];
-        }
-        __syncthreads();
-        for (int mb = 1; mb < 4; ++mb) {
-            // X_p = sum_{k=p}^{mb-1} A_{mb,k} T_{k,p}
-            for (int e = tid; e < mb * 256; e += NT) {
-                const int pb = e / 256, rr = (e / 16) % 16, cc = e % 16;
-                float acc = 0.f;
-                for (int kb = pb; kb < mb; ++kb) {
-                    const float* Ar = sm.As + (16 * mb + rr) * kALd + 16 * kb;
-                    const float* Tc = sm.Ts + (16 * kb) * kALd + 16 * pb + cc;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc = fmaf(Ar[i], Tc[i * kALd], acc);
-                }
-                sm.Xs[(pb * 16 + rr) * kXLd + cc] = acc;
-            }
-            __syncthreads();
-            // T_{mb,p} = -T_{mb,mb} X_p
-            for (int e = tid; e < mb * 256; e += NT) {
-                const int pb = e / 256, rr = (e / 16) % 16, cc = e % 16;
-                const float* Tr = sm.Ts + (16 * mb + rr) * kALd + 16 * mb;
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc = fmaf(Tr[i], sm.Xs[(pb * 16 + i) * kXLd + cc], acc);
-                sm.Ts[(16 * mb + rr) * kALd + 16 * pb + cc] = -acc;
-            }
-            __syncthreads();
-        }
-        // N = T - I (bf16) on the lower tiles
-        for (int e = tid; e < 10 * 256; e += NT) {
-            int m, pp;
-            tile_pair(e / 256, m, pp);
-            const int rr = 16 * m + (e / 16) % 16, cc = 16 * pp + e % 16;
-            const float v = sm.Ts[rr * kALd + cc] - (rr == cc ? 1.f : 0.f);
-            sm.Ns[rr * kKtLd + cc] = __bf16(v);
+            for (int rr = 0; rr < 16; ++rr)
+                sm.AN[(16 * m + rr) * kKtLd + 16 * m + c] = __bf16(rr == c ? 0.f : x[rr]);
         }
         __syncthreads();
 
@@ -412,34 +398,41 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
                     QS[m] = mfma16(lds_load4x2(&sm.Qs[off]), Bs[ks], QS[m]);
                 }
             }
-            // R = beta V - beta Gamma n_k (K S0); Delta = R + (T - I) R
+            // R = beta V - beta Gamma n_k (K S0)
             f32x4 R[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tau = 16 * m + 4 * lq + e;
-                    const float vv = float(sm.Vs[tau * VLd + cw]);
-                    R[m][e] = sm.beta[tau] * vv - sm.sR[tau] * KS[m][e];
+                    const f32x4 tk = sm.tok[tau];
+                    R[m][e] = tk[0] * float(sm.Vs[tau * VLd + cw]) - tk[1] * KS[m][e];
                 }
-            const bf16x8 BR[2] = {to_bf16x8(R[0], R[1]), to_bf16x8(R[2], R[3])};
+            // (I + A) Delta = R by blocked forward substitution over the four
+            // 16-row blocks: Y_m = R_m - sum_{k<m} A_mk Delta_k, then
+            // Delta_m = Y_m + N_mm Y_m.  The fp32 accumulator carries R and
+            // Y exactly; only the coupling terms see bf16 operands.
             f32x4 Dl[4];
+            bf16x4 Db[4];
+            const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                f32x4 acc = R[m];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || m >= 2)
-                        acc = mfma16(lds_load4x2(&sm.Ns[(16 * m + li) * kKtLd + 32 * ks + 4 * lq]), BR[ks], acc);
-                Dl[m] = acc;
+                const __bf16* arow = &sm.AN[(16 * m + li) * kKtLd + 4 * lq];
+                f32x4 y = R[m];
+                if (m == 1) y = mfma16(cat4(lds_load4(arow), z4), cat4(Db[0], z4), y);
+                if (m >= 2) y = mfma16(cat4(lds_load4(arow), lds_load4(arow + 16)), cat4(Db[0], Db[1]), y);
+                if (m == 3) y = mfma16(cat4(lds_load4(arow + 32), z4), cat4(Db[2], z4), y);
+                const bf16x4 yb = __builtin_convertvector(y, bf16x4);
+                Dl[m] = mfma16(cat4(lds_load4(arow + 16 * m), z4), cat4(yb, z4), y);
+                Db[m] = __builtin_convertvector(Dl[m], bf16x4);
             }
             // O = Gamma n_q (Q S0) + P Delta -> LDS staging
-            const bf16x8 BD[2] = {to_bf16x8(Dl[0], Dl[1]), to_bf16x8(Dl[2], Dl[3])};
+            const bf16x8 BD[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = sm.sO[16 * m + 4 * lq + e] * QS[m][e];
+                for (int e = 0; e < 4; ++e) acc[e] = sm.tok[16 * m + 4 * lq + e][2] * QS[m][e];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     if (ks == 0 || m >= 2)
@@ -452,7 +445,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Dq[m][e] = sm.sU[16 * m + 4 * lq + e] * Dl[m][e];
+                for (int e = 0; e < 4; ++e) Dq[m][e] = sm.tok[16 * m + 4 * lq + e][3] * Dl[m][e];
             bf16x8 BH[2], BL[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -464,7 +457,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
                                   Dq[2 * ks + 1][2] - back[6], Dq[2 * ks + 1][3] - back[7]};
                 BL[ks] = to_bf16x8(l0, l1);
             }
-            const float eC = sm.eC;
+            const float eC = expf(sm.gam[kC - 1]);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 f32x4 acc = S[t] * eC;
