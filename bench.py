@@ -49,6 +49,28 @@ def decode_bytes(B, Hk, Hv, d=128) -> int:
             + 2 * B * Hv * 2 + conv_dim * 4 * 2 + 2 * Hv * 4)
 
 
+def profiled_traffic(profile: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None
+    when the kernel's sources changed after the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "Command")):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_causal_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (source, "gdn_common.h", "gdn_launch.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def time_events(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -136,6 +158,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB fp32 elementwise copy (read 1 GiB, write 1 GiB) "
+                         "three times, the reference for scaling HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -172,7 +197,9 @@ def main():
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": achieved / 1e12,
                      "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_FLOPS, "traffic": None,
+                     "frac": achieved / BF16_PEAK_FLOPS,
+                     "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
+                                                 "gdn_prefill.hip"),
                      "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
                      "hbm_floor_frac": byts / t / HBM_PEAK_BYTES},
     }
@@ -184,11 +211,20 @@ def main():
             "us_per_step": td * 1e6, "tokens_per_s": wd.batch / td, "bytes_per_step": bd,
             "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": bd / td / 1e9,
                          "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
-                         "frac": bd / td / HBM_PEAK_BYTES, "traffic": None},
+                         "frac": bd / td / HBM_PEAK_BYTES,
+                         "traffic": profiled_traffic("decode_step_kernel_qwen36-27b_decode_b32.md",
+                                                     "gdn_decode.hip")},
         }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    if args.calibrate_copy:
+        n = 1 << 28
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
     rec["gpu"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
 

@@ -527,21 +527,21 @@ bool prefill_supported(int head_k_dim, int head_v_dim, int io_dtype, int conv_ke
            chunk == kC;
 }
 
-// Columns of S per workgroup: the whole head when there are enough (b, head)
-// chains to fill the chip, else split d_v so that more CUs share the chain.
-int prefill_waves(int64_t chains) {
+// Columns of S per workgroup.  One workgroup per (b, head) with all 128
+// columns (8 waves) is fastest on every measured workload, including the
+// 48-chain 16K prefill; 2 and 4 waves remain selectable for experiments
+// through GDN_PREFILL_WAVES.
+int prefill_waves() {
     if (const char* env = getenv("GDN_PREFILL_WAVES")) {
         const int v = atoi(env);
         if (v == 2 || v == 4 || v == 8) return v;
     }
-    if (chains >= 192) return 8;
-    if (chains >= 96) return 4;
-    return 2;
+    return 8;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    switch (prefill_waves((int64_t)p.batch * p.num_v_heads)) {
+    switch (prefill_waves()) {
         case 8: return launch_nw<8>(p, stream);
         case 4: return launch_nw<4>(p, stream);
         default: return launch_nw<2>(p, stream);
