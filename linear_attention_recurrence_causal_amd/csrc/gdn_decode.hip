@@ -21,6 +21,8 @@
 // NRG full row segments with 16-byte coalesced loads.  S' lives in registers
 // between the read and the write.  Reductions over rows use a fixed
 // butterfly + fixed cross-wave order (deterministic, no atomics).
+#include <cstdlib>
+
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -197,12 +199,20 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Columns of S per workgroup: all of d_v by default (1536 workgroups on the
+// 32 x 48 head decode, all resident at once; measured fastest against 32 and
+// 64); GDN_DECODE_COLS = 32 / 64 / 128 selects another split.
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
-    switch (p.head_v_dim) {
+    int cols = p.head_v_dim;
+    if (const char* env = getenv("GDN_DECODE_COLS")) {
+        const int v = atoi(env);
+        if ((v == 32 || v == 64 || v == 128) && v <= p.head_v_dim) cols = v;
+    }
+    switch (cols) {
         case 32: return launch_typed<IO, DK, 32>(p, stream);
         case 64: return launch_typed<IO, DK, 64>(p, stream);
-        case 128: return launch_typed<IO, DK, 64>(p, stream);
+        case 128: return launch_typed<IO, DK, 128>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

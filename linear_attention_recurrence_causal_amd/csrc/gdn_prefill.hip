@@ -52,6 +52,7 @@ constexpr int kD = 128;             // d_k = d_v
 constexpr int kKsLd = kD + 8;       // bf16 row stride of Q, K (rows = tokens)
 constexpr int kKtLd = kC + 8;       // bf16 row stride of K^T, P, AN
 constexpr int kXLd = 17;
+constexpr int kVtLd = kC + 12;      // bf16 row stride of V^T
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -97,16 +98,30 @@ struct alignas(16) Smem {
     __bf16 Ks[kC * kKsLd];
     __bf16 Qs[kC * kKsLd];
     __bf16 Kt[kD * kKtLd];
-    __bf16 Vs[kC * VLd];
+    __bf16 Vt[N * kVtLd];         // V transposed: [column][token]
     __bf16 Ps[kC * kKtLd];        // P = M .* (n_q n_k^T) .* Q K^T, lower incl. diagonal
     __bf16 AN[kC * kKtLd];        // -A below the diagonal blocks, T_mm - I on them
     __bf16 Os[kC * VLd];          // output staging (B -> C)
-    float Ad[4 * 16 * kXLd];      // the four diagonal 16x16 blocks of A (fp32)
-    float Ws[NCH * 4];
-    float beta[kC], gam[kC], nq[kC], nk[kC];
-    f32x4 tok[kC];                // per row: beta, beta Gamma n_k, Gamma n_q, exp(gamma_C - gamma) n_k
+    float AdT[4 * 16 * kXLd];     // the four diagonal 16x16 blocks of A, transposed (fp32)
+    float Ws[4 * NCH];           // conv taps, [tap][channel]
+    alignas(16) float beta[kC];
+    alignas(16) float gam[kC];
+    alignas(16) float nq[kC];
+    alignas(16) float nk[kC];
+    f32x4 Graw[(NW == 8 ? 20 : 1) * 64];  // raw Gram tiles between A2 and A3 (8 waves)
+    float tokS[4][kC];            // per row: beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k
     float eC;
 };
+
+// Column order inside Q, K (d_k columns) and K^T, P, AN (token columns).  An
+// index x = 32a + 16h + 4q + e is stored at 32a + 8q + 4h + e, so the eight
+// reduction slots that lane group q of v_mfma_f32_16x16x32_bf16 needs for
+// k-step a (indices 32a + 4q + {0..3} and 32a + 16 + 4q + {0..3}, the order
+// in which an accumulator tile is reused as a B operand) are one contiguous
+// 16-byte run, and runs of four consecutive indices stay contiguous.
+__device__ __forceinline__ int pos(int x) {
+    return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
+}
 
 // lower 16x16 tile pairs (m, p), p <= m, in a fixed order
 __device__ __forceinline__ void tile_pair(int idx, int& m, int& p) {
@@ -160,6 +175,143 @@ __device__ __forceinline__ void write_tail(const PrefillParams& p, int b, int64_
     }
 }
 
+constexpr int kTilesPerWave = 4;   // 20 Gram tiles over waves 3..7
+
+// Raw tile ti of K K^T (ti < 10) or Q K^T (ti >= 10) on the lower 16x16 tile
+// pair tile_pair(ti % 10): bf16 operands straight from LDS, fp32 accumulate.
+template <int NW>
+__device__ __forceinline__ f32x4 gram_tile(const Smem<NW>& sm, int ti, int li, int lq) {
+    int m, pp;
+    tile_pair(ti >= 10 ? ti - 10 : ti, m, pp);
+    const __bf16* arow = (ti >= 10 ? sm.Qs : sm.Ks) + (16 * m + li) * kKsLd + 8 * lq;
+    const __bf16* brow = sm.Ks + (16 * pp + li) * kKsLd + 8 * lq;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16(lds_load8(arow + 32 * ks), lds_load8(brow + 32 * ks), acc);
+    return acc;
+}
+
+// Decay masks and row/column scales of one lower tile pair (lane l of the
+// accumulator layout: column 16 pp + l % 16, rows 16 m + 4 (l / 16) + e):
+//   A[r,i] = beta_r n_k[r] n_k[i] exp(gamma_r - gamma_i) (K K^T)[r,i], i < r
+//     -> -A (bf16) off the diagonal blocks, fp32 transposed on them
+//   P[r,i] = n_q[r] n_k[i] exp(gamma_r - gamma_i) (Q K^T)[r,i], i <= r (bf16)
+template <int NW>
+__device__ __forceinline__ void mask_pair(Smem<NW>& sm, int pi, f32x4 g, f32x4 qk, int l) {
+    const int li = l % 16, lq = l / 16;
+    int m, pp;
+    tile_pair(pi, m, pp);
+    const int ii = 16 * pp + li, r0 = 16 * m + 4 * lq;
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.gam[r0]);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[r0]);
+    const f32x4 kr = *reinterpret_cast<const f32x4*>(&sm.nk[r0]);
+    const f32x4 qr = *reinterpret_cast<const f32x4*>(&sm.nq[r0]);
+    const float gi = sm.gam[ii], nki = sm.nk[ii];
+    const int pii = pos(ii);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int rr = r0 + e;
+        const float dec = ii <= rr ? __expf(gr[e] - gi) * nki : 0.f;
+        const float av = ii < rr ? br[e] * kr[e] * dec * g[e] : 0.f;
+        sm.Ps[rr * kKtLd + pii] = __bf16(qr[e] * dec * qk[e]);
+        if (m == pp) sm.AdT[(m * 16 + li) * kXLd + 4 * lq + e] = av;
+        else sm.AN[rr * kKtLd + pii] = __bf16(-av);
+    }
+}
+
+// Per-row scales of the state phase for row r = lane (one wave):
+//   beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k
+template <int NW>
+__device__ __forceinline__ void row_scales(Smem<NW>& sm, int r) {
+    const float gl = sm.gam[r], gC = sm.gam[kC - 1];
+    const float e = expf(gl), nkv = sm.nk[r], bv = sm.beta[r];
+    sm.tokS[0][r] = bv;
+    sm.tokS[1][r] = bv * e * nkv;
+    sm.tokS[2][r] = e * sm.nq[r];
+    sm.tokS[3][r] = expf(gC - gl) * nkv;
+}
+
+// Front end of one work item: 4 channels x 8 tokens of the chunk.  The
+// eleven 8-byte row loads (3 halo rows + 8) are issued together.  INTERIOR:
+// every row lies inside the call.  Otherwise row indices are clamped into the
+// call, rows before it are replaced by the carried conv state and rows outside
+// it produce zeros.
+template <bool INTERIOR, int NW>
+__device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm, int b, int kh, int h,
+                                           int zcol0, int64_t local0, int item) {
+    constexpr int NCH = Smem<NW>::NCH;
+    constexpr int CG4 = NCH / 4;
+    const int64_t L = p.seq_len;
+    const int cg = item % CG4, seg = item / CG4;
+    const int ch0 = cg * 4;
+    const int64_t gc = global_channel(ch0, kh, h, zcol0, p.num_k_heads);
+    const int tau0 = seg * 8;
+    const int64_t t_first = local0 + tau0 - 3;
+    uint2 raw[11];
+    if (INTERIOR) {
+        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) +
+                              ((int64_t)b * L + t_first) * p.conv_dim + gc;
+        const int cd = (int)p.conv_dim;
+#pragma unroll
+        for (int j = 0; j < 11; ++j) raw[j] = *reinterpret_cast<const uint2*>(src + j * cd);
+    } else {
+        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * L * p.conv_dim + gc;
+#pragma unroll
+        for (int j = 0; j < 11; ++j) {
+            const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
+            raw[j] = *reinterpret_cast<const uint2*>(src + tc * p.conv_dim);
+        }
+    }
+    float w[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(&sm.Ws[j * NCH + ch0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[j][i] = wv[i];
+    }
+    float hist[3][4];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) unpack_bf16x4(raw[j], hist[j]);
+    if (!INTERIOR && t_first < 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (t_first + j < 0) load_x4_state(p, b, t_first + j, gc, hist[j]);
+    }
+    const bool is_v = ch0 >= 2 * kD;
+    __bf16* dst0 = ch0 < kD ? &sm.Qs[pos(ch0)] : &sm.Ks[pos(ch0 - kD)];
+    bf16x8 vcol[4];   // v channels: 8 tokens of each of the 4 channels, stored as V^T rows
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const int tau = tau0 + tt;
+        const int64_t t = local0 + tau;
+        float x[4];
+        unpack_bf16x4(raw[3 + tt], x);
+        if (!INTERIOR && t < 0) load_x4_state(p, b, t, gc, x);
+        const bool valid = INTERIOR || (t >= 0 && t < L);
+        f32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], hist[2][i], fmaf(w[1][i], hist[1][i], w[0][i] * hist[0][i])));
+            u[i] = valid ? silu_fast(y) : 0.f;
+            hist[0][i] = hist[1][i];
+            hist[1][i] = hist[2][i];
+            hist[2][i] = x[i];
+        }
+        const bf16x4 ub = __builtin_convertvector(u, bf16x4);
+        if (is_v) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vcol[i][tt] = ub[i];
+        } else {
+            *reinterpret_cast<bf16x4*>(dst0 + tau * kKsLd) = ub;
+        }
+    }
+    if (is_v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<bf16x8*>(&sm.Vt[(ch0 - 2 * kD + i) * kVtLd + tau0]) = vcol[i];
+    }
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     constexpr int NT = 64 * NW;
@@ -169,6 +321,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     constexpr int VLd = SM::VLd;
     constexpr int NCH = SM::NCH;
     constexpr int CG4 = NCH / 4;
+    static_assert(NCH % 4 == 0, "channel groups of 4");
     __shared__ SM sm;
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -195,11 +348,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
         const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
         const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
-        sm.Ps[(16 * m + rr) * kKtLd + 16 * pp + cc] = __bf16(0.f);
+        sm.Ps[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
     }
     for (int e = tid; e < NCH * 4; e += NT) {
-        const int64_t gc = global_channel(e / 4, kh, h, zcol0, p.num_k_heads);
-        sm.Ws[e] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + (e % 4)]);
+        // taps stored [tap][channel] so that four channels of one tap are one
+        // conflict-free 16-byte read
+        const int ch = e % NCH, j = e / NCH;
+        const int64_t gc = global_channel(ch, kh, h, zcol0, p.num_k_heads);
+        sm.Ws[e] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + j]);
     }
     const float A_log_h = p.A_log[h], dt_h = p.dt_bias[h];
     const float neg_A = -expf(A_log_h);
@@ -221,59 +377,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         const int64_t local0 = kc * kC - sp;   // call-local index of chunk row 0
 
         // ================= A1: front end -> Q, K, K^T, V (bf16) in LDS
-        for (int item = tid; item < CG4 * 8; item += NT) {
-            const int cg = item % CG4, seg = item / CG4;
-            const int ch0 = cg * 4;
-            const int64_t gc = global_channel(ch0, kh, h, zcol0, p.num_k_heads);
-            const int tau0 = seg * 8;
-            const int64_t t_first = local0 + tau0 - 3;   // first of the 11 rows this item reads
-            // All eleven 8-byte row loads are issued unconditionally (the token
-            // index is clamped into the call, L >= 1 here), so they are in
-            // flight together; rows before the call are fixed up below.
-            uint2 raw[11];
-            const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * L * p.conv_dim + gc;
-#pragma unroll
-            for (int j = 0; j < 11; ++j) {
-                const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
-                raw[j] = *reinterpret_cast<const uint2*>(src + tc * p.conv_dim);
-            }
-            float w[4][4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w[j][i] = sm.Ws[(ch0 + i) * 4 + j];
-            float hist[3][4];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) unpack_bf16x4(raw[j], hist[j]);
-            if (t_first < 0) {
-                // rows before the call: the carried conv state (zeros if none)
-#pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    if (t_first + j < 0) load_x4_state(p, b, t_first + j, gc, hist[j]);
-            }
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                const int tau = tau0 + tt;
-                const int64_t t = local0 + tau;
-                float x[4];
-                unpack_bf16x4(raw[3 + tt], x);
-                if (t < 0) load_x4_state(p, b, t, gc, x);
-                const bool valid = t >= 0 && t < L;
-                f32x4 u;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], hist[2][i], fmaf(w[1][i], hist[1][i], w[0][i] * hist[0][i])));
-                    u[i] = valid ? silu_fast(y) : 0.f;
-                    hist[0][i] = hist[1][i];
-                    hist[1][i] = hist[2][i];
-                    hist[2][i] = x[i];
-                }
-                const bf16x4 ub = __builtin_convertvector(u, bf16x4);
-                __bf16* dst = ch0 < kD ? &sm.Qs[tau * kKsLd + ch0]
-                            : ch0 < 2 * kD ? &sm.Ks[tau * kKsLd + ch0 - kD]
-                                           : &sm.Vs[tau * VLd + ch0 - 2 * kD];
-                *reinterpret_cast<bf16x4*>(dst) = ub;
-            }
+        // Interior chunks (all 64 rows and the 3-row halo inside the call) take
+        // a path with no clamping and no masking.
+        if (local0 >= 3 && local0 + kC <= L) {
+            for (int item = tid; item < CG4 * 8; item += NT)
+                front_item<true, NW>(p, sm, b, kh, h, zcol0, local0, item);
+        } else {
+            for (int item = tid; item < CG4 * 8; item += NT)
+                front_item<false, NW>(p, sm, b, kh, h, zcol0, local0, item);
         }
         __syncthreads();
 
@@ -282,10 +393,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
             // K^T[d][tau0 .. tau0+7] from eight K rows; lanes walk d, so the
             // 2-byte LDS reads of one instruction hit consecutive addresses
             const int d = e % kD, tau0 = (e / kD) * 8;
-            bf16x8 col;
+            const int pd = pos(d);
+            bf16x4 c0, c1;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) col[i] = sm.Ks[(tau0 + i) * kKsLd + d];
-            *reinterpret_cast<bf16x8*>(&sm.Kt[d * kKtLd + tau0]) = col;
+            for (int i = 0; i < 4; ++i) {
+                c0[i] = sm.Ks[(tau0 + i) * kKsLd + pd];
+                c1[i] = sm.Ks[(tau0 + 4 + i) * kKsLd + pd];
+            }
+            *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0)]) = c0;
+            *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0 + 4)]) = c1;
         }
         for (int job = tid; job < 3 * kC; job += NT) {
             if (job < kC) {
@@ -323,39 +439,30 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
                 (isq ? sm.nq : sm.nk)[tau] = n;
             }
         }
+        // Raw K K^T / Q K^T tiles need only Q and K: with 8 waves, waves 3..7
+        // (idle after the K^T copy) compute them here into LDS (fp32, in the
+        // accumulator layout); A3 applies the masks.
+        if constexpr (NW == 8) {
+            if (wave >= 3) {
+#pragma unroll 1
+                for (int k = 0; k < kTilesPerWave; ++k) {
+                    const int ti = (wave - 3) + 5 * k;
+                    sm.Graw[ti * 64 + lane] = gram_tile(sm, ti, li, lq);
+                }
+            }
+        }
         __syncthreads();
 
-        // ================= A3: per-row scales; K K^T, Q K^T tiles on MFMA
-        if (tid < kC) {
-            const float gl = sm.gam[tid], gC = sm.gam[kC - 1];
-            const float e = expf(gl), nkv = sm.nk[tid], bv = sm.beta[tid];
-            sm.tok[tid] = f32x4{bv, bv * e * nkv, e * sm.nq[tid], expf(gC - gl) * nkv};
-        }
-        for (int pi = wave; pi < 10; pi += NW) {
-            int m, pp;
-            tile_pair(pi, m, pp);
-            f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int col = 32 * ks + 8 * lq;
-                const bf16x8 ak = lds_load8(&sm.Ks[(16 * m + li) * kKsLd + col]);
-                const bf16x8 aq = lds_load8(&sm.Qs[(16 * m + li) * kKsLd + col]);
-                const bf16x8 bk = lds_load8(&sm.Ks[(16 * pp + li) * kKsLd + col]);
-                accG = mfma16(ak, bk, accG);
-                accQ = mfma16(aq, bk, accQ);
-            }
-            const int ii = 16 * pp + li;
-            const float gi = sm.gam[ii], nki = sm.nk[ii];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * m + 4 * lq + e;
-                const float dec = ii <= rr ? __expf(sm.gam[rr] - gi) : 0.f;
-                const float av = ii < rr ? sm.beta[rr] * sm.nk[rr] * nki * dec * accG[e] : 0.f;
-                const float pv = ii <= rr ? sm.nq[rr] * nki * dec * accQ[e] : 0.f;
-                if (m == pp) sm.Ad[(m * 16 + 4 * lq + e) * kXLd + li] = av;
-                else sm.AN[rr * kKtLd + ii] = __bf16(-av);
-                sm.Ps[rr * kKtLd + ii] = __bf16(pv);
-            }
+        // ================= A3: decay masks on the Gram tiles; per-row scales
+        if constexpr (NW == 8) {
+            // job = (tile pair, lane): both the K K^T and the Q K^T tile of one
+            // lower tile pair, 640 jobs over 512 threads, branch-free within a wave
+            for (int j = tid; j < 10 * 64; j += NT) mask_pair(sm, j >> 6, sm.Graw[j], sm.Graw[640 + j], j & 63);
+            if (wave == NW - 1) row_scales(sm, lane);
+        } else {
+            if (wave == 0) row_scales(sm, lane);
+            for (int pi = wave - 1; pi >= 0 && pi < 10; pi += NW - 1)
+                mask_pair(sm, pi, gram_tile(sm, pi, li, lq), gram_tile(sm, 10 + pi, li, lq), lane);
         }
         __syncthreads();
 
@@ -364,23 +471,39 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         // column c).  The off-diagonal coupling is applied in B by blocked
         // forward substitution, so no other part of (I + A)^-1 is formed.
         if (wave == 0) {
+            // column c of block m; right-looking: once x[i] is final, subtract
+            // its contribution from every later row (column i of A_mm is row i
+            // of AdT), so the dependent chain is one FMA per row
             const int m = lane / 16, c = lane % 16;
-            const float* Ab = sm.Ad + m * 16 * kXLd;
+            const float* At = sm.AdT + m * 16 * kXLd;
             float x[16];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float acc = 0.f;
+            for (int rr = 0; rr < 16; ++rr) x[rr] = rr == c ? 1.f : 0.f;
+            // column i of A_mm is loaded one step ahead (two 16-float buffers)
+            float col[2][16];
 #pragma unroll
-                for (int i = 0; i < rr; ++i) acc = fmaf(Ab[rr * kXLd + i], x[i], acc);
-                x[rr] = rr < c ? 0.f : (rr == c ? 1.f : -acc);
+            for (int rr = 0; rr < 16; ++rr) col[0][rr] = At[rr];
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+                if (i + 1 < 15) {
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) col[(i + 1) & 1][rr] = At[(i + 1) * kXLd + rr];
+                }
+                const float xi = x[i];
+#pragma unroll
+                for (int rr = i + 1; rr < 16; ++rr) x[rr] = fmaf(-col[i & 1][rr], xi, x[rr]);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
-                sm.AN[(16 * m + rr) * kKtLd + 16 * m + c] = __bf16(rr == c ? 0.f : x[rr]);
+                sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
         }
         __syncthreads();
 
         // ================= B: state-dependent products, per wave
+        // Every block of LDS operands is loaded in one batch (fenced with a
+        // scheduling barrier) before the products that use it, so a wave has
+        // many reads in flight instead of one read per MFMA.
         {
             const int cw = 16 * wave + li;   // column inside the slice
             bf16x8 Bs[4];
@@ -388,26 +511,55 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
             for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
             f32x4 KS[4], QS[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                KS[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                QS[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int mh = 0; mh < 4; mh += 2) {
+                bf16x8 ak[2][4], aq[2][4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int off = (16 * m + li) * kKsLd + 32 * ks + 4 * lq;
-                    KS[m] = mfma16(lds_load4x2(&sm.Ks[off]), Bs[ks], KS[m]);
-                    QS[m] = mfma16(lds_load4x2(&sm.Qs[off]), Bs[ks], QS[m]);
+                for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int off = (16 * (mh + mm) + li) * kKsLd + 32 * ks + 8 * lq;
+                        ak[mm][ks] = lds_load8(&sm.Ks[off]);
+                        aq[mm][ks] = lds_load8(&sm.Qs[off]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    f32x4 k = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        k = mfma16(ak[mm][ks], Bs[ks], k);
+                        q = mfma16(aq[mm][ks], Bs[ks], q);
+                    }
+                    KS[mh + mm] = k;
+                    QS[mh + mm] = q;
                 }
             }
+            // row scales and V for this lane's 16 rows (16m + 4 lq + e), and the
+            // A / P operands of the substitution and of P Delta
+            f32x4 sb[4], sr[4];
+            bf16x4 vv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r0 = 16 * m + 4 * lq;
+                sb[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[0][r0]);
+                sr[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[1][r0]);
+                vv[m] = lds_load4(&sm.Vt[cw * kVtLd + r0]);
+            }
+            // AN row of this lane in block row m; token block k sits at
+            // 32(k/2) + 8 lq + 4(k%2)
+            const __bf16* an = &sm.AN[li * kKtLd + 8 * lq];
+            const bf16x4 d0 = lds_load4(an), d1 = lds_load4(an + 16 * kKtLd + 4);
+            const bf16x4 d2 = lds_load4(an + 32 * kKtLd + 32), d3 = lds_load4(an + 48 * kKtLd + 36);
+            const bf16x4 a10 = lds_load4(an + 16 * kKtLd);
+            const bf16x8 a2x = lds_load8(an + 32 * kKtLd), a3x = lds_load8(an + 48 * kKtLd);
+            const bf16x4 a32 = lds_load4(an + 48 * kKtLd + 32);
+            __builtin_amdgcn_sched_barrier(0);
             // R = beta V - beta Gamma n_k (K S0)
             f32x4 R[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tau = 16 * m + 4 * lq + e;
-                    const f32x4 tk = sm.tok[tau];
-                    R[m][e] = tk[0] * float(sm.Vs[tau * VLd + cw]) - tk[1] * KS[m][e];
-                }
+                for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
             // (I + A) Delta = R by blocked forward substitution over the four
             // 16-row blocks: Y_m = R_m - sum_{k<m} A_mk Delta_k, then
             // Delta_m = Y_m + N_mm Y_m.  The fp32 accumulator carries R and
@@ -415,57 +567,78 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
             f32x4 Dl[4];
             bf16x4 Db[4];
             const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
+            const bf16x4 dg[4] = {d0, d1, d2, d3};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const __bf16* arow = &sm.AN[(16 * m + li) * kKtLd + 4 * lq];
                 f32x4 y = R[m];
-                if (m == 1) y = mfma16(cat4(lds_load4(arow), z4), cat4(Db[0], z4), y);
-                if (m >= 2) y = mfma16(cat4(lds_load4(arow), lds_load4(arow + 16)), cat4(Db[0], Db[1]), y);
-                if (m == 3) y = mfma16(cat4(lds_load4(arow + 32), z4), cat4(Db[2], z4), y);
+                if (m == 1) y = mfma16(cat4(a10, z4), cat4(Db[0], z4), y);
+                if (m == 2) y = mfma16(a2x, cat4(Db[0], Db[1]), y);
+                if (m == 3) {
+                    y = mfma16(a3x, cat4(Db[0], Db[1]), y);
+                    y = mfma16(cat4(a32, z4), cat4(Db[2], z4), y);
+                }
                 const bf16x4 yb = __builtin_convertvector(y, bf16x4);
-                Dl[m] = mfma16(cat4(lds_load4(arow + 16 * m), z4), cat4(yb, z4), y);
+                Dl[m] = mfma16(cat4(dg[m], z4), cat4(yb, z4), y);
                 Db[m] = __builtin_convertvector(Dl[m], bf16x4);
             }
+            // P operands and the O scales
+            f32x4 so[4];
+            bf16x8 pa[6];
+#pragma unroll
+            for (int m = 0, i = 0; m < 4; ++m) {
+                so[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[2][16 * m + 4 * lq]);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks == 0 || m >= 2) pa[i++] = lds_load8(&sm.Ps[(16 * m + li) * kKtLd + 32 * ks + 8 * lq]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // O = Gamma n_q (Q S0) + P Delta -> LDS staging
             const bf16x8 BD[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = sm.tok[16 * m + 4 * lq + e][2] * QS[m][e];
+            for (int m = 0, i = 0; m < 4; ++m) {
+                f32x4 acc = so[m] * QS[m];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || m >= 2)
-                        acc = mfma16(lds_load4x2(&sm.Ps[(16 * m + li) * kKtLd + 32 * ks + 4 * lq]), BD[ks], acc);
+                    if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
             }
             // S <- exp(gamma_C) S + K^T Delta',  Delta' = exp(gamma_C - gamma) n_k Delta  (hi + lo)
-            f32x4 Dq[4];
+            f32x4 su[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m) su[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[3][16 * m + 4 * lq]);
+            bf16x8 akt[8][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Dq[m][e] = sm.tok[16 * m + 4 * lq + e][3] * Dl[m][e];
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) akt[t][ks] = lds_load8(&sm.Kt[(16 * t + li) * kKtLd + 32 * ks + 8 * lq]);
+            const float eC = expf(sm.gam[kC - 1]);
+            __builtin_amdgcn_sched_barrier(0);
             bf16x8 BH[2], BL[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                BH[ks] = to_bf16x8(Dq[2 * ks], Dq[2 * ks + 1]);
+                const f32x4 q0 = su[2 * ks] * Dl[2 * ks], q1 = su[2 * ks + 1] * Dl[2 * ks + 1];
+                BH[ks] = to_bf16x8(q0, q1);
                 const f32x8 back = to_f32x8(BH[ks]);
-                const f32x4 l0 = {Dq[2 * ks][0] - back[0], Dq[2 * ks][1] - back[1],
-                                  Dq[2 * ks][2] - back[2], Dq[2 * ks][3] - back[3]};
-                const f32x4 l1 = {Dq[2 * ks + 1][0] - back[4], Dq[2 * ks + 1][1] - back[5],
-                                  Dq[2 * ks + 1][2] - back[6], Dq[2 * ks + 1][3] - back[7]};
+                const f32x4 l0 = {q0[0] - back[0], q0[1] - back[1], q0[2] - back[2], q0[3] - back[3]};
+                const f32x4 l1 = {q1[0] - back[4], q1[1] - back[5], q1[2] - back[6], q1[3] - back[7]};
                 BL[ks] = to_bf16x8(l0, l1);
             }
-            const float eC = expf(sm.gam[kC - 1]);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
+                if (t == 4) {
+                    // second half of the K^T operands
+#pragma unroll
+                    for (int tt = 4; tt < 8; ++tt)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+                            akt[tt][ks] = lds_load8(&sm.Kt[(16 * tt + li) * kKtLd + 32 * ks + 8 * lq]);
+                }
                 f32x4 acc = S[t] * eC;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 akt = lds_load4x2(&sm.Kt[(16 * t + li) * kKtLd + 32 * ks + 4 * lq]);
-                    acc = mfma16(akt, BH[ks], acc);
-                    acc = mfma16(akt, BL[ks], acc);
+                    acc = mfma16(akt[t][ks], BH[ks], acc);
+                    acc = mfma16(akt[t][ks], BL[ks], acc);
                 }
                 S[t] = acc;
             }
