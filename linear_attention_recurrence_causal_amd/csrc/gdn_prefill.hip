@@ -95,22 +95,24 @@ struct alignas(16) Smem {
     static constexpr int N = 16 * NW;
     static constexpr int VLd = N + 8;
     static constexpr int NCH = 2 * kD + N;
-    __bf16 Ks[kC * kKsLd];
-    __bf16 Qs[kC * kKsLd];
+    // Double-buffered per chunk: while the state phase of chunk c reads
+    // buffer c % 2, the front end of chunk c + 1 fills the other one.
+    __bf16 Ks[2][kC * kKsLd];
+    __bf16 Qs[2][kC * kKsLd];     // Qs[c % 2] also stages chunk c's output once Q S0 is done
+    __bf16 Vt[2][N * kVtLd];      // V transposed: [column][token]
     __bf16 Kt[kD * kKtLd];
-    __bf16 Vt[N * kVtLd];         // V transposed: [column][token]
     __bf16 Ps[kC * kKtLd];        // P = M .* (n_q n_k^T) .* Q K^T, lower incl. diagonal
     __bf16 AN[kC * kKtLd];        // -A below the diagonal blocks, T_mm - I on them
-    __bf16 Os[kC * VLd];          // output staging (B -> C)
     float AdT[4 * 16 * kXLd];     // the four diagonal 16x16 blocks of A, transposed (fp32)
-    float Ws[4 * NCH];           // conv taps, [tap][channel]
+    float Ws[4 * NCH];            // conv taps, [tap][channel]
     alignas(16) float beta[kC];
     alignas(16) float gam[kC];
     alignas(16) float nq[kC];
     alignas(16) float nk[kC];
-    f32x4 Graw[(NW == 8 ? 20 : 1) * 64];  // raw Gram tiles between A2 and A3 (8 waves)
     float tokS[4][kC];            // per row: beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k
-    float eC;
+    static_assert(kC * VLd <= kC * kKsLd, "output staging fits a Q buffer");
+    static_assert(NW != 8 || (10 * 64 * 16 <= kC * kKsLd * 2 && 10 * 64 * 16 <= N * kVtLd * 2),
+                  "raw Gram tiles fit the dead K and V^T buffers");
 };
 
 // Column order inside Q, K (d_k columns) and K^T, P, AN (token columns).  An
@@ -175,16 +177,22 @@ __device__ __forceinline__ void write_tail(const PrefillParams& p, int b, int64_
     }
 }
 
+// Per-workgroup constants.
+struct Ctx {
+    int b, kh, h, zcol0;
+    int64_t L, sp;
+    float neg_A, dt_h;
+};
+
 constexpr int kTilesPerWave = 4;   // 20 Gram tiles over waves 3..7
 
 // Raw tile ti of K K^T (ti < 10) or Q K^T (ti >= 10) on the lower 16x16 tile
 // pair tile_pair(ti % 10): bf16 operands straight from LDS, fp32 accumulate.
-template <int NW>
-__device__ __forceinline__ f32x4 gram_tile(const Smem<NW>& sm, int ti, int li, int lq) {
+__device__ __forceinline__ f32x4 gram_tile(const __bf16* Ks, const __bf16* Qs, int ti, int li, int lq) {
     int m, pp;
     tile_pair(ti >= 10 ? ti - 10 : ti, m, pp);
-    const __bf16* arow = (ti >= 10 ? sm.Qs : sm.Ks) + (16 * m + li) * kKsLd + 8 * lq;
-    const __bf16* brow = sm.Ks + (16 * pp + li) * kKsLd + 8 * lq;
+    const __bf16* arow = (ti >= 10 ? Qs : Ks) + (16 * m + li) * kKsLd + 8 * lq;
+    const __bf16* brow = Ks + (16 * pp + li) * kKsLd + 8 * lq;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) acc = mfma16(lds_load8(arow + 32 * ks), lds_load8(brow + 32 * ks), acc);
@@ -237,25 +245,25 @@ __device__ __forceinline__ void row_scales(Smem<NW>& sm, int r) {
 // call, rows before it are replaced by the carried conv state and rows outside
 // it produce zeros.
 template <bool INTERIOR, int NW>
-__device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm, int b, int kh, int h,
-                                           int zcol0, int64_t local0, int item) {
+__device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+                                           int64_t local0, int item) {
     constexpr int NCH = Smem<NW>::NCH;
     constexpr int CG4 = NCH / 4;
-    const int64_t L = p.seq_len;
+    const int64_t L = cx.L;
     const int cg = item % CG4, seg = item / CG4;
     const int ch0 = cg * 4;
-    const int64_t gc = global_channel(ch0, kh, h, zcol0, p.num_k_heads);
+    const int64_t gc = global_channel(ch0, cx.kh, cx.h, cx.zcol0, p.num_k_heads);
     const int tau0 = seg * 8;
     const int64_t t_first = local0 + tau0 - 3;
     uint2 raw[11];
     if (INTERIOR) {
         const uint16_t* src = static_cast<const uint16_t*>(p.qkv) +
-                              ((int64_t)b * L + t_first) * p.conv_dim + gc;
+                              ((int64_t)cx.b * L + t_first) * p.conv_dim + gc;
         const int cd = (int)p.conv_dim;
 #pragma unroll
         for (int j = 0; j < 11; ++j) raw[j] = *reinterpret_cast<const uint2*>(src + j * cd);
     } else {
-        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * L * p.conv_dim + gc;
+        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)cx.b * L * p.conv_dim + gc;
 #pragma unroll
         for (int j = 0; j < 11; ++j) {
             const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
@@ -275,10 +283,10 @@ __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm,
     if (!INTERIOR && t_first < 0) {
 #pragma unroll
         for (int j = 0; j < 3; ++j)
-            if (t_first + j < 0) load_x4_state(p, b, t_first + j, gc, hist[j]);
+            if (t_first + j < 0) load_x4_state(p, cx.b, t_first + j, gc, hist[j]);
     }
     const bool is_v = ch0 >= 2 * kD;
-    __bf16* dst0 = ch0 < kD ? &sm.Qs[pos(ch0)] : &sm.Ks[pos(ch0 - kD)];
+    __bf16* dst0 = ch0 < kD ? &sm.Qs[buf][pos(ch0)] : &sm.Ks[buf][pos(ch0 - kD)];
     bf16x8 vcol[4];   // v channels: 8 tokens of each of the 4 channels, stored as V^T rows
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -286,7 +294,7 @@ __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm,
         const int64_t t = local0 + tau;
         float x[4];
         unpack_bf16x4(raw[3 + tt], x);
-        if (!INTERIOR && t < 0) load_x4_state(p, b, t, gc, x);
+        if (!INTERIOR && t < 0) load_x4_state(p, cx.b, t, gc, x);
         const bool valid = INTERIOR || (t >= 0 && t < L);
         f32x4 u;
 #pragma unroll
@@ -308,7 +316,345 @@ __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm,
     if (is_v) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<bf16x8*>(&sm.Vt[(ch0 - 2 * kD + i) * kVtLd + tau0]) = vcol[i];
+            *reinterpret_cast<bf16x8*>(&sm.Vt[buf][(ch0 - 2 * kD + i) * kVtLd + tau0]) = vcol[i];
+    }
+}
+
+// ---- A1: front end of a chunk into Q, K, V^T buffer `buf`
+template <int NW>
+__device__ __forceinline__ void phase_front(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+                                            int64_t local0, int tid) {
+    constexpr int NT = 64 * NW;
+    constexpr int CG4 = Smem<NW>::NCH / 4;
+    // interior chunks (all 64 rows and the 3-row halo inside the call) take a
+    // path with no clamping and no masking
+    if (local0 >= 3 && local0 + kC <= cx.L) {
+        for (int item = tid; item < CG4 * 8; item += NT) front_item<true, NW>(p, sm, cx, buf, local0, item);
+    } else {
+        for (int item = tid; item < CG4 * 8; item += NT) front_item<false, NW>(p, sm, cx, buf, local0, item);
+    }
+}
+
+// ---- A2: K^T, gates + inclusive scan of g, L2 norms; with 8 waves also the
+// raw Gram tiles, into the dead K / V^T buffer `gbuf` (fp32, accumulator layout)
+template <int NW>
+__device__ __forceinline__ void phase_rows(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+                                           int gbuf, int64_t local0, int tid) {
+    constexpr int NT = 64 * NW;
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, lq = lane / 16;
+    const __bf16* Ks = sm.Ks[buf];
+    const __bf16* Qs = sm.Qs[buf];
+    for (int e = tid; e < kD * (kC / 8); e += NT) {
+        // K^T[d][tau0 .. tau0+7] from eight K rows; lanes walk d, so the
+        // 2-byte LDS reads of one instruction hit consecutive addresses
+        const int d = e % kD, tau0 = (e / kD) * 8;
+        const int pd = pos(d);
+        bf16x4 c0, c1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c0[i] = Ks[(tau0 + i) * kKsLd + pd];
+            c1[i] = Ks[(tau0 + 4 + i) * kKsLd + pd];
+        }
+        *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0)]) = c0;
+        *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0 + 4)]) = c1;
+    }
+    for (int job = tid; job < 3 * kC; job += NT) {
+        if (job < kC) {
+            const int tau = job;
+            const int64_t t = local0 + tau;
+            const bool valid = t >= 0 && t < cx.L;
+            float gv = 0.f, bv = 0.f;
+            if (valid) {
+                const int64_t gi = ((int64_t)cx.b * cx.L + t) * p.num_v_heads + cx.h;
+                const float av = bf16_bits_to_f32(static_cast<const uint16_t*>(p.a)[gi]);
+                const float bb = bf16_bits_to_f32(static_cast<const uint16_t*>(p.b)[gi]);
+                gv = cx.neg_A * softplus_f32(av + cx.dt_h);
+                bv = sigmoid_f32(bb);
+            }
+            float s = gv;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(s, off, 64);
+                if (lane >= off) s += o;
+            }
+            sm.gam[tau] = s;
+            sm.beta[tau] = bv;
+        } else {
+            const bool isq = job < 2 * kC;
+            const int tau = job % kC;
+            const __bf16* row = (isq ? Qs : Ks) + tau * kKsLd;
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < kD; c += 8) {
+                const f32x8 v = to_f32x8(lds_load8(row + c));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc = fmaf(v[i], v[i], acc);
+            }
+            const float n = (isq ? p.q_scale : 1.0f) / sqrtf(acc + p.l2_eps);
+            (isq ? sm.nq : sm.nk)[tau] = n;
+        }
+    }
+    if constexpr (NW == 8) {
+        // raw K K^T / Q K^T tiles need only Q and K: waves 3..7 (idle after
+        // the K^T copy) compute them here; the masks follow in A3
+        if (wave >= 3) {
+            f32x4* G = reinterpret_cast<f32x4*>(sm.Ks[gbuf]);
+            f32x4* GQ = reinterpret_cast<f32x4*>(sm.Vt[gbuf]);
+#pragma unroll 1
+            for (int k = 0; k < kTilesPerWave; ++k) {
+                const int ti = (wave - 3) + 5 * k;
+                const f32x4 t = gram_tile(Ks, Qs, ti, li, lq);
+                if (ti < 10) G[ti * 64 + lane] = t;
+                else GQ[(ti - 10) * 64 + lane] = t;
+            }
+        }
+    }
+}
+
+// ---- A3: decay masks on the Gram tiles; per-row scales
+template <int NW>
+__device__ __forceinline__ void phase_masks(Smem<NW>& sm, int buf, int gbuf, int tid) {
+    constexpr int NT = 64 * NW;
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, lq = lane / 16;
+    if constexpr (NW == 8) {
+        // job = (tile pair, lane): both the K K^T and the Q K^T tile of one
+        // lower tile pair, 640 jobs over 512 threads, branch-free within a wave
+        const f32x4* G = reinterpret_cast<const f32x4*>(sm.Ks[gbuf]);
+        const f32x4* GQ = reinterpret_cast<const f32x4*>(sm.Vt[gbuf]);
+        for (int j = tid; j < 10 * 64; j += NT) mask_pair(sm, j >> 6, G[j], GQ[j], j & 63);
+        if (wave == NW - 1) row_scales(sm, lane);
+    } else {
+        if (wave == 0) row_scales(sm, lane);
+        for (int pi = wave - 1; pi >= 0 && pi < 10; pi += NW - 1)
+            mask_pair(sm, pi, gram_tile(sm.Ks[buf], sm.Qs[buf], pi, li, lq),
+                      gram_tile(sm.Ks[buf], sm.Qs[buf], 10 + pi, li, lq), lane);
+    }
+}
+
+// ---- A4: inverses of the four diagonal blocks, (I + A_mm)^-1 = I + N_mm, by
+// substitution (one wave, lane = (block m, column c)).  The off-diagonal
+// coupling is applied in the state phase by blocked forward substitution, so
+// no other part of (I + A)^-1 is formed.
+template <int NW>
+__device__ __forceinline__ void phase_diag(Smem<NW>& sm, int lane) {
+    // right-looking: once x[i] is final, subtract its contribution from every
+    // later row (column i of A_mm is row i of AdT), so the dependent chain is
+    // one FMA per row
+    const int m = lane / 16, c = lane % 16;
+    const float* At = sm.AdT + m * 16 * kXLd;
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) x[rr] = rr == c ? 1.f : 0.f;
+    float col[2][16];   // column i of A_mm, loaded one step ahead
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) col[0][rr] = At[rr];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+        if (i + 1 < 15) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) col[(i + 1) & 1][rr] = At[(i + 1) * kXLd + rr];
+        }
+        const float xi = x[i];
+#pragma unroll
+        for (int rr = i + 1; rr < 16; ++rr) x[rr] = fmaf(-col[i & 1][rr], xi, x[rr]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+        sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
+}
+
+// ---- B1: state-dependent products of a chunk, per wave (16 state columns):
+// K S0, Q S0, R, the blocked substitution for Delta, and the state update.
+// Every block of LDS operands is loaded in one batch (fenced with a
+// scheduling barrier) before the products that use it.  Returns Q S0 and
+// Delta (bf16, as the B operands of P Delta) for B2.
+template <int NW>
+__device__ __forceinline__ void phase_state(Smem<NW>& sm, int buf, f32x4 S[8], f32x4 QS[4], bf16x8 BD[2],
+                                            int wave, int li, int lq) {
+    const int cw = 16 * wave + li;   // column inside the slice
+    const __bf16* Ks = sm.Ks[buf];
+    const __bf16* Qs = sm.Qs[buf];
+    bf16x8 Bs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+    f32x4 KS[4];
+#pragma unroll
+    for (int mh = 0; mh < 4; mh += 2) {
+        bf16x8 ak[2][4], aq[2][4];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = (16 * (mh + mm) + li) * kKsLd + 32 * ks + 8 * lq;
+                ak[mm][ks] = lds_load8(&Ks[off]);
+                aq[mm][ks] = lds_load8(&Qs[off]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            f32x4 k = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                k = mfma16(ak[mm][ks], Bs[ks], k);
+                q = mfma16(aq[mm][ks], Bs[ks], q);
+            }
+            KS[mh + mm] = k;
+            QS[mh + mm] = q;
+        }
+    }
+    // row scales and V for this lane's 16 rows (16m + 4 lq + e), and the A
+    // operands of the substitution (token block k of an AN row sits at
+    // 32(k/2) + 8 lq + 4(k%2))
+    f32x4 sb[4], sr[4];
+    bf16x4 vv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r0 = 16 * m + 4 * lq;
+        sb[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[0][r0]);
+        sr[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[1][r0]);
+        vv[m] = lds_load4(&sm.Vt[buf][cw * kVtLd + r0]);
+    }
+    const __bf16* an = &sm.AN[li * kKtLd + 8 * lq];
+    const bf16x4 d0 = lds_load4(an), d1 = lds_load4(an + 16 * kKtLd + 4);
+    const bf16x4 d2 = lds_load4(an + 32 * kKtLd + 32), d3 = lds_load4(an + 48 * kKtLd + 36);
+    const bf16x4 a10 = lds_load4(an + 16 * kKtLd);
+    const bf16x8 a2x = lds_load8(an + 32 * kKtLd), a3x = lds_load8(an + 48 * kKtLd);
+    const bf16x4 a32 = lds_load4(an + 48 * kKtLd + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    // R = beta V - beta Gamma n_k (K S0)
+    f32x4 R[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
+    // (I + A) Delta = R by blocked forward substitution over the four 16-row
+    // blocks: Y_m = R_m - sum_{k<m} A_mk Delta_k, then Delta_m = Y_m + N_mm Y_m.
+    // The fp32 accumulator carries R and Y exactly; only the coupling terms
+    // see bf16 operands.
+    f32x4 Dl[4];
+    bf16x4 Db[4];
+    const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
+    const bf16x4 dg[4] = {d0, d1, d2, d3};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 y = R[m];
+        if (m == 1) y = mfma16(cat4(a10, z4), cat4(Db[0], z4), y);
+        if (m == 2) y = mfma16(a2x, cat4(Db[0], Db[1]), y);
+        if (m == 3) {
+            y = mfma16(a3x, cat4(Db[0], Db[1]), y);
+            y = mfma16(cat4(a32, z4), cat4(Db[2], z4), y);
+        }
+        const bf16x4 yb = __builtin_convertvector(y, bf16x4);
+        Dl[m] = mfma16(cat4(dg[m], z4), cat4(yb, z4), y);
+        Db[m] = __builtin_convertvector(Dl[m], bf16x4);
+    }
+    BD[0] = cat4(Db[0], Db[1]);
+    BD[1] = cat4(Db[2], Db[3]);
+    // S <- exp(gamma_C) S + K^T Delta',  Delta' = exp(gamma_C - gamma) n_k Delta  (hi + lo)
+    f32x4 su[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) su[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[3][16 * m + 4 * lq]);
+    bf16x8 akt[8][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) akt[t][ks] = lds_load8(&sm.Kt[(16 * t + li) * kKtLd + 32 * ks + 8 * lq]);
+    const float eC = expf(sm.gam[kC - 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 BH[2], BL[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 q0 = su[2 * ks] * Dl[2 * ks], q1 = su[2 * ks + 1] * Dl[2 * ks + 1];
+        BH[ks] = to_bf16x8(q0, q1);
+        const f32x8 back = to_f32x8(BH[ks]);
+        const f32x4 l0 = {q0[0] - back[0], q0[1] - back[1], q0[2] - back[2], q0[3] - back[3]};
+        const f32x4 l1 = {q1[0] - back[4], q1[1] - back[5], q1[2] - back[6], q1[3] - back[7]};
+        BL[ks] = to_bf16x8(l0, l1);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (t == 4) {
+            // second half of the K^T operands
+#pragma unroll
+            for (int tt = 4; tt < 8; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    akt[tt][ks] = lds_load8(&sm.Kt[(16 * tt + li) * kKtLd + 32 * ks + 8 * lq]);
+        }
+        f32x4 acc = S[t] * eC;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            acc = mfma16(akt[t][ks], BH[ks], acc);
+            acc = mfma16(akt[t][ks], BL[ks], acc);
+        }
+        S[t] = acc;
+    }
+}
+
+// ---- B2: O = Gamma n_q (Q S0) + P Delta, staged (bf16) into the chunk's Q
+// buffer, which no wave reads any more
+template <int NW>
+__device__ __forceinline__ void phase_out(Smem<NW>& sm, int buf, const f32x4 QS[4], const bf16x8 BD[2],
+                                          int wave, int li, int lq) {
+    constexpr int VLd = Smem<NW>::VLd;
+    const int cw = 16 * wave + li;
+    __bf16* Os = sm.Qs[buf];
+    f32x4 so[4];
+    bf16x8 pa[6];
+#pragma unroll
+    for (int m = 0, i = 0; m < 4; ++m) {
+        so[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[2][16 * m + 4 * lq]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks == 0 || m >= 2) pa[i++] = lds_load8(&sm.Ps[(16 * m + li) * kKtLd + 32 * ks + 8 * lq]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0, i = 0; m < 4; ++m) {
+        f32x4 acc = so[m] * QS[m];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
+    }
+}
+
+// ---- C: O rows -> HBM (16-byte stores); checkpoint slot when the chunk end
+// is a multiple of the checkpoint interval
+template <int NW>
+__device__ __forceinline__ void phase_store(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+                                            const f32x4 S[8], int64_t kc, int64_t s_base, bool owns_qk_tail,
+                                            int tid) {
+    constexpr int NT = 64 * NW;
+    constexpr int N = 16 * NW;
+    constexpr int VLd = Smem<NW>::VLd;
+    constexpr int NCH = Smem<NW>::NCH;
+    const int lane = tid % 64, lq = lane / 16;
+    const int64_t local0 = kc * kC - cx.sp;
+    const __bf16* Os = sm.Qs[buf];
+    constexpr int V8 = N / 8;
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    for (int e = tid; e < kC * V8; e += NT) {
+        const int tau = e / V8, c8 = e % V8;
+        const int64_t t = local0 + tau;
+        if (t >= 0 && t < cx.L)
+            *reinterpret_cast<uint4*>(out + (((int64_t)cx.b * cx.L + t) * p.num_v_heads + cx.h) * kD + cx.zcol0 + 8 * c8) =
+                *reinterpret_cast<const uint4*>(&Os[tau * VLd + 8 * c8]);
+    }
+    const int64_t pe = (kc + 1) * kC;   // absolute end of this chunk
+    if (p.ckpt_interval > 0 && pe % p.ckpt_interval == 0 && pe <= cx.sp + cx.L) {
+        char* slot = p.ckpt_buf + (uint64_t)(pe / p.ckpt_interval - 1) * p.slot_bytes;
+        float* rec = reinterpret_cast<float*>(slot + p.conv_slot_bytes);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rec[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+        uint16_t* ctail = reinterpret_cast<uint16_t*>(slot);
+        for (int ch = tid; ch < NCH; ch += NT)
+            if (ch >= 2 * kD || owns_qk_tail)
+                write_tail(p, cx.b, pe - cx.sp, global_channel(ch, cx.kh, cx.h, cx.zcol0, p.num_k_heads), ctail);
     }
 }
 
@@ -318,9 +664,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     constexpr int N = 16 * NW;
     constexpr int S_SPLIT = kD / N;
     using SM = Smem<NW>;
-    constexpr int VLd = SM::VLd;
     constexpr int NCH = SM::NCH;
-    constexpr int CG4 = NCH / 4;
     static_assert(NCH % 4 == 0, "channel groups of 4");
     __shared__ SM sm;
 
@@ -337,10 +681,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     const int grp = (bid / 8 / M) * 8 + bid % 8;
     const int mem = (bid / 8) % M;
     if (grp >= NG) return;
-    const int b = grp / p.num_k_heads, kh = grp % p.num_k_heads;
-    const int h = kh * r + mem / S_SPLIT, z = mem % S_SPLIT;
-    const int zcol0 = z * N;
-    const int64_t L = p.seq_len, sp = p.start_pos;
+    Ctx cx;
+    cx.b = grp / p.num_k_heads;
+    cx.kh = grp % p.num_k_heads;
+    cx.h = cx.kh * r + mem / S_SPLIT;
+    cx.zcol0 = (mem % S_SPLIT) * N;
+    cx.L = p.seq_len;
+    cx.sp = p.start_pos;
+    cx.neg_A = -expf(p.A_log[cx.h]);
+    cx.dt_h = p.dt_bias[cx.h];
     const bool owns_qk_tail = (mem == 0);
 
     // ---- one-time set-up: zero the upper tiles of P, conv taps -> LDS
@@ -354,14 +703,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         // taps stored [tap][channel] so that four channels of one tap are one
         // conflict-free 16-byte read
         const int ch = e % NCH, j = e / NCH;
-        const int64_t gc = global_channel(ch, kh, h, zcol0, p.num_k_heads);
+        const int64_t gc = global_channel(ch, cx.kh, cx.h, cx.zcol0, p.num_k_heads);
         sm.Ws[e] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + j]);
     }
-    const float A_log_h = p.A_log[h], dt_h = p.dt_bias[h];
-    const float neg_A = -expf(A_log_h);
 
     // ---- the state slice of this wave: S[16t + 4lq + e][zcol0 + 16 wave + li]
-    const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * kD * kD + zcol0 + 16 * wave + li;
+    const int64_t s_base = ((int64_t)cx.b * p.num_v_heads + cx.h) * kD * kD + cx.zcol0 + 16 * wave + li;
     f32x4 S[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -369,306 +716,50 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 4; ++e)
             S[t][e] = p.rec_in ? p.rec_in[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] : 0.f;
 
-    const int64_t k_first = sp / kC;
-    const int64_t k_end = L > 0 ? (sp + L - 1) / kC + 1 : k_first;
+    const int64_t k_first = cx.sp / kC;
+    const int64_t k_end = cx.L > 0 ? (cx.sp + cx.L - 1) / kC + 1 : k_first;
     __syncthreads();
 
+    // ---- prologue: the S-independent work of the first chunk
+    if (k_first < k_end) {
+        const int64_t local0 = k_first * kC - cx.sp;
+        phase_front(p, sm, cx, 0, local0, tid);
+        __syncthreads();
+        phase_rows(p, sm, cx, 0, 1, local0, tid);
+        __syncthreads();
+        phase_masks(sm, 0, 1, tid);
+        __syncthreads();
+        if (wave == 0) phase_diag(sm, lane);
+        __syncthreads();
+    }
+
+    // ---- software pipeline over chunks: the state phase of chunk kc runs
+    // next to the S-independent work of chunk kc + 1 (other buffer).  Within
+    // the first stage half the waves do the state products first and half the
+    // front end first, so each SIMD pairs MFMA/LDS work with VALU work.
     for (int64_t kc = k_first; kc < k_end; ++kc) {
-        const int64_t local0 = kc * kC - sp;   // call-local index of chunk row 0
-
-        // ================= A1: front end -> Q, K, K^T, V (bf16) in LDS
-        // Interior chunks (all 64 rows and the 3-row halo inside the call) take
-        // a path with no clamping and no masking.
-        if (local0 >= 3 && local0 + kC <= L) {
-            for (int item = tid; item < CG4 * 8; item += NT)
-                front_item<true, NW>(p, sm, b, kh, h, zcol0, local0, item);
+        const int buf = (int)((kc - k_first) & 1), nbuf = buf ^ 1;
+        const bool next = kc + 1 < k_end;
+        const int64_t nlocal0 = (kc + 1) * kC - cx.sp;
+        f32x4 QS[4];
+        bf16x8 BD[2];
+        if (wave < NW / 2 || !next) {
+            phase_state(sm, buf, S, QS, BD, wave, li, lq);
+            if (next) phase_front(p, sm, cx, nbuf, nlocal0, tid);
         } else {
-            for (int item = tid; item < CG4 * 8; item += NT)
-                front_item<false, NW>(p, sm, b, kh, h, zcol0, local0, item);
+            phase_front(p, sm, cx, nbuf, nlocal0, tid);
+            phase_state(sm, buf, S, QS, BD, wave, li, lq);
         }
         __syncthreads();
-
-        // ================= A2: gates + inclusive scan (wave 0), L2 norms, K^T
-        for (int e = tid; e < kD * (kC / 8); e += NT) {
-            // K^T[d][tau0 .. tau0+7] from eight K rows; lanes walk d, so the
-            // 2-byte LDS reads of one instruction hit consecutive addresses
-            const int d = e % kD, tau0 = (e / kD) * 8;
-            const int pd = pos(d);
-            bf16x4 c0, c1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                c0[i] = sm.Ks[(tau0 + i) * kKsLd + pd];
-                c1[i] = sm.Ks[(tau0 + 4 + i) * kKsLd + pd];
-            }
-            *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0)]) = c0;
-            *reinterpret_cast<bf16x4*>(&sm.Kt[d * kKtLd + pos(tau0 + 4)]) = c1;
-        }
-        for (int job = tid; job < 3 * kC; job += NT) {
-            if (job < kC) {
-                const int tau = job;
-                const int64_t t = local0 + tau;
-                const bool valid = t >= 0 && t < L;
-                float gv = 0.f, bv = 0.f;
-                if (valid) {
-                    const int64_t gi = ((int64_t)b * L + t) * p.num_v_heads + h;
-                    const float av = bf16_bits_to_f32(static_cast<const uint16_t*>(p.a)[gi]);
-                    const float bb = bf16_bits_to_f32(static_cast<const uint16_t*>(p.b)[gi]);
-                    gv = neg_A * softplus_f32(av + dt_h);
-                    bv = sigmoid_f32(bb);
-                }
-                float s = gv;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float o = __shfl_up(s, off, 64);
-                    if (lane >= off) s += o;
-                }
-                sm.gam[tau] = s;
-                sm.beta[tau] = bv;
-            } else {
-                const bool isq = job < 2 * kC;
-                const int tau = job % kC;
-                const __bf16* row = (isq ? sm.Qs : sm.Ks) + tau * kKsLd;
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < kD; c += 8) {
-                    const f32x8 v = to_f32x8(lds_load8(row + c));
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc = fmaf(v[i], v[i], acc);
-                }
-                const float n = (isq ? p.q_scale : 1.0f) / sqrtf(acc + p.l2_eps);
-                (isq ? sm.nq : sm.nk)[tau] = n;
-            }
-        }
-        // Raw K K^T / Q K^T tiles need only Q and K: with 8 waves, waves 3..7
-        // (idle after the K^T copy) compute them here into LDS (fp32, in the
-        // accumulator layout); A3 applies the masks.
-        if constexpr (NW == 8) {
-            if (wave >= 3) {
-#pragma unroll 1
-                for (int k = 0; k < kTilesPerWave; ++k) {
-                    const int ti = (wave - 3) + 5 * k;
-                    sm.Graw[ti * 64 + lane] = gram_tile(sm, ti, li, lq);
-                }
-            }
-        }
+        phase_out(sm, buf, QS, BD, wave, li, lq);
+        if (next) phase_rows(p, sm, cx, nbuf, buf, nlocal0, tid);
         __syncthreads();
-
-        // ================= A3: decay masks on the Gram tiles; per-row scales
-        if constexpr (NW == 8) {
-            // job = (tile pair, lane): both the K K^T and the Q K^T tile of one
-            // lower tile pair, 640 jobs over 512 threads, branch-free within a wave
-            for (int j = tid; j < 10 * 64; j += NT) mask_pair(sm, j >> 6, sm.Graw[j], sm.Graw[640 + j], j & 63);
-            if (wave == NW - 1) row_scales(sm, lane);
-        } else {
-            if (wave == 0) row_scales(sm, lane);
-            for (int pi = wave - 1; pi >= 0 && pi < 10; pi += NW - 1)
-                mask_pair(sm, pi, gram_tile(sm, pi, li, lq), gram_tile(sm, 10 + pi, li, lq), lane);
-        }
+        phase_store(p, sm, cx, buf, S, kc, s_base, owns_qk_tail, tid);
+        if (next) phase_masks(sm, nbuf, buf, tid);
         __syncthreads();
-
-        // ================= A4: inverses of the four diagonal blocks
-        // (I + A_mm)^-1 = I + N_mm by substitution, one wave, lane = (block m,
-        // column c).  The off-diagonal coupling is applied in B by blocked
-        // forward substitution, so no other part of (I + A)^-1 is formed.
-        if (wave == 0) {
-            // column c of block m; right-looking: once x[i] is final, subtract
-            // its contribution from every later row (column i of A_mm is row i
-            // of AdT), so the dependent chain is one FMA per row
-            const int m = lane / 16, c = lane % 16;
-            const float* At = sm.AdT + m * 16 * kXLd;
-            float x[16];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) x[rr] = rr == c ? 1.f : 0.f;
-            // column i of A_mm is loaded one step ahead (two 16-float buffers)
-            float col[2][16];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) col[0][rr] = At[rr];
-#pragma unroll
-            for (int i = 0; i < 15; ++i) {
-                if (i + 1 < 15) {
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) col[(i + 1) & 1][rr] = At[(i + 1) * kXLd + rr];
-                }
-                const float xi = x[i];
-#pragma unroll
-                for (int rr = i + 1; rr < 16; ++rr) x[rr] = fmaf(-col[i & 1][rr], xi, x[rr]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-                sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
-        }
-        __syncthreads();
-
-        // ================= B: state-dependent products, per wave
-        // Every block of LDS operands is loaded in one batch (fenced with a
-        // scheduling barrier) before the products that use it, so a wave has
-        // many reads in flight instead of one read per MFMA.
-        {
-            const int cw = 16 * wave + li;   // column inside the slice
-            bf16x8 Bs[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-            f32x4 KS[4], QS[4];
-#pragma unroll
-            for (int mh = 0; mh < 4; mh += 2) {
-                bf16x8 ak[2][4], aq[2][4];
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int off = (16 * (mh + mm) + li) * kKsLd + 32 * ks + 8 * lq;
-                        ak[mm][ks] = lds_load8(&sm.Ks[off]);
-                        aq[mm][ks] = lds_load8(&sm.Qs[off]);
-                    }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int mm = 0; mm < 2; ++mm) {
-                    f32x4 k = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        k = mfma16(ak[mm][ks], Bs[ks], k);
-                        q = mfma16(aq[mm][ks], Bs[ks], q);
-                    }
-                    KS[mh + mm] = k;
-                    QS[mh + mm] = q;
-                }
-            }
-            // row scales and V for this lane's 16 rows (16m + 4 lq + e), and the
-            // A / P operands of the substitution and of P Delta
-            f32x4 sb[4], sr[4];
-            bf16x4 vv[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r0 = 16 * m + 4 * lq;
-                sb[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[0][r0]);
-                sr[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[1][r0]);
-                vv[m] = lds_load4(&sm.Vt[cw * kVtLd + r0]);
-            }
-            // AN row of this lane in block row m; token block k sits at
-            // 32(k/2) + 8 lq + 4(k%2)
-            const __bf16* an = &sm.AN[li * kKtLd + 8 * lq];
-            const bf16x4 d0 = lds_load4(an), d1 = lds_load4(an + 16 * kKtLd + 4);
-            const bf16x4 d2 = lds_load4(an + 32 * kKtLd + 32), d3 = lds_load4(an + 48 * kKtLd + 36);
-            const bf16x4 a10 = lds_load4(an + 16 * kKtLd);
-            const bf16x8 a2x = lds_load8(an + 32 * kKtLd), a3x = lds_load8(an + 48 * kKtLd);
-            const bf16x4 a32 = lds_load4(an + 48 * kKtLd + 32);
-            __builtin_amdgcn_sched_barrier(0);
-            // R = beta V - beta Gamma n_k (K S0)
-            f32x4 R[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
-            // (I + A) Delta = R by blocked forward substitution over the four
-            // 16-row blocks: Y_m = R_m - sum_{k<m} A_mk Delta_k, then
-            // Delta_m = Y_m + N_mm Y_m.  The fp32 accumulator carries R and
-            // Y exactly; only the coupling terms see bf16 operands.
-            f32x4 Dl[4];
-            bf16x4 Db[4];
-            const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
-            const bf16x4 dg[4] = {d0, d1, d2, d3};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 y = R[m];
-                if (m == 1) y = mfma16(cat4(a10, z4), cat4(Db[0], z4), y);
-                if (m == 2) y = mfma16(a2x, cat4(Db[0], Db[1]), y);
-                if (m == 3) {
-                    y = mfma16(a3x, cat4(Db[0], Db[1]), y);
-                    y = mfma16(cat4(a32, z4), cat4(Db[2], z4), y);
-                }
-                const bf16x4 yb = __builtin_convertvector(y, bf16x4);
-                Dl[m] = mfma16(cat4(dg[m], z4), cat4(yb, z4), y);
-                Db[m] = __builtin_convertvector(Dl[m], bf16x4);
-            }
-            // P operands and the O scales
-            f32x4 so[4];
-            bf16x8 pa[6];
-#pragma unroll
-            for (int m = 0, i = 0; m < 4; ++m) {
-                so[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[2][16 * m + 4 * lq]);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || m >= 2) pa[i++] = lds_load8(&sm.Ps[(16 * m + li) * kKtLd + 32 * ks + 8 * lq]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // O = Gamma n_q (Q S0) + P Delta -> LDS staging
-            const bf16x8 BD[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
-#pragma unroll
-            for (int m = 0, i = 0; m < 4; ++m) {
-                f32x4 acc = so[m] * QS[m];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sm.Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
-            }
-            // S <- exp(gamma_C) S + K^T Delta',  Delta' = exp(gamma_C - gamma) n_k Delta  (hi + lo)
-            f32x4 su[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) su[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[3][16 * m + 4 * lq]);
-            bf16x8 akt[8][2];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) akt[t][ks] = lds_load8(&sm.Kt[(16 * t + li) * kKtLd + 32 * ks + 8 * lq]);
-            const float eC = expf(sm.gam[kC - 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 BH[2], BL[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 q0 = su[2 * ks] * Dl[2 * ks], q1 = su[2 * ks + 1] * Dl[2 * ks + 1];
-                BH[ks] = to_bf16x8(q0, q1);
-                const f32x8 back = to_f32x8(BH[ks]);
-                const f32x4 l0 = {q0[0] - back[0], q0[1] - back[1], q0[2] - back[2], q0[3] - back[3]};
-                const f32x4 l1 = {q1[0] - back[4], q1[1] - back[5], q1[2] - back[6], q1[3] - back[7]};
-                BL[ks] = to_bf16x8(l0, l1);
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t == 4) {
-                    // second half of the K^T operands
-#pragma unroll
-                    for (int tt = 4; tt < 8; ++tt)
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks)
-                            akt[tt][ks] = lds_load8(&sm.Kt[(16 * tt + li) * kKtLd + 32 * ks + 8 * lq]);
-                }
-                f32x4 acc = S[t] * eC;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    acc = mfma16(akt[t][ks], BH[ks], acc);
-                    acc = mfma16(akt[t][ks], BL[ks], acc);
-                }
-                S[t] = acc;
-            }
-        }
-        __syncthreads();
-
-        // ================= C: outputs and checkpoint slots
-        {
-            constexpr int V8 = N / 8;
-            uint16_t* out = static_cast<uint16_t*>(p.out);
-            for (int e = tid; e < kC * V8; e += NT) {
-                const int tau = e / V8, c8 = e % V8;
-                const int64_t t = local0 + tau;
-                if (t >= 0 && t < L)
-                    *reinterpret_cast<uint4*>(out + (((int64_t)b * L + t) * p.num_v_heads + h) * kD + zcol0 + 8 * c8) =
-                        *reinterpret_cast<const uint4*>(&sm.Os[tau * VLd + 8 * c8]);
-            }
-            const int64_t pe = (kc + 1) * kC;   // absolute end of this chunk
-            if (p.ckpt_interval > 0 && pe % p.ckpt_interval == 0 && pe <= sp + L) {
-                char* slot = p.ckpt_buf + (uint64_t)(pe / p.ckpt_interval - 1) * p.slot_bytes;
-                float* rec = reinterpret_cast<float*>(slot + p.conv_slot_bytes);
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rec[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
-                uint16_t* ctail = reinterpret_cast<uint16_t*>(slot);
-                for (int ch = tid; ch < NCH; ch += NT)
-                    if (ch >= 2 * kD || owns_qk_tail)
-                        write_tail(p, b, pe - sp, global_channel(ch, kh, h, zcol0, p.num_k_heads), ctail);
-            }
+        if (next) {
+            if (wave == 0) phase_diag(sm, lane);
+            __syncthreads();
         }
     }
 
@@ -679,7 +770,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 4; ++e) p.rec_out[s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
     for (int ch = tid; ch < NCH; ch += NT)
         if (ch >= 2 * kD || owns_qk_tail)
-            write_tail(p, b, L, global_channel(ch, kh, h, zcol0, p.num_k_heads),
+            write_tail(p, cx.b, cx.L, global_channel(ch, cx.kh, cx.h, cx.zcol0, p.num_k_heads),
                        static_cast<uint16_t*>(p.conv_out));
 }
 
