@@ -107,8 +107,18 @@ gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_
                                 int64_t interval, gdn_ckpt_entry* entries, int64_t capacity,
                                 int64_t* count, uint64_t* buffer_bytes);
 
-/* Workspace a prefill call needs (host only).  Currently always 0: the
- * prefill is one fused kernel that keeps every intermediate on chip. */
+/* Workspace for the two-pass prefill (host only): the bytes with which a call
+ * of seq_len tokens per sequence (any start_pos) runs each pass once,
+ *   B * (chunks the call can span) * (H_k * 49152 + H_v * 34048).
+ * The chunked form splits into per-chunk work that does not depend on the
+ * state and a short recurrence over chunks that does ("Performance note");
+ * with a workspace the first part runs for every chunk in parallel and only
+ * the second runs chunk by chunk, which fills the GPU when B * H_v is small.
+ * A smaller workspace, down to one chunk's worth (the value for seq_len = 1),
+ * is used segment by segment.  With less than that, or NULL, or a head group
+ * H_v / H_k above 8, gdn_prefill_chunked runs a fused single-pass kernel that
+ * keeps every intermediate on chip.  Both paths compute the same values in
+ * the same precision. */
 gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, uint64_t* bytes);
 
 /* Chunked prefill of seq_len tokens per sequence ("Performance note":
@@ -128,8 +138,10 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
  *                 a checkpoint repeats the uninterrupted call bit for bit
  *   ckpt_buf, ckpt_buf_bytes, ckpt_interval: see gdn_state_checkpoint;
  *                 interval 0 = none (ckpt_buf may then be NULL)
- *   workspace, workspace_bytes: at least gdn_prefill_workspace_bytes (NULL ok
- *                 when that is 0)
+ *   workspace, workspace_bytes: scratch device memory for the two-pass path
+ *                 (see gdn_prefill_workspace_bytes), 256-byte aligned, not
+ *                 overlapping any other buffer; its contents are clobbered.
+ *                 NULL / 0 selects the fused path.
  * With seq_len == 0 only the states are copied (qkv, a, b, out may be NULL).
  * The conv+SiLU output is rounded to the io dtype before the L2 norm, as the
  * stream it comes from is stored in that dtype. */

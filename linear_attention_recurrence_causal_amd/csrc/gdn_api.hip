@@ -114,7 +114,10 @@ gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_
 gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, uint64_t* bytes) {
     if (gdn_status s = check_config(cfg)) return s;
     if (!bytes || seq_len < 0) return GDN_EINVAL;
-    *bytes = 0;
+    // seq_len tokens starting anywhere inside a chunk span at most
+    // floor((seq_len + chunk - 2) / chunk) + 1 chunks
+    const int64_t chunks = seq_len == 0 ? 0 : (seq_len + cfg->chunk - 2) / cfg->chunk + 1;
+    *bytes = (uint64_t)chunks * gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads);
     return GDN_OK;
 }
 
@@ -125,8 +128,6 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
                                const float* rec_state_in, float* rec_state_out, void* out,
                                void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
                                void* workspace, uint64_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (gdn_status s = check_config(cfg)) return s;
     if (seq_len < 0 || start_pos < 0 || ckpt_interval < 0) return GDN_EINVAL;
     if (ckpt_interval > 0 && ckpt_interval % cfg->chunk != 0) return GDN_EINVAL;
@@ -141,7 +142,8 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
         return GDN_EINVAL;
     if (seq_len > 0 && (!qkv || !a || !b || !out)) return GDN_EINVAL;
     if (!aligned16(qkv) || !aligned16(out) || !aligned_to(a, ea) || !aligned_to(b, ea)) return GDN_EINVAL;
-    if (!aligned_to(conv_state_in, ea) || !aligned_to(rec_state_in, 4) || !aligned_to(ckpt_buf, 256))
+    if (!aligned_to(conv_state_in, ea) || !aligned_to(rec_state_in, 4) || !aligned_to(ckpt_buf, 256) ||
+        !aligned_to(workspace, 256))
         return GDN_EINVAL;
     if (!gdn::prefill_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype, cfg->conv_kernel,
                                 cfg->chunk))
@@ -174,6 +176,22 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
             return GDN_EALIAS;
     }
 
+    // the two-pass path runs when at least one chunk of records fits
+    const uint64_t chunk_ws = gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads);
+    const bool two_pass = workspace && chunk_ws > 0 && workspace_bytes >= chunk_ws &&
+                          cfg->num_v_heads / cfg->num_k_heads <= 8;
+    if (two_pass) {
+        // only the part a call can use is checked against the other buffers
+        const int64_t k_first = start_pos / cfg->chunk;
+        const int64_t chunks = L > 0 ? (start_pos + L - 1) / cfg->chunk + 1 - k_first : 0;
+        const uint64_t need = (uint64_t)chunks * chunk_ws;
+        const Range r_ws = range_of(workspace, need < workspace_bytes ? need : workspace_bytes);
+        const Range r_ck = range_of(ckpt_buf, plan.count > 0 ? plan.buffer_bytes : 0);
+        if (overlap(r_ws, r_qkv) || overlap(r_ws, r_out) || overlap(r_ws, r_rout) || overlap(r_ws, r_cout) ||
+            overlap(r_ws, r_cin) || overlap(r_ws, r_rin) || overlap(r_ws, r_ck))
+            return GDN_EALIAS;
+    }
+
     gdn::PrefillParams p{};
     p.qkv = qkv;
     p.a = a;
@@ -198,7 +216,8 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     p.num_v_heads = cfg->num_v_heads;
     p.q_scale = cfg->q_scale;
     p.l2_eps = cfg->l2_eps;
-    const hipError_t e = gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream))
+                                  : gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 

@@ -50,4 +50,11 @@ hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);
 bool prefill_supported(int head_k_dim, int head_v_dim, int io_dtype, int conv_kernel, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// Two-pass path: workspace bytes per chunk of every sequence, whether the
+// head grouping is supported, and the launcher (segments of
+// ws_bytes / prefill_split_chunk_bytes chunks; at least one must fit).
+uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads);
+bool prefill_split_supported(const PrefillParams& p);
+hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream);
+
 }  // namespace gdn

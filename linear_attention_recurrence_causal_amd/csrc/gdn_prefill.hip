@@ -1,94 +1,36 @@
-// gdn_prefill.hip -- fused chunked prefill of the Gated DeltaNet core (gfx950).
+// gdn_prefill.hip -- fused single-pass chunked prefill of the Gated DeltaNet
+// core (gfx950): the path taken when the caller passes no workspace.
 //
-// What is computed: the per-token gated delta rule of the cortex commit page
-// "feat(stage-8c): linear-attention layer (Qwen3-Next GatedDeltaNet)"
-// ("Block", "Discretisation", "Delta rule"), evaluated in chunks of C = 64
-// tokens ("Performance note").  Within a chunk with rows r, incoming state
-// S0, gamma = inclusive cumsum of g and Gamma = exp(gamma), the rule unrolls
-// to (derivation in the design notes; the pages only name the method):
-//   A[r,i] = beta_r exp(gamma_r - gamma_i) (k_r . k_i)      for i < r
-//   T      = (I + A)^-1                       ("direct solve", the stable
-//            variant of the Qwen3.6-27B PR, "Known limitations and follow-ups")
-//   Delta  = T (diag(beta) V - diag(beta Gamma) K S0)
-//   O      = diag(Gamma) Q S0 + (M .* Q K^T) Delta,  M[r,i] = exp(gamma_r - gamma_i), i <= r
-//   S_C    = exp(gamma_C) S0 + (diag(exp(gamma_C - gamma)) K)^T Delta
-// with q, k the unit-norm vectors.  Here they are kept as raw bf16 conv
-// outputs (exact MFMA operands) and the norms are folded into fp32 row scales.
-//
-// One workgroup owns (sequence b, value head h, a slice of N = 16*NW state
-// columns); wave w owns 16 columns and keeps its 128 x 16 fp32 slice of S in
-// MFMA accumulator registers for the whole call.  Per chunk:
-//   A1  front end: raw qkv (+3-token halo, or the carried conv state) ->
-//       depthwise conv (fp32) -> SiLU -> bf16 -> LDS (Q, K, K^T, V)
-//   A2  gates g, beta (fp32), inclusive scan of g; L2 norms of q and k
-//   A3  K K^T and Q K^T lower 16x16 tiles on MFMA (bf16 in, fp32 out),
-//       decay masks -> A (fp32) and P (bf16)
-//   A4  T = (I + A)^-1 by blocked forward substitution in fp32 (16x16
-//       diagonal blocks by substitution, off-diagonal blocks by products)
-//   B   per wave, on MFMA: K S0, Q S0 (S0 as bf16), R, Delta = R + (T-I) R,
-//       O, and S <- exp(gamma_C) S + K^T Delta' with Delta' split into bf16
-//       hi + lo (two MFMAs): the product that builds the state carries ~16
-//       significant bits, everything else bf16 operands with fp32 accumulate.
-//   C   O rows -> HBM (16-byte stores); checkpoint slots when the chunk end is
-//       a multiple of the checkpoint interval.
-// Chunk boundaries sit at absolute multiples of 64, so a partial first or
-// last chunk is padded with rows that have g = 0, beta = 0, q = k = v = 0,
-// which leaves the rule's result unchanged.
-//
-// MFMA v_mfma_f32_16x16x32_bf16 operand layout used throughout (lane l, i =
-// l % 16, q = l / 16): A row i and B column i each hold 8 reduction slots of
-// group q; D holds rows 4q..4q+3 of column i.  The reduction index a slot
-// stands for only has to agree between A and B, so the accumulator layout of
-// one product is reused as the B operand of the next without data movement.
-#include "gdn_common.h"
-#include "gdn_launch.h"
+// The chunked form and the MFMA operand layout are described in
+// gdn_chunk_common.h.  One workgroup owns (sequence b, value head h, a slice
+// of N = 16*NW state columns); wave w owns 16 columns and keeps its 128 x 16
+// fp32 slice of S in MFMA accumulator registers for the whole call.  Per
+// chunk:
+//   front  raw qkv (+3-token halo, or the carried conv state) -> depthwise
+//          conv (fp32) -> SiLU -> bf16 -> LDS (Q, K, V^T)
+//   rows   K^T, gates g, beta (fp32) and the inclusive scan of g, L2 norms
+//   masks  K K^T and Q K^T lower 16x16 tiles on MFMA (bf16 in, fp32 out),
+//          decay masks -> A and P (bf16)
+//   diag   inverses of the 16x16 diagonal blocks of I + A by substitution
+//   state  per wave, on MFMA: K S0, Q S0 (S0 as bf16), R, Delta by blocked
+//          forward substitution, and S <- exp(gamma_C) S + K^T Delta' with
+//          Delta' split into bf16 hi + lo (two MFMAs): the product that builds
+//          the state carries ~16 significant bits, everything else bf16
+//          operands with fp32 accumulate
+//   out    O = Gamma n_q Q S0 + P Delta, O rows -> HBM (16-byte stores);
+//          checkpoint slots when the chunk end is a multiple of the interval.
+// The chunk loop is software-pipelined: the S-independent work of chunk c + 1
+// (front, rows, masks, diag; double-buffered Q, K, V^T) runs beside the state
+// and output work of chunk c.
+#include "gdn_chunk_common.h"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kC = 64;              // chunk
-constexpr int kD = 128;             // d_k = d_v
-constexpr int kKsLd = kD + 8;       // bf16 row stride of Q, K (rows = tokens)
-constexpr int kKtLd = kC + 8;       // bf16 row stride of K^T, P, AN
-constexpr int kXLd = 17;
+using namespace chunked;
+
 constexpr int kVtLd = kC + 12;      // bf16 row stride of V^T
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 8 consecutive bf16 (16 bytes) from LDS
-__device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// two runs of 4 bf16 (8 bytes each): slots 0-3 from p, 4-7 from p + 16
-__device__ __forceinline__ bf16x8 lds_load4x2(const __bf16* p) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-__device__ __forceinline__ bf16x4 lds_load4(const __bf16* p) {
-    return *reinterpret_cast<const bf16x4*>(p);
-}
-
-__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {
-    const f32x8 v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return __builtin_convertvector(v, bf16x8);
-}
-
-__device__ __forceinline__ f32x8 to_f32x8(bf16x8 v) { return __builtin_convertvector(v, f32x8); }
 
 template <int NW>
 struct alignas(16) Smem {
@@ -115,66 +57,11 @@ struct alignas(16) Smem {
                   "raw Gram tiles fit the dead K and V^T buffers");
 };
 
-// Column order inside Q, K (d_k columns) and K^T, P, AN (token columns).  An
-// index x = 32a + 16h + 4q + e is stored at 32a + 8q + 4h + e, so the eight
-// reduction slots that lane group q of v_mfma_f32_16x16x32_bf16 needs for
-// k-step a (indices 32a + 4q + {0..3} and 32a + 16 + 4q + {0..3}, the order
-// in which an accumulator tile is reused as a B operand) are one contiguous
-// 16-byte run, and runs of four consecutive indices stay contiguous.
-__device__ __forceinline__ int pos(int x) {
-    return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
-}
-
-// lower 16x16 tile pairs (m, p), p <= m, in a fixed order
-__device__ __forceinline__ void tile_pair(int idx, int& m, int& p) {
-    m = idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : 3;
-    p = idx - (m * (m + 1)) / 2;
-}
-
 // Global channel of the WG's channel index ch (q: 0..127, k: 128..255, v: 256..)
 __device__ __forceinline__ int64_t global_channel(int ch, int kh, int h, int zcol0, int Hk) {
     if (ch < kD) return (int64_t)kh * kD + ch;
     if (ch < 2 * kD) return (int64_t)Hk * kD + (int64_t)kh * kD + (ch - kD);
     return 2 * (int64_t)Hk * kD + (int64_t)h * kD + zcol0 + (ch - 2 * kD);
-}
-
-__device__ __forceinline__ void unpack_bf16x4(uint2 raw, float x[4]) {
-    x[0] = bf16_bits_to_f32(raw.x & 0xffffu);
-    x[1] = bf16_bits_to_f32(raw.x >> 16);
-    x[2] = bf16_bits_to_f32(raw.y & 0xffffu);
-    x[3] = bf16_bits_to_f32(raw.y >> 16);
-}
-
-// SiLU with the hardware exp2 and reciprocal (about 2 ulp of fp32; the
-// result is rounded to bf16 right after).
-__device__ __forceinline__ float silu_fast(float y) {
-    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
-}
-
-// Pre-conv inputs of channels gc..gc+3 at call-local token t < 0: the
-// carried conv state for t >= -3 (zeros for a new request), else zeros.
-__device__ __forceinline__ void load_x4_state(const PrefillParams& p, int b, int64_t t, int64_t gc,
-                                              float x[4]) {
-    const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        x[i] = (cs && t >= -3) ? bf16_bits_to_f32(cs[((int64_t)b * p.conv_dim + gc + i) * 3 + (3 + t)]) : 0.f;
-}
-
-// Copy the conv tail that ends just before call-local token `end` (the last
-// three pre-conv inputs) for channel gc of sequence b into dst[b][gc][0..2].
-__device__ __forceinline__ void write_tail(const PrefillParams& p, int b, int64_t end, int64_t gc,
-                                           uint16_t* dst) {
-    const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
-    const uint16_t* cs = static_cast<const uint16_t*>(p.conv_in);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int64_t t = end - 3 + j;
-        uint16_t v;
-        if (t >= 0) v = qkv[((int64_t)b * p.seq_len + t) * p.conv_dim + gc];
-        else v = cs ? cs[((int64_t)b * p.conv_dim + gc) * 3 + (3 + t)] : uint16_t(0);
-        dst[((int64_t)b * p.conv_dim + gc) * 3 + j] = v;
-    }
 }
 
 // Per-workgroup constants.
@@ -186,90 +73,17 @@ struct Ctx {
 
 constexpr int kTilesPerWave = 4;   // 20 Gram tiles over waves 3..7
 
-// Raw tile ti of K K^T (ti < 10) or Q K^T (ti >= 10) on the lower 16x16 tile
-// pair tile_pair(ti % 10): bf16 operands straight from LDS, fp32 accumulate.
-__device__ __forceinline__ f32x4 gram_tile(const __bf16* Ks, const __bf16* Qs, int ti, int li, int lq) {
-    int m, pp;
-    tile_pair(ti >= 10 ? ti - 10 : ti, m, pp);
-    const __bf16* arow = (ti >= 10 ? Qs : Ks) + (16 * m + li) * kKsLd + 8 * lq;
-    const __bf16* brow = Ks + (16 * pp + li) * kKsLd + 8 * lq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16(lds_load8(arow + 32 * ks), lds_load8(brow + 32 * ks), acc);
-    return acc;
-}
-
-// Decay masks and row/column scales of one lower tile pair (lane l of the
-// accumulator layout: column 16 pp + l % 16, rows 16 m + 4 (l / 16) + e):
-//   A[r,i] = beta_r n_k[r] n_k[i] exp(gamma_r - gamma_i) (K K^T)[r,i], i < r
-//     -> -A (bf16) off the diagonal blocks, fp32 transposed on them
-//   P[r,i] = n_q[r] n_k[i] exp(gamma_r - gamma_i) (Q K^T)[r,i], i <= r (bf16)
-template <int NW>
-__device__ __forceinline__ void mask_pair(Smem<NW>& sm, int pi, f32x4 g, f32x4 qk, int l) {
-    const int li = l % 16, lq = l / 16;
-    int m, pp;
-    tile_pair(pi, m, pp);
-    const int ii = 16 * pp + li, r0 = 16 * m + 4 * lq;
-    const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.gam[r0]);
-    const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[r0]);
-    const f32x4 kr = *reinterpret_cast<const f32x4*>(&sm.nk[r0]);
-    const f32x4 qr = *reinterpret_cast<const f32x4*>(&sm.nq[r0]);
-    const float gi = sm.gam[ii], nki = sm.nk[ii];
-    const int pii = pos(ii);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int rr = r0 + e;
-        const float dec = ii <= rr ? __expf(gr[e] - gi) * nki : 0.f;
-        const float av = ii < rr ? br[e] * kr[e] * dec * g[e] : 0.f;
-        sm.Ps[rr * kKtLd + pii] = __bf16(qr[e] * dec * qk[e]);
-        if (m == pp) sm.AdT[(m * 16 + li) * kXLd + 4 * lq + e] = av;
-        else sm.AN[rr * kKtLd + pii] = __bf16(-av);
-    }
-}
-
-// Per-row scales of the state phase for row r = lane (one wave):
-//   beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k
-template <int NW>
-__device__ __forceinline__ void row_scales(Smem<NW>& sm, int r) {
-    const float gl = sm.gam[r], gC = sm.gam[kC - 1];
-    const float e = expf(gl), nkv = sm.nk[r], bv = sm.beta[r];
-    sm.tokS[0][r] = bv;
-    sm.tokS[1][r] = bv * e * nkv;
-    sm.tokS[2][r] = e * sm.nq[r];
-    sm.tokS[3][r] = expf(gC - gl) * nkv;
-}
-
-// Front end of one work item: 4 channels x 8 tokens of the chunk.  The
-// eleven 8-byte row loads (3 halo rows + 8) are issued together.  INTERIOR:
-// every row lies inside the call.  Otherwise row indices are clamped into the
-// call, rows before it are replaced by the carried conv state and rows outside
-// it produce zeros.
+// Front end of one work item (4 channels x 8 chunk rows) into buffer `buf`:
+// q, k channels -> Q, K rows, v channels -> V^T rows.
 template <bool INTERIOR, int NW>
 __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
                                            int64_t local0, int item) {
     constexpr int NCH = Smem<NW>::NCH;
     constexpr int CG4 = NCH / 4;
-    const int64_t L = cx.L;
     const int cg = item % CG4, seg = item / CG4;
     const int ch0 = cg * 4;
     const int64_t gc = global_channel(ch0, cx.kh, cx.h, cx.zcol0, p.num_k_heads);
     const int tau0 = seg * 8;
-    const int64_t t_first = local0 + tau0 - 3;
-    uint2 raw[11];
-    if (INTERIOR) {
-        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) +
-                              ((int64_t)cx.b * L + t_first) * p.conv_dim + gc;
-        const int cd = (int)p.conv_dim;
-#pragma unroll
-        for (int j = 0; j < 11; ++j) raw[j] = *reinterpret_cast<const uint2*>(src + j * cd);
-    } else {
-        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)cx.b * L * p.conv_dim + gc;
-#pragma unroll
-        for (int j = 0; j < 11; ++j) {
-            const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
-            raw[j] = *reinterpret_cast<const uint2*>(src + tc * p.conv_dim);
-        }
-    }
     float w[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -277,46 +91,19 @@ __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm,
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[j][i] = wv[i];
     }
-    float hist[3][4];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) unpack_bf16x4(raw[j], hist[j]);
-    if (!INTERIOR && t_first < 0) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-            if (t_first + j < 0) load_x4_state(p, cx.b, t_first + j, gc, hist[j]);
-    }
-    const bool is_v = ch0 >= 2 * kD;
-    __bf16* dst0 = ch0 < kD ? &sm.Qs[buf][pos(ch0)] : &sm.Ks[buf][pos(ch0 - kD)];
-    bf16x8 vcol[4];   // v channels: 8 tokens of each of the 4 channels, stored as V^T rows
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-        const int tau = tau0 + tt;
-        const int64_t t = local0 + tau;
-        float x[4];
-        unpack_bf16x4(raw[3 + tt], x);
-        if (!INTERIOR && t < 0) load_x4_state(p, cx.b, t, gc, x);
-        const bool valid = INTERIOR || (t >= 0 && t < L);
-        f32x4 u;
+    bf16x4 ub[8];
+    conv_item<INTERIOR>(p, cx.b, gc, local0, tau0, w, ub);
+    if (ch0 >= 2 * kD) {
+        // v channels: 8 tokens of each of the 4 channels, stored as V^T rows
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float y = fmaf(w[3][i], x[i], fmaf(w[2][i], hist[2][i], fmaf(w[1][i], hist[1][i], w[0][i] * hist[0][i])));
-            u[i] = valid ? silu_fast(y) : 0.f;
-            hist[0][i] = hist[1][i];
-            hist[1][i] = hist[2][i];
-            hist[2][i] = x[i];
+            const bf16x8 col{ub[0][i], ub[1][i], ub[2][i], ub[3][i], ub[4][i], ub[5][i], ub[6][i], ub[7][i]};
+            *reinterpret_cast<bf16x8*>(&sm.Vt[buf][(ch0 - 2 * kD + i) * kVtLd + tau0]) = col;
         }
-        const bf16x4 ub = __builtin_convertvector(u, bf16x4);
-        if (is_v) {
+    } else {
+        __bf16* dst0 = ch0 < kD ? &sm.Qs[buf][pos(ch0)] : &sm.Ks[buf][pos(ch0 - kD)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vcol[i][tt] = ub[i];
-        } else {
-            *reinterpret_cast<bf16x4*>(dst0 + tau * kKsLd) = ub;
-        }
-    }
-    if (is_v) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<bf16x8*>(&sm.Vt[buf][(ch0 - 2 * kD + i) * kVtLd + tau0]) = vcol[i];
+        for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
     }
 }
 
@@ -360,37 +147,11 @@ __device__ __forceinline__ void phase_rows(const PrefillParams& p, Smem<NW>& sm,
     }
     for (int job = tid; job < 3 * kC; job += NT) {
         if (job < kC) {
-            const int tau = job;
-            const int64_t t = local0 + tau;
-            const bool valid = t >= 0 && t < cx.L;
-            float gv = 0.f, bv = 0.f;
-            if (valid) {
-                const int64_t gi = ((int64_t)cx.b * cx.L + t) * p.num_v_heads + cx.h;
-                const float av = bf16_bits_to_f32(static_cast<const uint16_t*>(p.a)[gi]);
-                const float bb = bf16_bits_to_f32(static_cast<const uint16_t*>(p.b)[gi]);
-                gv = cx.neg_A * softplus_f32(av + cx.dt_h);
-                bv = sigmoid_f32(bb);
-            }
-            float s = gv;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(s, off, 64);
-                if (lane >= off) s += o;
-            }
-            sm.gam[tau] = s;
-            sm.beta[tau] = bv;
+            gates_scan(p, cx.b, cx.h, cx.neg_A, cx.dt_h, local0, lane, sm.gam, sm.beta);
         } else {
             const bool isq = job < 2 * kC;
             const int tau = job % kC;
-            const __bf16* row = (isq ? Qs : Ks) + tau * kKsLd;
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < kD; c += 8) {
-                const f32x8 v = to_f32x8(lds_load8(row + c));
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(v[i], v[i], acc);
-            }
-            const float n = (isq ? p.q_scale : 1.0f) / sqrtf(acc + p.l2_eps);
+            const float n = row_inv_norm((isq ? Qs : Ks) + tau * kKsLd, isq ? p.q_scale : 1.0f, p.l2_eps);
             (isq ? sm.nq : sm.nk)[tau] = n;
         }
     }
@@ -429,39 +190,6 @@ __device__ __forceinline__ void phase_masks(Smem<NW>& sm, int buf, int gbuf, int
             mask_pair(sm, pi, gram_tile(sm.Ks[buf], sm.Qs[buf], pi, li, lq),
                       gram_tile(sm.Ks[buf], sm.Qs[buf], 10 + pi, li, lq), lane);
     }
-}
-
-// ---- A4: inverses of the four diagonal blocks, (I + A_mm)^-1 = I + N_mm, by
-// substitution (one wave, lane = (block m, column c)).  The off-diagonal
-// coupling is applied in the state phase by blocked forward substitution, so
-// no other part of (I + A)^-1 is formed.
-template <int NW>
-__device__ __forceinline__ void phase_diag(Smem<NW>& sm, int lane) {
-    // right-looking: once x[i] is final, subtract its contribution from every
-    // later row (column i of A_mm is row i of AdT), so the dependent chain is
-    // one FMA per row
-    const int m = lane / 16, c = lane % 16;
-    const float* At = sm.AdT + m * 16 * kXLd;
-    float x[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) x[rr] = rr == c ? 1.f : 0.f;
-    float col[2][16];   // column i of A_mm, loaded one step ahead
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) col[0][rr] = At[rr];
-#pragma unroll
-    for (int i = 0; i < 15; ++i) {
-        if (i + 1 < 15) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) col[(i + 1) & 1][rr] = At[(i + 1) * kXLd + rr];
-        }
-        const float xi = x[i];
-#pragma unroll
-        for (int rr = i + 1; rr < 16; ++rr) x[rr] = fmaf(-col[i & 1][rr], xi, x[rr]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
 }
 
 // ---- B1: state-dependent products of a chunk, per wave (16 state columns):
@@ -528,27 +256,10 @@ __device__ __forceinline__ void phase_state(Smem<NW>& sm, int buf, f32x4 S[8], f
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
-    // (I + A) Delta = R by blocked forward substitution over the four 16-row
-    // blocks: Y_m = R_m - sum_{k<m} A_mk Delta_k, then Delta_m = Y_m + N_mm Y_m.
-    // The fp32 accumulator carries R and Y exactly; only the coupling terms
-    // see bf16 operands.
     f32x4 Dl[4];
     bf16x4 Db[4];
-    const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
     const bf16x4 dg[4] = {d0, d1, d2, d3};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f32x4 y = R[m];
-        if (m == 1) y = mfma16(cat4(a10, z4), cat4(Db[0], z4), y);
-        if (m == 2) y = mfma16(a2x, cat4(Db[0], Db[1]), y);
-        if (m == 3) {
-            y = mfma16(a3x, cat4(Db[0], Db[1]), y);
-            y = mfma16(cat4(a32, z4), cat4(Db[2], z4), y);
-        }
-        const bf16x4 yb = __builtin_convertvector(y, bf16x4);
-        Dl[m] = mfma16(cat4(dg[m], z4), cat4(yb, z4), y);
-        Db[m] = __builtin_convertvector(Dl[m], bf16x4);
-    }
+    delta_substitution(R, dg, a10, a2x, a3x, a32, Dl, Db);
     BD[0] = cat4(Db[0], Db[1]);
     BD[1] = cat4(Db[2], Db[3]);
     // S <- exp(gamma_C) S + K^T Delta',  Delta' = exp(gamma_C - gamma) n_k Delta  (hi + lo)
@@ -563,15 +274,7 @@ __device__ __forceinline__ void phase_state(Smem<NW>& sm, int buf, f32x4 S[8], f
     const float eC = expf(sm.gam[kC - 1]);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 BH[2], BL[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const f32x4 q0 = su[2 * ks] * Dl[2 * ks], q1 = su[2 * ks + 1] * Dl[2 * ks + 1];
-        BH[ks] = to_bf16x8(q0, q1);
-        const f32x8 back = to_f32x8(BH[ks]);
-        const f32x4 l0 = {q0[0] - back[0], q0[1] - back[1], q0[2] - back[2], q0[3] - back[3]};
-        const f32x4 l1 = {q1[0] - back[4], q1[1] - back[5], q1[2] - back[6], q1[3] - back[7]};
-        BL[ks] = to_bf16x8(l0, l1);
-    }
+    split_hi_lo(su, Dl, BH, BL);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         if (t == 4) {
@@ -729,7 +432,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         __syncthreads();
         phase_masks(sm, 0, 1, tid);
         __syncthreads();
-        if (wave == 0) phase_diag(sm, lane);
+        if (wave == 0) diag_solve<false>(sm, lane);
         __syncthreads();
     }
 
@@ -758,7 +461,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         if (next) phase_masks(sm, nbuf, buf, tid);
         __syncthreads();
         if (next) {
-            if (wave == 0) phase_diag(sm, lane);
+            if (wave == 0) diag_solve<false>(sm, lane);
             __syncthreads();
         }
     }

@@ -141,11 +141,15 @@ def prefill_workspace_bytes(cfg: Config, seq_len: int) -> int:
 def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
                     rec_state_in=None, *, start_pos: int = 0, ckpt_interval: int = 0,
                     ckpt_buf=None, out=None, conv_state_out=None, rec_state_out=None,
-                    stream=None):
+                    workspace="auto", stream=None):
     """Chunked prefill; returns (out, conv_state_out, rec_state_out).
 
     Outputs not passed in are allocated with torch.  ``ckpt_buf`` is a uint8
     device tensor of at least ``state_checkpoint(...)[1]`` bytes.
+    ``workspace``: "auto" allocates ``prefill_workspace_bytes`` (two-pass
+    path, whole call in one segment); a contiguous uint8 device tensor is used
+    as given (any size; below one chunk's worth the fused path runs); None
+    runs the fused single-pass kernel.
     """
     B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
     L = qkv.shape[1]
@@ -173,8 +177,17 @@ def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_i
         if not ckpt_buf.is_cuda or not ckpt_buf.is_contiguous():
             raise ValueError("ckpt_buf must be a contiguous device tensor")
         ck_bytes = ckpt_buf.numel() * ckpt_buf.element_size()
-    ws = prefill_workspace_bytes(cfg, L)
-    wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        ws = prefill_workspace_bytes(cfg, L)
+        wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    elif workspace is None:
+        ws, wsbuf = 0, None
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws, wsbuf = workspace.numel() * workspace.element_size(), workspace
     st = _lib.gdn_prefill_chunked(
         ctypes.byref(cfg.c()), L, start_pos, _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
         _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out),

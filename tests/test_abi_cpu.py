@@ -86,8 +86,17 @@ def test_checkpoint_plan_errors(G):
     assert f(ctypes.byref(bad.c()), 0, 100, 64, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
 
 
-def test_workspace_is_zero(G):
-    assert G.prefill_workspace_bytes(cfg(G), 16384) == 0
+def test_workspace_bytes(G):
+    """B x (chunks a call of L tokens can span, from any start) x per-chunk
+    records (H_k x (Q, K, K^T) + H_v x (P, AN, row scales, V^T))."""
+    for B, Hk, Hv in ((1, 16, 48), (8, 16, 32), (2, 2, 6)):
+        per = B * (Hk * 3 * 64 * 128 * 2 + Hv * (2 * 64 * 64 * 2 + 5 * 64 * 4 + 128 * 64 * 2))
+        c = cfg(G, batch=B, num_k_heads=Hk, num_v_heads=Hv)
+        for L in (0, 1, 2, 63, 64, 65, 127, 128, 16384):
+            # brute force over the start offset inside a chunk
+            span = max((((s + L - 1) // 64) - s // 64 + 1) if L else 0 for s in range(64))
+            assert G.prefill_workspace_bytes(c, L) == span * per, (B, Hk, Hv, L)
+    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 49152 + 48 * 34048)
 
 
 FAKE = 1 << 34  # aligned, far-apart addresses that are never dereferenced: every call below fails validation
@@ -128,6 +137,13 @@ def test_prefill_rejects_unsupported_and_aliasing(G):
     assert f(*prefill_args(G, cfg(G), out=P(FAKE))) == G.GDN_EALIAS
     # checkpoint buffer too small
     assert f(*prefill_args(G, cfg(G), iv=64, ck=P(FAKE * 20), ck_bytes=16)) == G.GDN_ESPACE
+    # workspace: 256-byte alignment, no overlap with the other buffers (a
+    # workspace below one chunk's worth is not used, so it is not checked)
+    per = G.prefill_workspace_bytes(cfg(G), 1)
+    assert f(*prefill_args(G, cfg(G), ws=P(FAKE * 30 + 16), ws_bytes=per)) == G.GDN_EINVAL
+    assert f(*prefill_args(G, cfg(G), ws=P(FAKE * 9), ws_bytes=per)) == G.GDN_EALIAS
+    assert f(*prefill_args(G, cfg(G), ws=P(FAKE * 8 - 256), ws_bytes=per)) == G.GDN_EALIAS
+    assert f(*prefill_args(G, cfg(G), ws=P(FAKE * 30), ws_bytes=per, qkv=None)) == G.GDN_EINVAL
     # bad config
     assert f(*prefill_args(G, cfg(G, num_v_heads=20))) == G.GDN_EINVAL
     assert f(*prefill_args(G, cfg(G, l2_eps=-1.0))) == G.GDN_EINVAL

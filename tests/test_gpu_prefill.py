@@ -1,7 +1,9 @@
-"""GPU parity of the fused chunked prefill (gdn_prefill_chunked) with the fp64
-oracle, through the C ABI: small cases spanning several chunks and ragged
-tails in every kernel variant, edge lengths, unaligned starts, checkpoints and
-bitwise resume, continuation into decode, and the full-size workloads.
+"""GPU parity of the chunked prefill (gdn_prefill_chunked) with the fp64
+oracle, through the C ABI, on both paths (the fused single-pass kernel, run
+without a workspace, and the two-pass prep + state kernels, run with one):
+small cases spanning several chunks and ragged tails in every kernel variant,
+edge lengths, unaligned starts, checkpoints and bitwise resume, segmented
+workspaces, continuation into decode, and the full-size workloads.
 """
 import os
 
@@ -24,19 +26,29 @@ def G():
     return gdn
 
 
+PATHS = ["fused", "split"]
+WAVE_VARS = ("GDN_PREFILL_WAVES", "GDN_PREFILL_STATE_WAVES")
+
+
 @pytest.fixture
 def waves():
     """Force a kernel variant (2, 4 or 8 waves = 32, 64 or 128 state columns
-    per workgroup) for one test, then restore the size-based choice."""
-    old = os.environ.get("GDN_PREFILL_WAVES")
+    per workgroup of the fused or the state kernel) for one test, then
+    restore the size-based choice."""
+    old = {k: os.environ.get(k) for k in WAVE_VARS}
 
     def set_(n):
-        if n is None:
-            os.environ.pop("GDN_PREFILL_WAVES", None)
-        else:
-            os.environ["GDN_PREFILL_WAVES"] = str(n)
+        for k in WAVE_VARS:
+            if n is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = str(n)
     yield set_
-    set_(None if old is None else int(old))
+    for k, v in old.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
 
 
 def cfg_of(G, w):
@@ -44,15 +56,18 @@ def cfg_of(G, w):
 
 
 def gpu_prefill(G, w, d, seq=slice(None), start_pos=0, conv_in="init", rec_in="init",
-                ckpt_interval=0, ckpt_buf=None, rec_out=None):
+                ckpt_interval=0, ckpt_buf=None, rec_out=None, path="split", workspace="auto"):
+    """path "fused": no workspace; "split": the given workspace ("auto" = the
+    whole call in one segment)."""
     c = cfg_of(G, w)
+    ws = None if path == "fused" else workspace
     cin = d["conv_state"] if conv_in == "init" else conv_in
     rin = d["rec_state"] if rec_in == "init" else rec_in
     out, conv, S = G.prefill_chunked(c, d["qkv"][:, seq].contiguous(), d["a"][:, seq].contiguous(),
                                      d["b"][:, seq].contiguous(), d["conv_w"], d["A_log"],
                                      d["dt_bias"], cin, rin, start_pos=start_pos,
                                      ckpt_interval=ckpt_interval, ckpt_buf=ckpt_buf,
-                                     rec_state_out=rec_out)
+                                     rec_state_out=rec_out, workspace=ws)
     torch.cuda.synchronize()
     return out, conv, S
 
@@ -77,50 +92,99 @@ def small(**kw):
     return I.Workload(**base)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("nw", [2, 4, 8])
 @pytest.mark.parametrize("init", [False, True])
-def test_prefill_small_all_variants(G, waves, nw, init):
+def test_prefill_small_all_variants(G, waves, path, nw, init):
     """200 tokens = 3 full chunks + a ragged 8-token tail, two sequences."""
     waves(nw)
     w = small(init_state=init, seed=21 + init)
     inp = I.generate(w)
-    out, conv, S = gpu_prefill(G, w, to_dev(inp))
-    compare(f"small nw={nw} init={init}", w, out, conv, S, oracle_prefill(w, inp))
+    out, conv, S = gpu_prefill(G, w, to_dev(inp), path=path)
+    compare(f"small {path} nw={nw} init={init}", w, out, conv, S, oracle_prefill(w, inp))
 
 
-def test_prefill_gqa3_odd_group_count(G):
-    """r = 3 (the Qwen3.6-27B ratio) and B*H_k = 3 groups (not a multiple of 8)."""
-    w = small(batch=3, num_k_heads=1, num_v_heads=3, seq_len=130, init_state=True, seed=23)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("r", [3, 8])
+def test_prefill_gqa_odd_group_count(G, path, r):
+    """r = 3 (the Qwen3.6-27B ratio) and r = 8 (the largest group the
+    two-pass path takes) with B*H_k = 3 groups (not a multiple of 8)."""
+    w = small(batch=3, num_k_heads=1, num_v_heads=r, seq_len=130, init_state=True, seed=23)
     inp = I.generate(w)
-    out, conv, S = gpu_prefill(G, w, to_dev(inp))
-    compare("gqa3", w, out, conv, S, oracle_prefill(w, inp))
+    out, conv, S = gpu_prefill(G, w, to_dev(inp), path=path)
+    compare(f"gqa{r} {path}", w, out, conv, S, oracle_prefill(w, inp))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("L", [0, 1, 2, 3, 63, 64, 65])
-def test_prefill_edge_lengths(G, L):
+def test_prefill_edge_lengths(G, path, L):
     w = small(batch=1, seq_len=max(L, 1), init_state=True, seed=30 + L)
     inp = I.generate(w)
     d = to_dev(inp)
-    out, conv, S = gpu_prefill(G, w, d, seq=slice(0, L))
+    out, conv, S = gpu_prefill(G, w, d, seq=slice(0, L), path=path)
     if L == 0:
         assert torch.equal(S, d["rec_state"]) and torch.equal(conv, d["conv_state"])
         return
-    compare(f"L={L}", w, out, conv, S, oracle_prefill(w, inp, seq_slice=slice(0, L)))
+    compare(f"L={L} {path}", w, out, conv, S, oracle_prefill(w, inp, seq_slice=slice(0, L)))
 
 
-def test_prefill_unaligned_split_continuation(G):
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_unaligned_split_continuation(G, path):
     """Tokens 0..99 then 100..299 from the carried state (start_pos = 100,
     first chunk partial) == the oracle over all 300 tokens."""
     w = small(seq_len=300, init_state=True, seed=24)
     inp = I.generate(w)
     d = to_dev(inp)
-    o1, c1, S1 = gpu_prefill(G, w, d, seq=slice(0, 100))
-    o2, c2, S2 = gpu_prefill(G, w, d, seq=slice(100, 300), start_pos=100, conv_in=c1, rec_in=S1)
+    o1, c1, S1 = gpu_prefill(G, w, d, seq=slice(0, 100), path=path)
+    o2, c2, S2 = gpu_prefill(G, w, d, seq=slice(100, 300), start_pos=100, conv_in=c1, rec_in=S1,
+                             path=path)
     ref = oracle_prefill(w, inp)
-    compare("split@100", w, torch.cat([o1, o2], 1), c2, S2, ref)
+    compare(f"split@100 {path}", w, torch.cat([o1, o2], 1), c2, S2, ref)
 
 
-def test_prefill_checkpoints_and_bitwise_resume(G):
+@pytest.mark.parametrize("chunks", [1, 2, 3])
+def test_prefill_segmented_workspace(G, chunks):
+    """A workspace of 1, 2 or 3 chunks' worth runs the two passes segment by
+    segment (state carried through rec_state_out, checkpoints included) and
+    gives the single-segment result bit for bit; a workspace one byte short
+    of a chunk runs the fused path."""
+    w = small(seq_len=460, init_state=True, seed=29)
+    inp = I.generate(w)
+    d = to_dev(inp)
+    c = cfg_of(G, w)
+    per = G.prefill_workspace_bytes(c, 1)
+    ents, nbytes = G.state_checkpoint(c, 37, 423, 128)
+    bufs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    seq = slice(37, 460)
+    full = gpu_prefill(G, w, d, seq=seq, start_pos=37, ckpt_interval=128, ckpt_buf=bufs[0])
+    ws = torch.empty(chunks * per + 100, dtype=torch.uint8, device="cuda")
+    seg = gpu_prefill(G, w, d, seq=seq, start_pos=37, ckpt_interval=128, ckpt_buf=bufs[1], workspace=ws)
+    for x, y in zip(full, seg):
+        assert torch.equal(x, y)
+    assert torch.equal(bufs[0], bufs[1])
+    fused = gpu_prefill(G, w, d, seq=seq, start_pos=37, path="fused")
+    short = gpu_prefill(G, w, d, seq=seq, start_pos=37, workspace=ws[:per - 1])
+    for x, y in zip(fused, short):
+        assert torch.equal(x, y)
+
+
+def test_prefill_paths_agree(G):
+    """The two paths compute the same values in the same precision; print how
+    far apart they are and hold them to a bar well inside the oracle's."""
+    w = small(batch=2, seq_len=700, num_k_heads=2, num_v_heads=6, init_state=True, seed=31)
+    d = to_dev(I.generate(w))
+    f = gpu_prefill(G, w, d, path="fused")
+    s = gpu_prefill(G, w, d, path="split")
+    e_out = rel(s[0].double().cpu().numpy(), f[0].double().cpu().numpy())
+    e_state = rel(s[2].double().cpu().numpy(), f[2].double().cpu().numpy())
+    print(f"[paths] out rel {e_out:.3e}, state rel {e_state:.3e}, bitwise "
+          f"{torch.equal(f[0], s[0]) and torch.equal(f[2], s[2])}", flush=True)
+    assert torch.equal(f[1], s[1])
+    assert e_out <= 1e-3 and e_state <= 1e-4
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_checkpoints_and_bitwise_resume(G, path):
     """Slots every 128 tokens hold the oracle's state after those positions and
     bit copies of the conv tail; resuming from a slot repeats the
     uninterrupted call bit for bit."""
@@ -131,9 +195,9 @@ def test_prefill_checkpoints_and_bitwise_resume(G):
     ents, nbytes = G.state_checkpoint(c, 0, 600, 128)
     assert [e.position for e in ents] == [128, 256, 384, 512]
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    out, conv, S = gpu_prefill(G, w, d, ckpt_interval=128, ckpt_buf=buf)
+    out, conv, S = gpu_prefill(G, w, d, ckpt_interval=128, ckpt_buf=buf, path=path)
     ref = oracle_prefill(w, inp, want_ckpt=True, ckpt_interval=128)
-    compare("ckpt run", w, out, conv, S, ref)
+    compare(f"ckpt run {path}", w, out, conv, S, ref)
 
     def slot(e):
         cv = buf[e.conv_offset:e.conv_offset + w.batch * w.conv_dim * 3 * 2].view(torch.bfloat16)
@@ -149,7 +213,7 @@ def test_prefill_checkpoints_and_bitwise_resume(G):
     cv, rs = slot(ents[1])
     buf2 = torch.zeros_like(buf)
     o2, c2, S2 = gpu_prefill(G, w, d, seq=slice(256, 600), start_pos=256, conv_in=cv.clone(),
-                             rec_in=rs.clone(), ckpt_interval=128, ckpt_buf=buf2)
+                             rec_in=rs.clone(), ckpt_interval=128, ckpt_buf=buf2, path=path)
     assert torch.equal(o2, out[:, 256:]) and torch.equal(S2, S) and torch.equal(c2, conv)
     for e in ents[2:]:
         assert torch.equal(buf2[e.conv_offset:e.conv_offset + ents[0].rec_offset],
@@ -158,24 +222,26 @@ def test_prefill_checkpoints_and_bitwise_resume(G):
         assert torch.equal(buf2[e.rec_offset:e.rec_offset + n], buf[e.rec_offset:e.rec_offset + n])
 
 
-def test_prefill_deterministic_and_in_place(G):
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_deterministic_and_in_place(G, path):
     w = small(seq_len=257, init_state=True, seed=26)
     d = to_dev(I.generate(w))
-    a = gpu_prefill(G, w, d)
-    b = gpu_prefill(G, w, d)
+    a = gpu_prefill(G, w, d, path=path)
+    b = gpu_prefill(G, w, d, path=path)
     S_in = d["rec_state"].clone()
-    c = gpu_prefill(G, w, d, rec_in=S_in, rec_out=S_in)
+    c = gpu_prefill(G, w, d, rec_in=S_in, rec_out=S_in, path=path)
     for x, y, z in zip(a, b, c):
         assert torch.equal(x, y) and torch.equal(x, z)
 
 
-def test_prefill_then_decode(G):
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_then_decode(G, path):
     """Prefill 192 tokens, then 16 decode steps from the produced state ==
     the oracle over the 208 tokens."""
     w = small(seq_len=208, init_state=True, seed=27)
     inp = I.generate(w)
     d = to_dev(inp)
-    out, conv, S = gpu_prefill(G, w, d, seq=slice(0, 192))
+    out, conv, S = gpu_prefill(G, w, d, seq=slice(0, 192), path=path)
     c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
     outs = []
     for t in range(192, 208):
@@ -185,18 +251,19 @@ def test_prefill_then_decode(G):
         outs.append(o)
     torch.cuda.synchronize()
     full = torch.cat([out, torch.stack(outs, 1)], 1)
-    compare("prefill+decode", w, full, conv, S, oracle_prefill(w, inp))
+    compare(f"prefill+decode {path}", w, full, conv, S, oracle_prefill(w, inp))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("stress", ["slowdecay", "extreme"])
-def test_prefill_stress(G, stress):
+def test_prefill_stress(G, path, stress):
     """Not part of the target bars' workloads, held to the same bars: long
     memory (decay close to 1) and gates in their tails."""
     w = small(seq_len=640, init_state=True, seed=28)
     w = I.slow_decay(w) if stress == "slowdecay" else I.extreme_gates(w)
     inp = I.generate(w)
-    out, conv, S = gpu_prefill(G, w, to_dev(inp))
-    compare(stress, w, out, conv, S, oracle_prefill(w, inp))
+    out, conv, S = gpu_prefill(G, w, to_dev(inp), path=path)
+    compare(f"{stress} {path}", w, out, conv, S, oracle_prefill(w, inp))
 
 
 # ------------------------------------------------------------ full workloads
@@ -206,9 +273,12 @@ def test_workload_qwen36_prefill_16k(G):
     (several key heads, each position in the repeat-interleave group)."""
     w = I.WORKLOADS[2]
     inp = I.generate(w)
-    out, conv, S = gpu_prefill(G, w, to_dev(inp))
+    d = to_dev(inp)
     heads = [0, 1, 2, 23, 46, 47]
-    compare("16k", w, out, conv, S, oracle_prefill(w, inp, heads=heads), heads=heads)
+    ref = oracle_prefill(w, inp, heads=heads)
+    for path in PATHS:
+        out, conv, S = gpu_prefill(G, w, d, path=path)
+        compare(f"16k {path}", w, out, conv, S, ref, heads=heads)
 
 
 def test_workload_coder_next_prefill_4k_then_decode(G):
@@ -218,11 +288,13 @@ def test_workload_coder_next_prefill_4k_then_decode(G):
     w = I.WORKLOADS[3]
     inp = I.generate(w)
     d = to_dev(inp)
-    out, conv, S = gpu_prefill(G, w, d)
     heads, bi = [0, 1, 17, 31], [0, 5]
     full = oracle_prefill(w, inp, batch_idx=bi)
     ref = {"out": full["out"][:, :, heads], "S": full["S"][:, heads], "conv_tail": full["conv_tail"]}
-    compare("4k prefill", w, out, conv, S, ref, heads=heads, batch_idx=bi)
+    out, conv, S = gpu_prefill(G, w, d, path="fused")
+    compare("4k prefill fused", w, out, conv, S, ref, heads=heads, batch_idx=bi)
+    out, conv, S = gpu_prefill(G, w, d, path="split")
+    compare("4k prefill split", w, out, conv, S, ref, heads=heads, batch_idx=bi)
     c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
     outs = []
     for s in range(64):
