@@ -121,32 +121,40 @@ __device__ __forceinline__ void write_tail(const PrefillParams& p, int b, int64_
     }
 }
 
-// Front end of one work item: channels gc..gc+3 of sequence b at the eight
-// chunk rows tau0..tau0+7 (call-local tokens local0 + tau): depthwise causal
-// conv with taps w[j][i] (tap j of channel i; tap 3 multiplies the current
-// token) in fp32, SiLU, bf16.  The eleven 8-byte row loads (3 halo rows + 8)
-// are issued together.  INTERIOR: every row lies inside the call.  Otherwise
+// Front end of one work item: channels gc..gc+3 of sequence b at the TT
+// chunk rows tau0..tau0+TT-1 (call-local tokens local0 + tau): depthwise
+// causal conv with taps w[j][i] (tap j of channel i; tap 3 multiplies the
+// current token) in fp32, SiLU, bf16.  raw[k] holds the pre-conv inputs of
+// the four channels at row tau0 - 3 + k.  conv_load issues the TT + 3 8-byte
+// row loads together, so a caller can start the next item's loads before
+// computing this one.  INTERIOR: every row lies inside the call.  Otherwise
 // row indices are clamped into the call, rows before it are replaced by the
 // carried conv state and rows outside it produce zeros.
-template <bool INTERIOR>
-__device__ __forceinline__ void conv_item(const PrefillParams& p, int b, int64_t gc, int64_t local0, int tau0,
-                                          const float w[4][4], bf16x4 ub[8]) {
+template <bool INTERIOR, int TT = 8>
+__device__ __forceinline__ void conv_load(const PrefillParams& p, int b, int64_t gc, int64_t local0, int tau0,
+                                          uint2 raw[TT + 3]) {
     const int64_t L = p.seq_len;
     const int64_t t_first = local0 + tau0 - 3;
-    uint2 raw[11];
     if (INTERIOR) {
         const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + ((int64_t)b * L + t_first) * p.conv_dim + gc;
         const int cd = (int)p.conv_dim;
 #pragma unroll
-        for (int j = 0; j < 11; ++j) raw[j] = *reinterpret_cast<const uint2*>(src + j * cd);
+        for (int j = 0; j < TT + 3; ++j) raw[j] = *reinterpret_cast<const uint2*>(src + j * cd);
     } else {
         const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * L * p.conv_dim + gc;
 #pragma unroll
-        for (int j = 0; j < 11; ++j) {
+        for (int j = 0; j < TT + 3; ++j) {
             const int64_t tc = min(max(t_first + j, (int64_t)0), L - 1);
             raw[j] = *reinterpret_cast<const uint2*>(src + tc * p.conv_dim);
         }
     }
+}
+
+template <bool INTERIOR, int TT = 8>
+__device__ __forceinline__ void conv_compute(const PrefillParams& p, int b, int64_t gc, int64_t local0, int tau0,
+                                             const float w[4][4], const uint2 raw[TT + 3], bf16x4 ub[TT]) {
+    const int64_t L = p.seq_len;
+    const int64_t t_first = local0 + tau0 - 3;
     float hist[3][4];
 #pragma unroll
     for (int j = 0; j < 3; ++j) unpack_bf16x4(raw[j], hist[j]);
@@ -156,7 +164,7 @@ __device__ __forceinline__ void conv_item(const PrefillParams& p, int b, int64_t
             if (t_first + j < 0) load_x4_state(p, b, t_first + j, gc, hist[j]);
     }
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
         const int64_t t = local0 + tau0 + tt;
         float x[4];
         unpack_bf16x4(raw[3 + tt], x);
@@ -173,6 +181,14 @@ __device__ __forceinline__ void conv_item(const PrefillParams& p, int b, int64_t
         }
         ub[tt] = __builtin_convertvector(u, bf16x4);
     }
+}
+
+template <bool INTERIOR>
+__device__ __forceinline__ void conv_item(const PrefillParams& p, int b, int64_t gc, int64_t local0, int tau0,
+                                          const float w[4][4], bf16x4 ub[8]) {
+    uint2 raw[11];
+    conv_load<INTERIOR>(p, b, gc, local0, tau0, raw);
+    conv_compute<INTERIOR>(p, b, gc, local0, tau0, w, raw, ub);
 }
 
 // Gates of value head h for the 64 chunk rows (one full wave, lane = row):

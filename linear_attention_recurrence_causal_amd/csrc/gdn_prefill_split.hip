@@ -8,16 +8,20 @@
 //
 //   prep  (one workgroup per sequence, key head and chunk; every chunk of a
 //         segment in parallel): front end of the q, k channels of the key
-//         head and the v channels of its value heads, K^T, L2 norms, the raw
-//         K K^T / Q K^T tiles, and per value head the gates, decay masks,
-//         row scales and the diagonal-block inverses.  Results go to
-//         workspace records in the operand order of the state kernel.
-//   state (one workgroup per sequence, value head and slice of 16*NW state
-//         columns; chunks in order): per chunk only the state-dependent
-//         products -- K S0, Q S0, R, Delta by blocked forward substitution,
-//         O, and the state update -- with the next chunk's records copied
-//         into the other LDS buffer by global_load_lds while this chunk
-//         computes.
+//         head, L2 norms, the raw K K^T / Q K^T tiles, and per value head
+//         of the group the gates, decay masks, row scales and the
+//         diagonal-block inverses.  Results go to workspace records in the
+//         operand order of the state kernel.
+//   state (one workgroup per sequence, value head and slice of 16 * NW
+//         state columns, NW = 2 or 4; chunks in order): NW compute waves do
+//         only the state-dependent products of each chunk -- K S0, Q S0, R,
+//         Delta by blocked forward substitution, the state update, O --
+//         while 8 - NW memory waves store the previous chunk's O rows and
+//         prepare the next chunk in the other LDS buffer: its records by
+//         global_load_lds, K^T by an LDS transpose of K, and the front end of
+//         the slice's v channels (conv + SiLU from a raw slab copied one chunk
+//         earlier; the slice's own columns, so no value-head data goes
+//         through the workspace).
 //
 // A workspace smaller than the whole call is used segment by segment (prep
 // then state for each run of chunks that fits); the state travels between
@@ -33,28 +37,19 @@ namespace {
 using namespace chunked;
 
 // ---- workspace records.  Matrices are row-major, columns in pos() order,
-// unpadded.  Key record (sequence, key head, chunk): Q | K | K^T.  Value
-// record (sequence, value head, chunk): P | AN | five rows of 64 fp32
+// unpadded.  Key record (sequence, key head, chunk): Q | K.  Value record
+// (sequence, value head, chunk): P | AN | five rows of 64 fp32
 // (beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k |
-// exp(gamma_C), 0, ...) | V^T ([column][token], natural token order).
+// exp(gamma_C), 0, ...).
 constexpr int kRecQ = 0;
 constexpr int kRecK = kC * kD * 2;
-constexpr int kRecKt = 2 * kC * kD * 2;
-constexpr int kKeyRec = 3 * kC * kD * 2;            // 49152
+constexpr int kKeyRec = 2 * kC * kD * 2;            // 32768
 constexpr int kRecP = 0;
 constexpr int kRecAN = kC * kC * 2;
 constexpr int kRecTok = 2 * kC * kC * 2;
 constexpr int kTokBytes = 5 * kC * 4;
-constexpr int kRecVt = kRecTok + kTokBytes;
-constexpr int kValRec = kRecVt + kD * kC * 2;       // 34048
+constexpr int kValRec = kRecTok + kTokBytes;        // 17664
 static_assert(kKeyRec % 256 == 0 && kValRec % 256 == 0, "records keep 256-byte alignment");
-
-// State-kernel LDS buffer: the key record and the first three parts of the
-// value record, back to back (Q | K | K^T | P | AN | rows).
-constexpr int kBufQ = 0, kBufK = kRecK, kBufKt = kRecKt, kBufP = kKeyRec, kBufAN = kKeyRec + kRecAN,
-              kBufTok = kKeyRec + kRecTok;
-constexpr int kBufBytes = kKeyRec + kRecVt;         // 66816
-constexpr int kPieces = (kBufBytes + 1023) / 1024;  // 1 KiB per wave-wide global_load_lds
 
 constexpr int kMaxGroup = 8;                        // value heads per key head on this path
 
@@ -83,6 +78,10 @@ __device__ __forceinline__ char* val_rec(const SplitParams& s, int b, int h, int
 __device__ __forceinline__ int swz256(int row, int g) { return row * 256 + 16 * (g ^ (row & 7)); }
 __device__ __forceinline__ int swz128(int row, int g) { return row * 128 + 16 * (g ^ (row & 7)); }
 
+__device__ __forceinline__ void copy16(char* dst, const void* src) {
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
 // ============================================================ prep kernel
 constexpr int kPrepWaves = 8;
 constexpr int kPrepThreads = 64 * kPrepWaves;
@@ -93,16 +92,50 @@ struct alignas(16) PrepSmem {
     __bf16 Ps[kC * kKtLd];
     __bf16 AN[kC * kKtLd];
     float AdT[4 * 16 * kXLd];
-    alignas(16) float beta[kC];
-    alignas(16) float gam[kC];
+    alignas(16) float beta[kMaxGroup][kC];   // per value head of the group
+    alignas(16) float gam[kMaxGroup][kC];
     alignas(16) float nq[kC];
     alignas(16) float nk[kC];
     float tokS[5][kC];
-    float Ws[4 * (2 + kMaxGroup) * kD];   // conv taps [tap][channel]: q, k, then the group's v
+    uint16_t Ws[4 * 2 * kD];   // conv taps (bf16 bits) [tap][channel]: q, then k
 };
 
-__device__ __forceinline__ void copy16(char* dst, const void* src) {
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+// One value head's view of the prep LDS, in the member names the shared
+// mask, row-scale and solve helpers use.
+struct PrepHeadView {
+    float* gam;
+    float* beta;
+    float* nq;
+    float* nk;
+    __bf16* Ps;
+    __bf16* AN;
+    float* AdT;
+    float (*tokS)[kC];
+};
+
+// Global channel of prep channel index ch: q then k of key head kh
+__device__ __forceinline__ int64_t qk_channel(int ch, int kh, int Hk) {
+    return ch < kD ? (int64_t)kh * kD + ch : (int64_t)Hk * kD + (int64_t)kh * kD + ch - kD;
+}
+
+// Front end of the q, k channels of a chunk -> LDS rows (4 channels x 8 rows
+// per item, one item per thread)
+template <bool INTERIOR>
+__device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm, int b, int kh, int64_t local0,
+                                           int tid) {
+    static_assert(2 * kD / 4 * 8 == kPrepThreads, "one front-end item per thread");
+    const int ch0 = (tid % 64) * 4, tau0 = (tid / 64) * 8;
+    const int64_t gc = qk_channel(ch0, kh, p.num_k_heads);
+    uint2 raw[11];
+    conv_load<INTERIOR>(p, b, gc, local0, tau0, raw);
+    float w[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) unpack_bf16x4(*reinterpret_cast<const uint2*>(&sm.Ws[t * 2 * kD + ch0]), w[t]);
+    bf16x4 ub[8];
+    conv_compute<INTERIOR>(p, b, gc, local0, tau0, w, raw, ub);
+    __bf16* dst0 = ch0 < kD ? &sm.Qs[pos(ch0)] : &sm.Ks[pos(ch0 - kD)];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
 }
 
 __global__ __launch_bounds__(kPrepThreads)
@@ -117,15 +150,17 @@ void prep_kernel(SplitParams sp) {
     const int b = grp / Hk, kh = grp % Hk;
     const int64_t local0 = (sp.k0 + j) * kC - p.start_pos;
     char* krec = key_rec(sp, b, kh, j);
-    const int nch = (2 + r) * kD;
 
-    // ---- set-up: conv taps -> LDS; zero the upper tiles of P and AN (the
+    // ---- set-up: gates of every value head of the group (wave hh: head
+    // kh r + hh); conv taps -> LDS; zero the upper tiles of P and AN (the
     // masks never write them) and the unused part of the fifth row
-    for (int e = tid; e < nch * 4; e += kPrepThreads) {
-        const int ch = e % nch, tap = e / nch;
-        const int64_t gc = ch < 2 * kD ? (ch < kD ? (int64_t)kh * kD + ch : (int64_t)Hk * kD + (int64_t)kh * kD + ch - kD)
-                                       : 2 * (int64_t)Hk * kD + (int64_t)kh * r * kD + (ch - 2 * kD);
-        sm.Ws[tap * nch + ch] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + tap]);
+    if (wave < r) {
+        const int h = kh * r + wave;
+        gates_scan(p, b, h, -expf(p.A_log[h]), p.dt_bias[h], local0, lane, sm.gam[wave], sm.beta[wave]);
+    }
+    for (int e = tid; e < 2 * kD * 4; e += kPrepThreads) {
+        const int ch = e % (2 * kD), tap = e / (2 * kD);
+        sm.Ws[e] = static_cast<const uint16_t*>(p.conv_w)[qk_channel(ch, kh, Hk) * 4 + tap];
     }
     for (int e = tid; e < 6 * 256; e += kPrepThreads) {
         const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
@@ -137,59 +172,15 @@ void prep_kernel(SplitParams sp) {
     if (tid < kC) sm.tokS[4][tid] = 0.f;
     __syncthreads();
 
-    // ---- front end: q, k -> LDS rows; v -> the V^T part of each value record
-    {
-        const int cg4 = nch / 4;
-        const bool interior = local0 >= 3 && local0 + kC <= p.seq_len;
-        for (int item = tid; item < cg4 * 8; item += kPrepThreads) {
-            const int ch0 = (item % cg4) * 4, tau0 = (item / cg4) * 8;
-            const int64_t gc = ch0 < 2 * kD ? (ch0 < kD ? (int64_t)kh * kD + ch0
-                                                         : (int64_t)Hk * kD + (int64_t)kh * kD + ch0 - kD)
-                                            : 2 * (int64_t)Hk * kD + (int64_t)kh * r * kD + (ch0 - 2 * kD);
-            float w[4][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const f32x4 wv = *reinterpret_cast<const f32x4*>(&sm.Ws[t * nch + ch0]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[t][i] = wv[i];
-            }
-            bf16x4 ub[8];
-            if (interior) conv_item<true>(p, b, gc, local0, tau0, w, ub);
-            else conv_item<false>(p, b, gc, local0, tau0, w, ub);
-            if (ch0 < 2 * kD) {
-                __bf16* dst0 = ch0 < kD ? &sm.Qs[pos(ch0)] : &sm.Ks[pos(ch0 - kD)];
-#pragma unroll
-                for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
-            } else {
-                const int hh = (ch0 - 2 * kD) / kD, col = (ch0 - 2 * kD) % kD;
-                char* vt = val_rec(sp, b, kh * r + hh, j) + kRecVt;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x8 v{ub[0][i], ub[1][i], ub[2][i], ub[3][i], ub[4][i], ub[5][i], ub[6][i], ub[7][i]};
-                    *reinterpret_cast<bf16x8*>(vt + (col + i) * (kC * 2) + tau0 * 2) = v;
-                }
-            }
-        }
-    }
+    // ---- front end of q, k
+    if (local0 >= 3 && local0 + kC <= p.seq_len) prep_front<true>(p, sm, b, kh, local0, tid);
+    else prep_front<false>(p, sm, b, kh, local0, tid);
     __syncthreads();
 
-    // ---- Q, K, K^T -> key record; L2 norms; raw Gram tiles (registers)
+    // ---- Q, K -> key record; L2 norms; raw Gram tiles (registers)
     for (int e = tid; e < 2 * kC * 16; e += kPrepThreads) {
         const int mat = e >> 10, row = (e >> 4) & 63, g = e & 15;
         copy16(krec + (mat ? kRecK : kRecQ) + row * 256 + 16 * g, (mat ? sm.Ks : sm.Qs) + row * kKsLd + 8 * g);
-    }
-    for (int e = tid; e < kD * 8; e += kPrepThreads) {
-        // granule G of K^T row d holds tokens 32a + 4q + {0..3}, 32a + 16 + 4q + {0..3}
-        const int d = e >> 3, G = e & 7;
-        const int x0 = 32 * (G >> 2) + 4 * (G & 3);
-        const int pd = pos(d);
-        bf16x8 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = sm.Ks[(x0 + i) * kKsLd + pd];
-            v[4 + i] = sm.Ks[(x0 + 16 + i) * kKsLd + pd];
-        }
-        *reinterpret_cast<bf16x8*>(krec + kRecKt + d * (kC * 2) + 16 * G) = v;
     }
     if (tid < 2 * kC) {
         const bool isq = tid < kC;
@@ -207,28 +198,20 @@ void prep_kernel(SplitParams sp) {
     }
     __syncthreads();
 
-    // ---- per value head of the group: gates, masks, row scales, diagonal
+    // ---- per value head of the group: masks, row scales, diagonal
     // inverses -> value record
     for (int hh = 0; hh < r; ++hh) {
-        const int h = kh * r + hh;
-        char* vrec = val_rec(sp, b, h, j);
-        if (wave == 0) {
-            gates_scan(p, b, h, -expf(p.A_log[h]), p.dt_bias[h], local0, lane, sm.gam, sm.beta);
-        } else if (hh > 0) {
-            char* prev = val_rec(sp, b, h - 1, j) + kRecAN;
-            for (int e = tid - 64; e < kC * 8; e += kPrepThreads - 64)
-                copy16(prev + (e >> 3) * 128 + 16 * (e & 7), sm.AN + (e >> 3) * kKtLd + 8 * (e & 7));
-        }
-        __syncthreads();
-        mask_pair(sm, wave, gk[0], gq[0], lane);
-        if (wave < 2) mask_pair(sm, 8 + wave, gk[1], gq[1], lane);
+        char* vrec = val_rec(sp, b, kh * r + hh, j);
+        PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, sm.Ps, sm.AN, sm.AdT, sm.tokS};
+        mask_pair(hv, wave, gk[0], gq[0], lane);
+        if (wave < 2) mask_pair(hv, 8 + wave, gk[1], gq[1], lane);
         if (wave == kPrepWaves - 1) {
-            row_scales(sm, lane);
-            if (lane == 0) sm.tokS[4][0] = expf(sm.gam[kC - 1]);
+            row_scales(hv, lane);
+            if (lane == 0) sm.tokS[4][0] = expf(sm.gam[hh][kC - 1]);
         }
         __syncthreads();
         if (wave == 0) {
-            diag_solve<true>(sm, lane);
+            diag_solve<true>(hv, lane);
         } else {
             for (int e = tid - 64; e < kC * 8 + kTokBytes / 16; e += kPrepThreads - 64) {
                 if (e < kC * 8) copy16(vrec + kRecP + (e >> 3) * 128 + 16 * (e & 7), sm.Ps + (e >> 3) * kKtLd + 8 * (e & 7));
@@ -236,47 +219,85 @@ void prep_kernel(SplitParams sp) {
             }
         }
         __syncthreads();
+        for (int e = tid; e < kC * 8; e += kPrepThreads)
+            copy16(vrec + kRecAN + (e >> 3) * 128 + 16 * (e & 7), sm.AN + (e >> 3) * kKtLd + 8 * (e & 7));
+        if (hh + 1 < r) __syncthreads();
     }
-    char* last = val_rec(sp, b, kh * r + r - 1, j) + kRecAN;
-    for (int e = tid; e < kC * 8; e += kPrepThreads)
-        copy16(last + (e >> 3) * 128 + 16 * (e & 7), sm.AN + (e >> 3) * kKtLd + 8 * (e & 7));
 }
 
 // ============================================================ state kernel
 #define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
 
-// Start the copy of one chunk's records into an LDS buffer: 1 KiB pieces,
-// one wave-wide global_load_lds_dwordx4 each, granules placed by swz256 /
-// swz128.  Completion is awaited with the workgroup barrier.
-template <int NW>
-__device__ __forceinline__ void issue_chunk(char* lds, const char* krec, const char* vrec, int wave, int lane) {
-    for (int pc = wave; pc < kPieces; pc += NW) {
-        const int o = pc * 1024 + 16 * lane;
-        const char* src;
-        bool act = true;
-        if (o < kBufKt) {
-            const int row = (o >> 8) & (kC - 1), s = (o >> 4) & 15;
-            src = krec + (o & ~255) + 16 * (s ^ (row & 7));
-        } else if (o < kBufP) {
-            const int l = o - kBufKt, row = l >> 7, s = (l >> 4) & 7;
-            src = krec + kRecKt + (l & ~127) + 16 * (s ^ (row & 7));
-        } else if (o < kBufTok) {
-            const int l = o - kBufP, row = l >> 7, s = (l >> 4) & 7;
-            src = vrec + (l & ~127) + 16 * (s ^ (row & 7));
-        } else {
-            const int l = o - kBufTok;
-            act = l < kTokBytes;
-            src = vrec + kRecTok + l;
-        }
-        if (act) __builtin_amdgcn_global_load_lds(src, LDS_PTR(lds + pc * 1024), 16, 0, 0);
-    }
+// P and AN in LDS hold only their lower triangle of 16x16 tiles: rows 0..31
+// keep granules 0..3 (64-byte rows), rows 32..63 all eight (128-byte rows).
+// Granules are XOR-swizzled so that eight consecutive rows read by one phase
+// of an LDS read hit eight different bank groups.
+constexpr int kPaMat = 32 * 64 + 32 * 128;          // 6144 bytes per matrix
+__device__ __forceinline__ int pa_off(int mat, int row, int g) {
+    return mat * kPaMat + (row < 32 ? row * 64 + 16 * (g ^ ((row >> 1) & 3))
+                                    : 2048 + (row - 32) * 128 + 16 * (g ^ (row & 7)));
 }
 
-// V rows 16m + 4lq + {0..3} of this lane's column (registers)
-__device__ __forceinline__ void load_v(const char* vrec, int col, int lq, bf16x4 vv[4]) {
-    const char* base = vrec + kRecVt + col * (kC * 2);
+// LDS buffer of one chunk: Q | K | K^T | P | AN | rows | V^T (V^T of the
+// slice's columns, row stride kVtLd).  Once the chunk's products are done,
+// its Q region stages the chunk's O rows ([64][slice] bf16).
+constexpr int kVtLd = kC + 4;                       // bf16 row stride of V^T (conflict-free column reads)
+constexpr int kBufQ = 0, kBufK = kC * kD * 2, kBufKt = 2 * kC * kD * 2, kBufPA = 3 * kC * kD * 2,
+              kBufTok = kBufPA + 2 * kPaMat, kBufVt = kBufTok + kTokBytes;
+static_assert(kBufPA % 1024 == 0 && kBufTok % 1024 == 0 && kBufVt % 16 == 0, "piece and row alignment");
+
+// Record copies of one chunk: 1 KiB pieces, one wave-wide
+// global_load_lds_dwordx4 each.  Pieces 0..15: Q, 16..31: K (256-byte rows),
+// 32..43: P | AN triangles, 44..45: the rows of scales (1280 bytes).
+constexpr int kPiecesK = 16, kPiecesPA = 32, kPiecesTok = 44, kPieces = 46;
+
+__device__ __forceinline__ void issue_piece(char* lds, const char* krec, const char* vrec, int pc, int lane) {
+    const char* src;
+    int dst;
+    bool act = true;
+    if (pc < kPiecesPA) {
+        const int o = (pc & 15) * 1024 + 16 * lane;   // offset inside Q or K
+        const int row = o >> 8, s = (o >> 4) & 15;
+        src = krec + (pc < kPiecesK ? kRecQ : kRecK) + row * 256 + 16 * (s ^ (row & 7));
+        dst = (pc < kPiecesK ? kBufQ : kBufK) + o;
+    } else if (pc < kPiecesTok) {
+        const int o = (pc - kPiecesPA) * 1024 + 16 * lane;
+        const int mat = o / kPaMat, l = o % kPaMat;
+        int row, g;
+        if (l < 2048) {
+            row = l >> 6;
+            g = ((l >> 4) & 3) ^ ((row >> 1) & 3);
+        } else {
+            row = 32 + ((l - 2048) >> 7);
+            g = ((l >> 4) & 7) ^ (row & 7);
+        }
+        src = vrec + mat * (kC * kC * 2) + row * 128 + 16 * g;
+        dst = kBufPA + o;
+    } else {
+        const int l = (pc - kPiecesTok) * 1024 + 16 * lane;
+        act = l < kTokBytes;
+        src = vrec + kRecTok + l;
+        dst = kBufTok + l;
+    }
+    if (act) __builtin_amdgcn_global_load_lds(src, LDS_PTR(lds + (dst & ~1023)), 16, 0, 0);
+}
+
+// K^T granules G in [g0, g0 + 4) of every row d from the chunk's K: granule G
+// of K^T row d holds tokens 32a + 4q + {0..3}, 32a + 16 + 4q + {0..3}
+// (a = G / 4, q = G % 4), which all lie in K rows 32a .. 32a + 31.
+__device__ __forceinline__ void transpose_k(char* buf, int g0, int lane) {
+    for (int e = lane; e < kD * 4; e += 64) {
+        const int d = e >> 2, G = g0 + (e & 3);
+        const int x0 = 32 * (G >> 2) + 4 * (G & 3);
+        const int pd = pos(d), gk = pd >> 3, ek = (pd & 7) * 2;
+        bf16x8 v;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) vv[m] = *reinterpret_cast<const bf16x4*>(base + (16 * m + 4 * lq) * 2);
+        for (int i = 0; i < 4; ++i) {
+            v[i] = *reinterpret_cast<const __bf16*>(buf + kBufK + swz256(x0 + i, gk) + ek);
+            v[4 + i] = *reinterpret_cast<const __bf16*>(buf + kBufK + swz256(x0 + 16 + i, gk) + ek);
+        }
+        *reinterpret_cast<bf16x8*>(buf + kBufKt + swz128(d, G)) = v;
+    }
 }
 
 __device__ __forceinline__ bf16x8 ld8(const char* buf, int off) { return *reinterpret_cast<const bf16x8*>(buf + off); }
@@ -326,14 +347,15 @@ __device__ __forceinline__ void state_products(const char* buf, f32x4 S[8], cons
         sb[m] = ldf4(buf, kBufTok + 4 * (0 * kC + r0));
         sr[m] = ldf4(buf, kBufTok + 4 * (1 * kC + r0));
     }
-    const bf16x4 d0 = ld4(buf, kBufAN + swz128(li, lq));
-    const bf16x4 d1 = ld4(buf, kBufAN + swz128(16 + li, lq) + 8);
-    const bf16x4 d2 = ld4(buf, kBufAN + swz128(32 + li, 4 + lq));
-    const bf16x4 d3 = ld4(buf, kBufAN + swz128(48 + li, 4 + lq) + 8);
-    const bf16x4 a10 = ld4(buf, kBufAN + swz128(16 + li, lq));
-    const bf16x8 a2x = ld8(buf, kBufAN + swz128(32 + li, lq));
-    const bf16x8 a3x = ld8(buf, kBufAN + swz128(48 + li, lq));
-    const bf16x4 a32 = ld4(buf, kBufAN + swz128(48 + li, 4 + lq));
+    const char* an = buf + kBufPA;
+    const bf16x4 d0 = ld4(an, pa_off(1, li, lq));
+    const bf16x4 d1 = ld4(an, pa_off(1, 16 + li, lq) + 8);
+    const bf16x4 d2 = ld4(an, pa_off(1, 32 + li, 4 + lq));
+    const bf16x4 d3 = ld4(an, pa_off(1, 48 + li, 4 + lq) + 8);
+    const bf16x4 a10 = ld4(an, pa_off(1, 16 + li, lq));
+    const bf16x8 a2x = ld8(an, pa_off(1, 32 + li, lq));
+    const bf16x8 a3x = ld8(an, pa_off(1, 48 + li, lq));
+    const bf16x4 a32 = ld4(an, pa_off(1, 48 + li, 4 + lq));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 R[4];
 #pragma unroll
@@ -377,10 +399,10 @@ __device__ __forceinline__ void state_products(const char* buf, f32x4 S[8], cons
     }
 }
 
-// O = Gamma n_q (Q S0) + P Delta for this wave's 16 columns -> Os (bf16)
-template <int VLd>
-__device__ __forceinline__ void out_tile(const char* buf, __bf16* Os, const f32x4 QS[4], const bf16x8 BD[2],
-                                         int cw, int li, int lq) {
+// O = Gamma n_q (Q S0) + P Delta for this wave's 16 columns (fp32 registers,
+// rows 16m + 4lq + e)
+__device__ __forceinline__ void out_tile(const char* buf, const f32x4 QS[4], const bf16x8 BD[2], f32x4 O[4], int li,
+                                         int lq) {
     f32x4 so[4];
     bf16x8 pa[6];
 #pragma unroll
@@ -388,7 +410,7 @@ __device__ __forceinline__ void out_tile(const char* buf, __bf16* Os, const f32x
         so[m] = ldf4(buf, kBufTok + 4 * (2 * kC + 16 * m + 4 * lq));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            if (ks == 0 || m >= 2) pa[i++] = ld8(buf, kBufP + swz128(16 * m + li, 4 * ks + lq));
+            if (ks == 0 || m >= 2) pa[i++] = ld8(buf + kBufPA, pa_off(0, 16 * m + li, 4 * ks + lq));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -397,9 +419,30 @@ __device__ __forceinline__ void out_tile(const char* buf, __bf16* Os, const f32x
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
+        O[m] = acc;
     }
+}
+
+// O (bf16) -> the chunk's Q region as [64][N] rows.  Lanes 2i and 2i + 1
+// (adjacent columns) swap values so that each writes two columns of two of
+// its four rows as one 4-byte word.
+template <int N>
+__device__ __forceinline__ void stage_out(char* buf, const f32x4 O[4], int cw, int li, int lq) {
+    const bool odd = li & 1;
+    uint32_t* os = reinterpret_cast<uint32_t*>(buf + kBufQ) + (cw >> 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const float mine = odd ? O[m][2 + e2] : O[m][e2];
+            const float give = odd ? O[m][e2] : O[m][2 + e2];
+            const float got = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(give), 0xB1, 0xF, 0xF, false));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 pr = __builtin_convertvector(
+                (f32x4{odd ? got : mine, odd ? mine : got, 0.f, 0.f}).xy, bf16x2);
+            const int row = 16 * m + 4 * lq + (odd ? 2 + e2 : e2);
+            os[row * (N / 2)] = __builtin_bit_cast(uint32_t, pr);
+        }
 }
 
 struct StateCtx {
@@ -416,30 +459,98 @@ __device__ __forceinline__ int64_t state_channel(const PrefillParams& p, const S
     return 2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + (ch - 2 * kD);
 }
 
-// O rows of chunk kc (staged in Os) -> HBM, 16-byte stores, spread over
-// `nthr` threads starting at thread `t0`
+// Layout and memory-wave roles of the state kernel with NW compute waves
+// (16 state columns each) and 8 - NW memory waves.  Wave w runs on SIMD
+// w % 4.
+//   K waves (m 0, 1)   K rows 0..31 / 32..63, wait, K^T granules 0..3 / 4..7
+//   V waves            the slice's v front end, one 4-channel x 4-row item
+//                      per lane (NW = 4: every memory wave; NW = 2: waves 6, 7,
+//                      on the SIMDs without a compute wave)
+//   copy waves         the other record pieces and the raw slab, round robin
+//   every memory wave  first stores its O pieces of the previous chunk from
+//                      the Q region it is about to refill, then refills
+//                      those Q pieces itself
 template <int NW>
-__device__ __forceinline__ void store_rows(const PrefillParams& p, const StateCtx& cx, const __bf16* Os, int64_t kc,
-                                           int t0, int nthr) {
-    constexpr int N = 16 * NW, VLd = N + 8, V8 = N / 8;
-    const int64_t local0 = kc * kC - p.start_pos;
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-    for (int e = t0; e < kC * V8; e += nthr) {
-        const int tau = e / V8, c8 = e % V8;
-        const int64_t t = local0 + tau;
-        if (t >= 0 && t < p.seq_len)
-            *reinterpret_cast<uint4*>(out + (((int64_t)cx.b * p.seq_len + t) * p.num_v_heads + cx.h) * kD + cx.zcol0 + 8 * c8) =
-                *reinterpret_cast<const uint4*>(&Os[tau * VLd + 8 * c8]);
+struct StateShape {
+    static constexpr int NM = 8 - NW;
+    static constexpr int N = 16 * NW;                        // state columns per workgroup
+    static constexpr int SPLIT = kD / N;
+    static constexpr int BUF = kBufVt + N * kVtLd * 2;
+    static constexpr int SLAB_ROW = N * 2;                   // raw v slab: [67 rows][N channels] bf16
+    static constexpr int SLAB = (kC + 3) * SLAB_ROW;
+    static constexpr int SLAB_PIECES = (SLAB + 1023) / 1024;
+    static constexpr int O_PIECES = kC * N * 2 / 1024;       // O staged in Q pieces 0 .. O_PIECES - 1
+    static constexpr int NV = NW == 4 ? 4 : 2;               // V waves
+    static constexpr int OTHER = (16 - O_PIECES) + 12 + 2 + SLAB_PIECES;
+    static constexpr int NCOPY = NW == 4 ? 4 : 4;            // copy waves: NW = 4: m 0..3; NW = 2: m 2..5
+    __device__ static bool is_v(int m) { return NW == 4 || m >= 4; }
+    __device__ static int v_part(int m) { return NW == 4 ? m : m - 4; }
+    __device__ static int copy_index(int m) { return NW == 4 ? m : m - 2; }   // < 0: not a copy wave
+};
+
+// Copy piece pc of a chunk's raw v slab (first row at call-local token
+// local0 - 3) into `slab`
+template <int NW>
+__device__ __forceinline__ void issue_slab(const PrefillParams& p, const StateCtx& cx, char* slab, int64_t local0,
+                                           int pc, int lane) {
+    using SS = StateShape<NW>;
+    const int o = pc * 1024 + 16 * lane;
+    if (o < SS::SLAB) {
+        const int row = o / SS::SLAB_ROW, g = (o % SS::SLAB_ROW) / 16;
+        const int64_t t = min(max(local0 - 3 + row, (int64_t)0), p.seq_len - 1);
+        const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + ((int64_t)cx.b * p.seq_len + t) * p.conv_dim +
+                              2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + 8 * g;
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(slab + pc * 1024), 16, 0, 0);
     }
 }
 
+// Front end of part `part` of the slice's v channels for one chunk from its
+// raw slab -> V^T in the chunk's buffer.  Items of 4 channels x 4 rows, one
+// per lane: N / 4 channel groups x 16 row groups, 64 items per part.
+template <int NW, bool INTERIOR>
+__device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& cx, const float* Wv, const char* slab,
+                                        char* buf, int64_t local0, int part, int lane) {
+    using SS = StateShape<NW>;
+    constexpr int CG = SS::N / 4;
+    const int item = 64 * part + lane;
+    const int c0 = (item % CG) * 4, tau0 = (item / CG) * 4;
+    const int64_t gc = 2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + c0;
+    uint2 raw[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) raw[k] = *reinterpret_cast<const uint2*>(slab + (tau0 + k) * SS::SLAB_ROW + 2 * c0);
+    float w[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[t][i] = Wv[t * SS::N + c0 + i];
+    bf16x4 ub[4];
+    conv_compute<INTERIOR, 4>(p, cx.b, gc, local0, tau0, w, raw, ub);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<bf16x4*>(buf + kBufVt + ((c0 + i) * kVtLd + tau0) * 2) = bf16x4{ub[0][i], ub[1][i], ub[2][i], ub[3][i]};
+}
+
+// O piece o of chunk kc (staged in buf's Q region) -> HBM: 16 bytes per lane
+template <int NW>
+__device__ __forceinline__ void store_out_piece(const PrefillParams& p, const StateCtx& cx, const char* buf,
+                                                int64_t kc, int o, int lane) {
+    using SS = StateShape<NW>;
+    const int off = o * 1024 + 16 * lane;
+    const int row = off / (SS::N * 2), c8 = (off % (SS::N * 2)) / 16;
+    const uint4 v = *reinterpret_cast<const uint4*>(buf + kBufQ + off);
+    const int64_t t = kc * kC - p.start_pos + row;
+    if (t >= 0 && t < p.seq_len)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) +
+                                  (((int64_t)cx.b * p.seq_len + t) * p.num_v_heads + cx.h) * kD + cx.zcol0 + 8 * c8) = v;
+}
+
 // Checkpoint slot when the end of chunk kc is a multiple of the checkpoint
-// interval: this wave's state slice and (with the compute threads) the conv
-// tails of the workgroup's channels
+// interval: this compute wave's state slice and (over the compute threads)
+// the conv tails of the workgroup's channels
 template <int NW>
 __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCtx& cx, const f32x4 S[8], int64_t kc,
                                            int tid) {
-    constexpr int NT = 64 * NW, N = 16 * NW, NCH = 2 * kD + N;
+    constexpr int NT = 64 * NW, NCH = 2 * kD + 16 * NW;
     const int lq = (tid % 64) / 16;
     const int64_t pe = (kc + 1) * kC;
     if (p.ckpt_interval > 0 && pe % p.ckpt_interval == 0 && pe <= p.start_pos + p.seq_len) {
@@ -455,64 +566,68 @@ __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCt
     }
 }
 
-// Memory waves per state workgroup: eight waves in all
-template <int NW> constexpr int kMemWaves = 8 - NW;
-
-// One chunk of the state kernel.  Compute waves (0..NW-1): prefetch the next
-// chunk's V rows, the state-dependent products, O -> Os[j % 2]; after the
-// barrier the checkpoint.  Memory waves (NW..7): copy the next chunk's
-// records into the other buffer, store the previous chunk's O rows, wait for
-// the copies.  Every wave passes the same barrier outside the role branches.
+// Memory wave m's share of one chunk: store the O pieces of chunk jn - 2
+// (staged in buf's Q region) and refill buf with chunk jn: records, raw slab
+// of chunk jn + 1 into slab_next, v front end from `slab`, K^T.
 template <int NW>
-__device__ __forceinline__ void state_step(const SplitParams& sp, const StateCtx& cx, const char* cur, char* nxt,
-                                           __bf16* Os, const __bf16* Os_prev, f32x4 S[8], bf16x4 vv[4], int j,
-                                           int wave, int tid) {
-    constexpr int VLd = 16 * NW + 8, NM = kMemWaves<NW>;
-    const int lane = tid % 64, li = lane % 16, lq = lane / 16;
-    const bool mem = wave >= NW;
-    const bool more = j + 1 < sp.nseg;
-    bf16x4 vn[4];
-    if (mem) {
-        if (more) issue_chunk<NM>(nxt, key_rec(sp, cx.b, cx.kh, j + 1), val_rec(sp, cx.b, cx.h, j + 1), wave - NW, lane);
-        if (j > 0) store_rows<NW>(sp.p, cx, Os_prev, sp.k0 + j - 1, tid - 64 * NW, 64 * NM);
-    } else {
-        f32x4 QS[4];
-        bf16x8 BD[2];
-        if (more) load_v(val_rec(sp, cx.b, cx.h, j + 1), cx.zcol0 + 16 * wave + li, lq, vn);
-        state_products(cur, S, vv, QS, BD, li, lq);
-        out_tile<VLd>(cur, Os, QS, BD, 16 * wave + li, li, lq);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (!mem) {
-        if (more) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) vv[m] = vn[m];
+__device__ __forceinline__ void mem_chunk(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf,
+                                          const char* slab, char* slab_next, int jn, bool store_prev, int m, int lane) {
+    using SS = StateShape<NW>;
+    const bool fill = jn < sp.nseg;
+    // O pieces of the chunk that last used this buffer, then the same Q pieces
+    if (store_prev)
+        for (int o = m; o < SS::O_PIECES; o += SS::NM) store_out_piece<NW>(sp.p, cx, buf, sp.k0 + jn - 2, o, lane);
+    if (!fill) return;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the O rows are in registers before the buffer is refilled
+    const char* krec = key_rec(sp, cx.b, cx.kh, jn);
+    const char* vrec = val_rec(sp, cx.b, cx.h, jn);
+    for (int o = m; o < SS::O_PIECES; o += SS::NM) issue_piece(buf, krec, vrec, o, lane);
+    if (m < 2)
+        for (int pc = kPiecesK + 8 * m; pc < kPiecesK + 8 * m + 8; ++pc) issue_piece(buf, krec, vrec, pc, lane);
+    const int ci = SS::copy_index(m);
+    if (ci >= 0) {
+        for (int i = ci; i < SS::OTHER; i += SS::NCOPY) {
+            // other pieces: Q pieces O_PIECES..15, P | AN, scale rows, then the next slab
+            if (i < 16 - SS::O_PIECES) issue_piece(buf, krec, vrec, SS::O_PIECES + i, lane);
+            else if (i < 16 - SS::O_PIECES + 14) issue_piece(buf, krec, vrec, kPiecesPA + (i - (16 - SS::O_PIECES)), lane);
+            else if (jn + 1 < sp.nseg)
+                issue_slab<NW>(sp.p, cx, slab_next, (sp.k0 + jn + 1) * kC - sp.p.start_pos, i - (30 - SS::O_PIECES), lane);
         }
-        checkpoint<NW>(sp.p, cx, S, sp.k0 + j, tid);
+    }
+    if (SS::is_v(m)) {
+        const int64_t local0 = (sp.k0 + jn) * kC - sp.p.start_pos;
+        if (local0 >= 3 && local0 + kC <= sp.p.seq_len) v_front<NW, true>(sp.p, cx, Wv, slab, buf, local0, SS::v_part(m), lane);
+        else v_front<NW, false>(sp.p, cx, Wv, slab, buf, local0, SS::v_part(m), lane);
+    }
+    if (m < 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        transpose_k(buf, 4 * m, lane);
     }
 }
 
-// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.
+// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  Per chunk
+// two barriers: E (the chunk's products are done and the next chunk's buffer
+// is filled) and B (the chunk's O rows are staged in its Q region).
 template <int NW>
 __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
-    static_assert(NW == 2 || NW == 4, "two or four compute waves");
-    constexpr int NTALL = 512, N = 16 * NW, VLd = N + 8, NCH = 2 * kD + N, NM = kMemWaves<NW>;
-    constexpr int S_SPLIT = kD / N;
+    using SS = StateShape<NW>;
+    constexpr int N = SS::N, NCH = 2 * kD + N;
     const PrefillParams& p = sp.p;
-    __shared__ __attribute__((aligned(16))) char buf0[kBufBytes];
-    __shared__ __attribute__((aligned(16))) char buf1[kBufBytes];
-    __shared__ __attribute__((aligned(16))) __bf16 Os[2][kC * VLd];   // output staging, per chunk parity
+    __shared__ __attribute__((aligned(16))) char buf0[SS::BUF];
+    __shared__ __attribute__((aligned(16))) char buf1[SS::BUF];
+    __shared__ __attribute__((aligned(16))) char slab0[SS::SLAB];   // raw v slabs, per chunk parity
+    __shared__ __attribute__((aligned(16))) char slab1[SS::SLAB];
+    __shared__ float Wv[4 * N];                                     // conv taps of the slice's v channels
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: role branches stay scalar
     const int li = lane % 16, lq = lane / 16;
-    const bool mem = wave >= NW;
-    // workgroup -> (b, key head, member); the r * S_SPLIT members of one
+    const bool compute = wave < NW;
+    // workgroup -> (b, key head, member); the r * SPLIT members of one
     // (b, key head) share a blockIdx % 8, so the round-robin dispatch puts
     // them on one XCD and its L2, where their common key records stay
     const int r = p.num_v_heads / p.num_k_heads;
-    const int M = r * S_SPLIT;
+    const int M = r * SS::SPLIT;
     const int NG = p.batch * p.num_k_heads;
     const int bid = blockIdx.x;
     const int grp = (bid / 8 / M) * 8 + bid % 8;
@@ -521,41 +636,88 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
     StateCtx cx;
     cx.b = grp / p.num_k_heads;
     cx.kh = grp % p.num_k_heads;
-    cx.h = cx.kh * r + member / S_SPLIT;
-    cx.zcol0 = (member % S_SPLIT) * N;
+    cx.h = cx.kh * r + member / SS::SPLIT;
+    cx.zcol0 = (member % SS::SPLIT) * N;
     cx.owns_qk_tail = member == 0;
-    cx.s_base = ((int64_t)cx.b * p.num_v_heads + cx.h) * kD * kD + cx.zcol0 + 16 * (mem ? 0 : wave) + li;
+    cx.s_base = ((int64_t)cx.b * p.num_v_heads + cx.h) * kD * kD + cx.zcol0 + 16 * (compute ? wave : 0) + li;
 
-    const float* s_src = sp.first_seg ? p.rec_in : p.rec_out;
-    f32x4 S[8];
-    bf16x4 vv[4];
-    if (!mem) {
+    for (int e = tid; e < 4 * N; e += 512) {
+        const int t = e / N, c = e % N;
+        const int64_t gc = 2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + c;
+        Wv[e] = bf16_bits_to_f32(static_cast<const uint16_t*>(p.conv_w)[gc * 4 + t]);
+    }
+    __syncthreads();
+
+    // The two roles run separate loops with the same barriers (two in the
+    // prologue, two per chunk), so their registers do not add up.
+    if (compute) {
+        const float* s_src = sp.first_seg ? p.rec_in : p.rec_out;
+        f32x4 S[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[t][e] = s_src ? s_src[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] : 0.f;
-        if (sp.nseg > 0) load_v(val_rec(sp, cx.b, cx.h, 0), cx.zcol0 + 16 * wave + li, lq, vv);
-    } else if (sp.nseg > 0) {
-        issue_chunk<NM>(buf0, key_rec(sp, cx.b, cx.kh, 0), val_rec(sp, cx.b, cx.h, 0), wave - NW, lane);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // two chunks per trip so that each LDS buffer is a distinct object: the
-    // compiler then orders reads of one buffer only after its own copies
-    for (int j = 0; j < sp.nseg; j += 2) {
-        state_step<NW>(sp, cx, buf0, buf1, Os[0], Os[1], S, vv, j, wave, tid);
-        if (j + 1 < sp.nseg) state_step<NW>(sp, cx, buf1, buf0, Os[1], Os[0], S, vv, j + 1, wave, tid);
-    }
-    if (mem && sp.nseg > 0) store_rows<NW>(p, cx, Os[(sp.nseg - 1) & 1], sp.k0 + sp.nseg - 1, tid - 64 * NW, 64 * NM);
-
-    if (!mem) {
+        __syncthreads();
+        __syncthreads();
+        const int cw = 16 * wave + li;
+        for (int j = 0; j < sp.nseg; ++j) {
+            char* cur = (j & 1) ? buf1 : buf0;
+            bf16x4 vv[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                vv[mb] = *reinterpret_cast<const bf16x4*>(cur + kBufVt + (cw * kVtLd + 16 * mb + 4 * lq) * 2);
+            f32x4 QS[4], O[4];
+            bf16x8 BD[2];
+            state_products(cur, S, vv, QS, BD, li, lq);
+            out_tile(cur, QS, BD, O, li, lq);
+            // finish O before E (the compiler would otherwise sink it past
+            // the barrier, where the memory waves wait for it)
+            asm volatile("" ::"v"(O[0]), "v"(O[1]), "v"(O[2]), "v"(O[3]));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();   // E
+            stage_out<N>(cur, O, cw, li, lq);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();   // B
+            checkpoint<NW>(p, cx, S, sp.k0 + j, tid);
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) p.rec_out[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+    } else {
+        const int m = wave - NW;
+        // raw slab of chunk 0, then chunk 0 into buf0 (and chunk 1's slab)
+        if (sp.nseg > 0)
+            for (int pc = m; pc < SS::SLAB_PIECES; pc += SS::NM) issue_slab<NW>(p, cx, slab0, sp.k0 * kC - p.start_pos, pc, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        mem_chunk<NW>(sp, cx, Wv, buf0, slab0, slab1, 0, false, m, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // Step j: store O of chunk j - 1 from the other buffer and refill it
+        // with chunk j + 1.  Two chunks per trip so that each LDS buffer is a
+        // distinct object: the compiler then orders reads of one buffer only
+        // after its own copies.  Chunk c's slab lives in slab[c % 2].
+        for (int j = 0; j < sp.nseg; j += 2) {
+            mem_chunk<NW>(sp, cx, Wv, buf1, slab1, slab0, j + 1, j >= 1, m, lane);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();   // E
+            __syncthreads();   // B
+            if (j + 1 < sp.nseg) {
+                mem_chunk<NW>(sp, cx, Wv, buf0, slab0, slab1, j + 2, true, m, lane);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();   // E
+                __syncthreads();   // B
+            }
+        }
+        // O of the last chunk
+        if (sp.nseg > 0) {
+            const char* last = ((sp.nseg - 1) & 1) ? buf1 : buf0;
+            for (int o = m; o < SS::O_PIECES; o += SS::NM) store_out_piece<NW>(p, cx, last, sp.k0 + sp.nseg - 1, o, lane);
+        }
     }
     if (sp.last_seg) {
-        for (int ch = tid; ch < NCH; ch += NTALL)
+        for (int ch = tid; ch < NCH; ch += 512)
             if (ch >= 2 * kD || cx.owns_qk_tail)
                 write_tail(p, cx.b, p.seq_len, state_channel(p, cx, ch), static_cast<uint16_t*>(p.conv_out));
     }
@@ -563,19 +725,18 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
 
 template <int NW>
 hipError_t launch_state(const SplitParams& sp, hipStream_t stream) {
-    const int s_split = kD / (16 * NW);
     const int r = sp.p.num_v_heads / sp.p.num_k_heads;
     const int ng = sp.p.batch * sp.p.num_k_heads;
-    const int blocks = ((ng + 7) / 8) * 8 * r * s_split;
+    const int blocks = ((ng + 7) / 8) * 8 * r * StateShape<NW>::SPLIT;
     hipLaunchKernelGGL((state_kernel<NW>), dim3(blocks), dim3(512), 0, stream, sp);
     return hipGetLastError();
 }
 
-// Compute waves (16 state columns each) per state workgroup.  One workgroup
-// fits a CU (two 65 KiB LDS buffers), and a CU streams the records at a
-// bounded rate, so with few (sequence, head) pairs the narrower workgroups
-// spread the chains over more CUs.  GDN_PREFILL_STATE_WAVES (2 or 4)
-// overrides the choice.
+// Compute waves per state workgroup (16 state columns each).  A workgroup
+// streams its chunk records at a bounded rate per CU, so with few
+// (sequence, head) pairs the narrower workgroups spread the chains over more
+// CUs; with many, the wider ones do more work per byte moved.
+// GDN_PREFILL_STATE_WAVES (2 or 4) overrides the choice.
 int state_waves(const PrefillParams& p) {
     if (const char* env = getenv("GDN_PREFILL_STATE_WAVES")) {
         const int v = atoi(env);
@@ -583,6 +744,10 @@ int state_waves(const PrefillParams& p) {
     }
     const int64_t heads = (int64_t)p.batch * p.num_v_heads;
     return heads * 4 <= 256 ? 2 : 4;
+}
+
+hipError_t launch_state_any(const SplitParams& sp, hipStream_t stream) {
+    return state_waves(sp.p) == 4 ? launch_state<4>(sp, stream) : launch_state<2>(sp, stream);
 }
 
 }  // namespace
@@ -605,7 +770,6 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
     int64_t max_seg = (int64_t)(ws_bytes / per);
     const int64_t grid_cap = ((int64_t)1 << 30) / ((int64_t)p.batch * p.num_k_heads);
     if (max_seg > grid_cap) max_seg = grid_cap;
-    const int nw = state_waves(p);
     SplitParams sp{};
     sp.p = p;
     sp.ws = static_cast<char*>(ws);
@@ -614,7 +778,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         sp.k0 = k_first;
         sp.nseg = 0;
         sp.last_seg = 1;
-        return nw == 4 ? launch_state<4>(sp, stream) : launch_state<2>(sp, stream);
+        return launch_state_any(sp, stream);
     }
     for (int64_t k0 = k_first; k0 < k_end; k0 += max_seg) {
         const int64_t n = k_end - k0 < max_seg ? k_end - k0 : max_seg;
@@ -624,7 +788,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(p.batch * p.num_k_heads * n)), dim3(kPrepThreads), 0, stream, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = nw == 4 ? launch_state<4>(sp, stream) : launch_state<2>(sp, stream);
+        e = launch_state_any(sp, stream);
         if (e != hipSuccess) return e;
         sp.first_seg = 0;
     }

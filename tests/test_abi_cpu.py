@@ -88,15 +88,15 @@ def test_checkpoint_plan_errors(G):
 
 def test_workspace_bytes(G):
     """B x (chunks a call of L tokens can span, from any start) x per-chunk
-    records (H_k x (Q, K, K^T) + H_v x (P, AN, row scales, V^T))."""
+    records (H_k x (Q, K) + H_v x (P, AN, row scales))."""
     for B, Hk, Hv in ((1, 16, 48), (8, 16, 32), (2, 2, 6)):
-        per = B * (Hk * 3 * 64 * 128 * 2 + Hv * (2 * 64 * 64 * 2 + 5 * 64 * 4 + 128 * 64 * 2))
+        per = B * (Hk * 2 * 64 * 128 * 2 + Hv * (2 * 64 * 64 * 2 + 5 * 64 * 4))
         c = cfg(G, batch=B, num_k_heads=Hk, num_v_heads=Hv)
         for L in (0, 1, 2, 63, 64, 65, 127, 128, 16384):
             # brute force over the start offset inside a chunk
             span = max((((s + L - 1) // 64) - s // 64 + 1) if L else 0 for s in range(64))
             assert G.prefill_workspace_bytes(c, L) == span * per, (B, Hk, Hv, L)
-    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 49152 + 48 * 34048)
+    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 17664)
 
 
 FAKE = 1 << 34  # aligned, far-apart addresses that are never dereferenced: every call below fails validation

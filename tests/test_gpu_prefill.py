@@ -61,6 +61,10 @@ def gpu_prefill(G, w, d, seq=slice(None), start_pos=0, conv_in="init", rec_in="i
     whole call in one segment)."""
     c = cfg_of(G, w)
     ws = None if path == "fused" else workspace
+    # a workspace enables the two-pass path; force it where the size-based
+    # choice would take the fused kernel
+    old_env = os.environ.get("GDN_PREFILL_PATH")
+    os.environ["GDN_PREFILL_PATH"] = "split" if path == "split" else "auto"
     cin = d["conv_state"] if conv_in == "init" else conv_in
     rin = d["rec_state"] if rec_in == "init" else rec_in
     out, conv, S = G.prefill_chunked(c, d["qkv"][:, seq].contiguous(), d["a"][:, seq].contiguous(),
@@ -68,6 +72,10 @@ def gpu_prefill(G, w, d, seq=slice(None), start_pos=0, conv_in="init", rec_in="i
                                      d["dt_bias"], cin, rin, start_pos=start_pos,
                                      ckpt_interval=ckpt_interval, ckpt_buf=ckpt_buf,
                                      rec_state_out=rec_out, workspace=ws)
+    if old_env is None:
+        os.environ.pop("GDN_PREFILL_PATH", None)
+    else:
+        os.environ["GDN_PREFILL_PATH"] = old_env
     torch.cuda.synchronize()
     return out, conv, S
 
