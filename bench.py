@@ -4,7 +4,9 @@
 One step = one chunked-prefill call (front end + chunked rule + final state)
 over the Qwen3.6-27B-shaped layer: B=1, L=16384 tokens, 16 key / 48 value
 heads, head dims 128, chunk 64, bf16 io, fp32 state, synthetic seeded inputs
-resident in HBM.  ``value`` is prefill tokens/s.  The same run also times the
+resident in HBM, with a workspace allocated once before timing (the call then
+runs the two-pass path: chunk-prep kernel + state kernel).  ``value`` is
+prefill tokens/s; the fused single-pass kernel is timed beside it.  The same run also times the
 one-token decode step of the Qwen3.6-27B-shaped decode workload (B=32, 256
 consecutive steps, state ~N(0, 0.05)) and reports its HBM bandwidth, and
 times the fp64 CPU oracle on a bounded sample of the prefill workload.
@@ -49,10 +51,11 @@ def decode_bytes(B, Hk, Hv, d=128) -> int:
             + 2 * B * Hv * 2 + conv_dim * 4 * 2 + 2 * Hv * 4)
 
 
-def profiled_traffic(profile: str, source: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None
-    when the kernel's sources changed after the counters were taken."""
+def profiled_traffic(profile: str, sources):
+    """HBM bytes per call from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE of every kernel the call launches, scaled by a
+    copy-kernel calibration), or None when a kernel source changed after the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
@@ -64,11 +67,16 @@ def profiled_traffic(profile: str, source: str):
             fields[k.strip()] = v.strip()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_causal_amd", "csrc")
     h = hashlib.sha256()
-    for f in (source, "gdn_common.h", "gdn_launch.h"):
+    for f in list(sources) + ["gdn_common.h", "gdn_launch.h"]:
         h.update(open(os.path.join(csrc, f), "rb").read())
     if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+PREFILL_SOURCES = ("gdn_prefill_split.hip", "gdn_chunk_common.h", "gdn_api.hip")
+FUSED_SOURCES = ("gdn_prefill.hip", "gdn_chunk_common.h")
+DECODE_SOURCES = ("gdn_decode.hip",)
 
 
 def time_events(fn, steps, warmup):
@@ -87,6 +95,10 @@ def time_events(fn, steps, warmup):
 
 
 def bench_prefill(args):
+    """The prefill call as a user makes it for this shape: with a workspace
+    (allocated once, outside the timed region), which selects the two-pass
+    path for B * H_v <= 128.  The fused single-pass kernel (no workspace) is
+    timed beside it for reference."""
     import torch
     from linear_attention_recurrence_causal_amd import gdn, inputs as I
     w = I.WORKLOADS[2]
@@ -96,17 +108,20 @@ def bench_prefill(args):
     out = torch.empty(w.batch, w.seq_len, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
     conv = torch.empty(w.batch, w.conv_dim, 3, dtype=torch.bfloat16, device="cuda")
     S = torch.empty(w.batch, w.num_v_heads, 128, 128, device="cuda")
+    ws = torch.empty(gdn.prefill_workspace_bytes(cfg, w.seq_len), dtype=torch.uint8, device="cuda")
 
-    def step():
+    def step(workspace):
         gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"],
-                            None, None, out=out, conv_state_out=conv, rec_state_out=S)
+                            None, None, out=out, conv_state_out=conv, rec_state_out=S,
+                            workspace=workspace)
 
     torch.cuda.synchronize()
-    t = time_events(step, args.steps, args.warmup)
+    t = time_events(lambda: step(ws), args.steps, args.warmup)
+    t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
     tokens = w.batch * w.seq_len
     flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
     byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads)
-    return w, t, tokens, flops, byts, inp
+    return w, t, t_fused, tokens, flops, byts, inp, ws.numel()
 
 
 def bench_decode(args):
@@ -176,7 +191,7 @@ def main():
     torch.cuda.set_device(0)
 
     print("bench: prefill", file=sys.stderr, flush=True)
-    w, t, tokens, flops, byts, inp = bench_prefill(args)
+    w, t, t_fused, tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
     achieved = flops / t
     rec = {
         "metric": METRIC,
@@ -195,13 +210,20 @@ def main():
                    "seq_len": w.seq_len, "num_k_heads": w.num_k_heads,
                    "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk": 64,
                    "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": achieved / 1e12,
+        "roofline": {"kernel": "two-pass prefill: prep_kernel + state_kernel<2> (one call)",
+                     "bound": "mfma", "achieved": achieved / 1e12,
                      "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_FLOPS,
-                     "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
-                                                 "gdn_prefill.hip"),
+                     "traffic": profiled_traffic("prefill_two_pass_qwen36-27b_prefill_16k.md",
+                                                 PREFILL_SOURCES),
                      "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
-                     "hbm_floor_frac": byts / t / HBM_PEAK_BYTES},
+                     "hbm_floor_frac": byts / t / HBM_PEAK_BYTES,
+                     "workspace_bytes": ws_bytes},
+        "fused_path": {"kernel": "prefill_kernel<8>", "ms_per_call": t_fused * 1e3,
+                       "tokens_per_s": tokens / t_fused,
+                       "frac": flops / t_fused / BF16_PEAK_FLOPS,
+                       "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
+                                                   FUSED_SOURCES)},
     }
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
@@ -213,7 +235,7 @@ def main():
                          "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
                          "frac": bd / td / HBM_PEAK_BYTES,
                          "traffic": profiled_traffic("decode_step_kernel_qwen36-27b_decode_b32.md",
-                                                     "gdn_decode.hip")},
+                                                     DECODE_SOURCES)},
         }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
