@@ -327,8 +327,11 @@ __device__ __forceinline__ void diag_solve(SM& sm, int lane) {
 // exactly; only the coupling terms see bf16 operands.  d[m] are this lane's
 // A-operand slots of N_mm; a10, a2x, a3x, a32 those of -A_10, -[A_20 A_21],
 // -[A_30 A_31], -A_32.
+// hook(s), s = 0..7, runs right after the MFMAs of step s (two per block), so
+// a caller can put independent work into the latency of this dependent chain.
+template <class Hook>
 __device__ __forceinline__ void delta_substitution(const f32x4 R[4], const bf16x4 d[4], bf16x4 a10, bf16x8 a2x,
-                                                   bf16x8 a3x, bf16x4 a32, f32x4 Dl[4], bf16x4 Db[4]) {
+                                                   bf16x8 a3x, bf16x4 a32, f32x4 Dl[4], bf16x4 Db[4], Hook&& hook) {
     const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -339,10 +342,17 @@ __device__ __forceinline__ void delta_substitution(const f32x4 R[4], const bf16x
             y = mfma16(a3x, cat4(Db[0], Db[1]), y);
             y = mfma16(cat4(a32, z4), cat4(Db[2], z4), y);
         }
+        hook(2 * m);
         const bf16x4 yb = __builtin_convertvector(y, bf16x4);
         Dl[m] = mfma16(cat4(d[m], z4), cat4(yb, z4), y);
+        hook(2 * m + 1);
         Db[m] = __builtin_convertvector(Dl[m], bf16x4);
     }
+}
+
+__device__ __forceinline__ void delta_substitution(const f32x4 R[4], const bf16x4 d[4], bf16x4 a10, bf16x8 a2x,
+                                                   bf16x8 a3x, bf16x4 a32, f32x4 Dl[4], bf16x4 Db[4]) {
+    delta_substitution(R, d, a10, a2x, a3x, a32, Dl, Db, [](int) {});
 }
 
 // Delta' = exp(gamma_C - gamma) n_k Delta as bf16 hi + lo B operands of the

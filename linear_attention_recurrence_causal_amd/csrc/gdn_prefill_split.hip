@@ -15,13 +15,13 @@
 //   state (one workgroup per sequence, value head and slice of 16 * NW
 //         state columns, NW = 2 or 4; chunks in order): NW compute waves do
 //         only the state-dependent products of each chunk -- K S0, Q S0, R,
-//         Delta by blocked forward substitution, the state update, O --
-//         while 8 - NW memory waves store the previous chunk's O rows and
-//         prepare the next chunk in the other LDS buffer: its records by
-//         global_load_lds, K^T by an LDS transpose of K, and the front end of
-//         the slice's v channels (conv + SiLU from a raw slab copied one chunk
-//         earlier; the slice's own columns, so no value-head data goes
-//         through the workspace).
+//         Delta by blocked forward substitution, the state update, O, which
+//         they store straight from registers -- while 8 - NW memory waves
+//         fill the other LDS buffer with the next chunk: its records by
+//         global_load_lds and the front end of the slice's v channels (conv +
+//         SiLU from a raw slab copied one chunk earlier; the slice's own
+//         columns, so no value-head data goes through the workspace).  K^T
+//         is read from K with the transposing LDS reads.
 //
 // A workspace smaller than the whole call is used segment by segment (prep
 // then state for each run of chunks that fits); the state travels between
@@ -72,11 +72,11 @@ __device__ __forceinline__ char* val_rec(const SplitParams& s, int b, int h, int
 }
 
 // Byte offset of 16-byte granule g of row `row` in the state kernel's LDS
-// copy of a 256-byte-row (Q, K) or 128-byte-row (K^T, P, AN) matrix: the
-// granule index is XORed with row % 8, so the eight rows read by one phase
-// of a ds_read_b128 hit eight different granule columns (no bank conflict).
-__device__ __forceinline__ int swz256(int row, int g) { return row * 256 + 16 * (g ^ (row & 7)); }
-__device__ __forceinline__ int swz128(int row, int g) { return row * 128 + 16 * (g ^ (row & 7)); }
+// copy of a 256-byte-row matrix (Q, K): the granule index is XORed with
+// row % 16, so the sixteen rows read by one phase of a ds_read_b128 hit
+// sixteen different granule columns, and so do the sixteen rows of one
+// transposing read of K (four lanes per row, granules 4u + 0..3).
+__device__ __forceinline__ int swz256(int row, int g) { return row * 256 + 16 * (g ^ (row & 15)); }
 
 __device__ __forceinline__ void copy16(char* dst, const void* src) {
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
@@ -238,11 +238,10 @@ __device__ __forceinline__ int pa_off(int mat, int row, int g) {
                                     : 2048 + (row - 32) * 128 + 16 * (g ^ (row & 7)));
 }
 
-// LDS buffer of one chunk: Q | K | K^T | P | AN | rows | V^T (V^T of the
-// slice's columns, row stride kVtLd).  Once the chunk's products are done,
-// its Q region stages the chunk's O rows ([64][slice] bf16).
+// LDS buffer of one chunk: Q | K | P | AN | rows | V^T (V^T of the slice's
+// columns, row stride kVtLd).  K^T is read from K by transposing LDS reads.
 constexpr int kVtLd = kC + 4;                       // bf16 row stride of V^T (conflict-free column reads)
-constexpr int kBufQ = 0, kBufK = kC * kD * 2, kBufKt = 2 * kC * kD * 2, kBufPA = 3 * kC * kD * 2,
+constexpr int kBufQ = 0, kBufK = kC * kD * 2, kBufPA = 2 * kC * kD * 2,
               kBufTok = kBufPA + 2 * kPaMat, kBufVt = kBufTok + kTokBytes;
 static_assert(kBufPA % 1024 == 0 && kBufTok % 1024 == 0 && kBufVt % 16 == 0, "piece and row alignment");
 
@@ -258,7 +257,7 @@ __device__ __forceinline__ void issue_piece(char* lds, const char* krec, const c
     if (pc < kPiecesPA) {
         const int o = (pc & 15) * 1024 + 16 * lane;   // offset inside Q or K
         const int row = o >> 8, s = (o >> 4) & 15;
-        src = krec + (pc < kPiecesK ? kRecQ : kRecK) + row * 256 + 16 * (s ^ (row & 7));
+        src = krec + (pc < kPiecesK ? kRecQ : kRecK) + swz256(row, s);
         dst = (pc < kPiecesK ? kBufQ : kBufK) + o;
     } else if (pc < kPiecesTok) {
         const int o = (pc - kPiecesPA) * 1024 + 16 * lane;
@@ -282,64 +281,48 @@ __device__ __forceinline__ void issue_piece(char* lds, const char* krec, const c
     if (act) __builtin_amdgcn_global_load_lds(src, LDS_PTR(lds + (dst & ~1023)), 16, 0, 0);
 }
 
-// K^T granules G in [g0, g0 + 4) of every row d from the chunk's K: granule G
-// of K^T row d holds tokens 32a + 4q + {0..3}, 32a + 16 + 4q + {0..3}
-// (a = G / 4, q = G % 4), which all lie in K rows 32a .. 32a + 31.
-__device__ __forceinline__ void transpose_k(char* buf, int g0, int lane) {
-    for (int e = lane; e < kD * 4; e += 64) {
-        const int d = e >> 2, G = g0 + (e & 3);
-        const int x0 = 32 * (G >> 2) + 4 * (G & 3);
-        const int pd = pos(d), gk = pd >> 3, ek = (pd & 7) * 2;
-        bf16x8 v;
+// A-operand fragment of K^T (rows d_k 16t..16t+15, reduction slots of token
+// block ks) straight from the row-major K by two ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane j reads d_k columns 16t + 4(j % 4) + 0..3 of token
+// row 32ks + 16h + 4q + j / 4 (q = lane group, h = half), and the read hands
+// lane i of the group column 16t + i of those four rows -- tokens
+// 32ks + 4q + 0..3 and 32ks + 16 + 4q + 0..3, the slot order of pos().
+// Four consecutive d_k columns sit in one half (8 bytes) of a granule:
+// granule 4(t / 2) + j % 4, half t % 2.
+__device__ __forceinline__ bf16x8 kt_frag(const char* buf, int t, int ks, int li, int lq) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    bf16x4 h[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = *reinterpret_cast<const __bf16*>(buf + kBufK + swz256(x0 + i, gk) + ek);
-            v[4 + i] = *reinterpret_cast<const __bf16*>(buf + kBufK + swz256(x0 + 16 + i, gk) + ek);
-        }
-        *reinterpret_cast<bf16x8*>(buf + kBufKt + swz128(d, G)) = v;
+    for (int hh = 0; hh < 2; ++hh) {
+        const int row = 32 * ks + 16 * hh + 4 * lq + li / 4;
+        const int off = kBufK + swz256(row, 4 * (t / 2) + li % 4) + 8 * (t % 2);
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + off));
     }
+    return cat4(h[0], h[1]);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const char* buf, int off) { return *reinterpret_cast<const bf16x8*>(buf + off); }
 __device__ __forceinline__ bf16x4 ld4(const char* buf, int off) { return *reinterpret_cast<const bf16x4*>(buf + off); }
 __device__ __forceinline__ f32x4 ldf4(const char* buf, int off) { return *reinterpret_cast<const f32x4*>(buf + off); }
 
-// State-dependent products of one chunk for this wave's 16 columns: K S0,
-// Q S0, R = beta V - beta Gamma n_k (K S0), Delta, the state update.
-// Returns Q S0 and Delta (bf16 B operands of P Delta).
-__device__ __forceinline__ void state_products(const char* buf, f32x4 S[8], const bf16x4 vv[4], f32x4 QS[4],
-                                               bf16x8 BD[2], int li, int lq) {
-    bf16x8 Bs[4];
+// One chunk for this wave's 16 state columns: K S0, R = beta V - beta
+// Gamma n_k (K S0), Delta by blocked substitution with (Q S0)^T in its
+// latency, O^T = (Q S0)^T diag(Gamma n_q) + (P Delta)^T, then the state update
+// S <- exp(gamma_C) S + K^T Delta' (Delta' as bf16 hi + lo).  O comes out
+// before the update, so its stores overlap the update.  Lane (i, q) of O
+// tile m holds token 16m + i, columns 4q..4q+3: a transposed tile comes from
+// the same operand registers with A and B swapped.  LDS operands are
+// requested in three batches, each well ahead of its use.
+__device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], const bf16x4 vv[4], f32x4 O[4], int li,
+                                               int lq) {
+    // batch 1: K fragments, the row scales of R (this lane's rows
+    // 16m + 4lq + e) and the substitution's A-operand slots (token block k
+    // of an AN row sits in granule 4 (k / 2) + lq, half k % 2)
+    bf16x8 ak[4][4], aq[4][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-    f32x4 KS[4];
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int mh = 0; mh < 4; mh += 2) {
-        bf16x8 ak[2][4], aq[2][4];
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int off = swz256(16 * (mh + mm) + li, 4 * ks + lq);
-                ak[mm][ks] = ld8(buf, kBufK + off);
-                aq[mm][ks] = ld8(buf, kBufQ + off);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            f32x4 k = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                k = mfma16(ak[mm][ks], Bs[ks], k);
-                q = mfma16(aq[mm][ks], Bs[ks], q);
-            }
-            KS[mh + mm] = k;
-            QS[mh + mm] = q;
-        }
-    }
-    // row scales for this lane's rows 16m + 4lq + e and the A-operand slots
-    // of the substitution (token block k of an AN row sits in granule
-    // 4 (k / 2) + lq, half k % 2)
+        for (int ks = 0; ks < 4; ++ks) ak[m][ks] = ld8(buf, kBufK + swz256(16 * m + li, 4 * ks + lq));
     f32x4 sb[4], sr[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -348,46 +331,78 @@ __device__ __forceinline__ void state_products(const char* buf, f32x4 S[8], cons
         sr[m] = ldf4(buf, kBufTok + 4 * (1 * kC + r0));
     }
     const char* an = buf + kBufPA;
-    const bf16x4 d0 = ld4(an, pa_off(1, li, lq));
-    const bf16x4 d1 = ld4(an, pa_off(1, 16 + li, lq) + 8);
-    const bf16x4 d2 = ld4(an, pa_off(1, 32 + li, 4 + lq));
-    const bf16x4 d3 = ld4(an, pa_off(1, 48 + li, 4 + lq) + 8);
+    const bf16x4 dg[4] = {ld4(an, pa_off(1, li, lq)), ld4(an, pa_off(1, 16 + li, lq) + 8),
+                          ld4(an, pa_off(1, 32 + li, 4 + lq)), ld4(an, pa_off(1, 48 + li, 4 + lq) + 8)};
     const bf16x4 a10 = ld4(an, pa_off(1, 16 + li, lq));
     const bf16x8 a2x = ld8(an, pa_off(1, 32 + li, lq));
     const bf16x8 a3x = ld8(an, pa_off(1, 48 + li, lq));
     const bf16x4 a32 = ld4(an, pa_off(1, 48 + li, 4 + lq));
+    bf16x8 Bs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 R[4];
 #pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 k = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) k = mfma16(ak[m][ks], Bs[ks], k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * k[e];
+    }
+    // batch 2: Q and P fragments
+#pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
-    f32x4 Dl[4];
-    bf16x4 Db[4];
-    const bf16x4 dg[4] = {d0, d1, d2, d3};
-    delta_substitution(R, dg, a10, a2x, a3x, a32, Dl, Db);
-    BD[0] = cat4(Db[0], Db[1]);
-    BD[1] = cat4(Db[2], Db[3]);
-    // S <- exp(gamma_C) S + K^T Delta'  (Delta' as bf16 hi + lo)
-    f32x4 su[4];
+        for (int ks = 0; ks < 4; ++ks) aq[m][ks] = ld8(buf, kBufQ + swz256(16 * m + li, 4 * ks + lq));
+    bf16x8 pa[6];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) su[m] = ldf4(buf, kBufTok + 4 * (3 * kC + 16 * m + 4 * lq));
+    for (int m = 0, i = 0; m < 4; ++m)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks == 0 || m >= 2) pa[i++] = ld8(buf + kBufPA, pa_off(0, 16 * m + li, 4 * ks + lq));
+    f32x4 Dl[4], QT[4];
+    bf16x4 Db[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) QT[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    delta_substitution(R, dg, a10, a2x, a3x, a32, Dl, Db, [&](int s) {
+        const int m = s / 2, k0 = 2 * (s % 2);
+        QT[m] = mfma16(Bs[k0], aq[m][k0], QT[m]);
+        QT[m] = mfma16(Bs[k0 + 1], aq[m][k0 + 1], QT[m]);
+    });
+    // batch 3: the scales of O and of the update, K^T fragments of the
+    // update (the second half once the first tiles are under way)
+    f32x4 su[4];
+    float so[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        su[m] = ldf4(buf, kBufTok + 4 * (3 * kC + 16 * m + 4 * lq));
+        so[m] = *reinterpret_cast<const float*>(buf + kBufTok + 4 * (2 * kC + 16 * m + li));
+    }
+    const float eC = *reinterpret_cast<const float*>(buf + kBufTok + 4 * 4 * kC);
     bf16x8 akt[8][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) akt[t][ks] = ld8(buf, kBufKt + swz128(16 * t + li, 4 * ks + lq));
-    const float eC = *reinterpret_cast<const float*>(buf + kBufTok + 4 * 4 * kC);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < 2; ++ks) akt[t][ks] = kt_frag(buf, t, ks, li, lq);
+    const bf16x8 BD[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
+#pragma unroll
+    for (int m = 0, i = 0; m < 4; ++m) {
+        f32x4 acc = QT[m] * so[m];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks == 0 || m >= 2) acc = mfma16(BD[ks], pa[i++], acc);
+        O[m] = acc;
+    }
     bf16x8 BH[2], BL[2];
     split_hi_lo(su, Dl, BH, BL);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        if (t == 4) {
+        if (t == 2) {
 #pragma unroll
             for (int tt = 4; tt < 8; ++tt)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) akt[tt][ks] = ld8(buf, kBufKt + swz128(16 * tt + li, 4 * ks + lq));
+                for (int ks = 0; ks < 2; ++ks) akt[tt][ks] = kt_frag(buf, tt, ks, li, lq);
         }
         f32x4 acc = S[t] * eC;
 #pragma unroll
@@ -397,52 +412,6 @@ __device__ __forceinline__ void state_products(const char* buf, f32x4 S[8], cons
         }
         S[t] = acc;
     }
-}
-
-// O = Gamma n_q (Q S0) + P Delta for this wave's 16 columns (fp32 registers,
-// rows 16m + 4lq + e)
-__device__ __forceinline__ void out_tile(const char* buf, const f32x4 QS[4], const bf16x8 BD[2], f32x4 O[4], int li,
-                                         int lq) {
-    f32x4 so[4];
-    bf16x8 pa[6];
-#pragma unroll
-    for (int m = 0, i = 0; m < 4; ++m) {
-        so[m] = ldf4(buf, kBufTok + 4 * (2 * kC + 16 * m + 4 * lq));
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            if (ks == 0 || m >= 2) pa[i++] = ld8(buf + kBufPA, pa_off(0, 16 * m + li, 4 * ks + lq));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0, i = 0; m < 4; ++m) {
-        f32x4 acc = so[m] * QS[m];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
-        O[m] = acc;
-    }
-}
-
-// O (bf16) -> the chunk's Q region as [64][N] rows.  Lanes 2i and 2i + 1
-// (adjacent columns) swap values so that each writes two columns of two of
-// its four rows as one 4-byte word.
-template <int N>
-__device__ __forceinline__ void stage_out(char* buf, const f32x4 O[4], int cw, int li, int lq) {
-    const bool odd = li & 1;
-    uint32_t* os = reinterpret_cast<uint32_t*>(buf + kBufQ) + (cw >> 1);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-            const float mine = odd ? O[m][2 + e2] : O[m][e2];
-            const float give = odd ? O[m][e2] : O[m][2 + e2];
-            const float got = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(give), 0xB1, 0xF, 0xF, false));
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const bf16x2 pr = __builtin_convertvector(
-                (f32x4{odd ? got : mine, odd ? mine : got, 0.f, 0.f}).xy, bf16x2);
-            const int row = 16 * m + 4 * lq + (odd ? 2 + e2 : e2);
-            os[row * (N / 2)] = __builtin_bit_cast(uint32_t, pr);
-        }
 }
 
 struct StateCtx {
@@ -460,64 +429,68 @@ __device__ __forceinline__ int64_t state_channel(const PrefillParams& p, const S
 }
 
 // Layout and memory-wave roles of the state kernel with NW compute waves
-// (16 state columns each) and 8 - NW memory waves.  Wave w runs on SIMD
-// w % 4.
-//   K waves (m 0, 1)   K rows 0..31 / 32..63, wait, K^T granules 0..3 / 4..7
-//   V waves            the slice's v front end, one 4-channel x 4-row item
-//                      per lane (NW = 4: every memory wave; NW = 2: waves 6, 7,
-//                      on the SIMDs without a compute wave)
-//   copy waves         the other record pieces and the raw slab, round robin
-//   every memory wave  first stores its O pieces of the previous chunk from
-//                      the Q region it is about to refill, then refills
-//                      those Q pieces itself
+// (16 state columns each) and 8 - NW memory waves (m = wave - NW; wave w
+// runs on SIMD w % 4).  Memory wave m copies the record pieces
+// [rec_lo(m), rec_hi(m)) of each chunk.  The V waves (NW = 4: every memory
+// wave; NW = 2: m = 4, 5, on the SIMDs without a compute wave) also run the
+// front end of the slice's v channels, part v_part(m) of the chunk's rows,
+// one 4-channel x 4-row item per lane, from a raw slab of exactly those rows
+// (+ 3 rows of conv history) that the same wave copied one chunk earlier
+// into its own slab region.
 template <int NW>
 struct StateShape {
     static constexpr int NM = 8 - NW;
     static constexpr int N = 16 * NW;                        // state columns per workgroup
     static constexpr int SPLIT = kD / N;
     static constexpr int BUF = kBufVt + N * kVtLd * 2;
-    static constexpr int SLAB_ROW = N * 2;                   // raw v slab: [67 rows][N channels] bf16
-    static constexpr int SLAB = (kC + 3) * SLAB_ROW;
-    static constexpr int SLAB_PIECES = (SLAB + 1023) / 1024;
-    static constexpr int O_PIECES = kC * N * 2 / 1024;       // O staged in Q pieces 0 .. O_PIECES - 1
-    static constexpr int NV = NW == 4 ? 4 : 2;               // V waves
-    static constexpr int OTHER = (16 - O_PIECES) + 12 + 2 + SLAB_PIECES;
-    static constexpr int NCOPY = NW == 4 ? 4 : 4;            // copy waves: NW = 4: m 0..3; NW = 2: m 2..5
-    __device__ static bool is_v(int m) { return NW == 4 || m >= 4; }
-    __device__ static int v_part(int m) { return NW == 4 ? m : m - 4; }
-    __device__ static int copy_index(int m) { return NW == 4 ? m : m - 2; }   // < 0: not a copy wave
+    static constexpr int NV = NW == 4 ? 4 : 2;               // V waves = parts of the chunk's rows
+    static constexpr int SLAB_ROW = N * 2;                   // raw v slab: [rows][N channels] bf16
+    static constexpr int PART_ROWS = kC / NV;
+    static constexpr int SLAB_ROWS = PART_ROWS + 3;
+    static constexpr int SLAB_PIECES = (SLAB_ROWS * SLAB_ROW + 1023) / 1024;
+    static constexpr int SLAB = SLAB_PIECES * 1024;          // one part's slab region
+    static_assert(SLAB_PIECES == 3, "three slab pieces per V wave");
+    static constexpr bool is_v(int m) { return NW == 4 || m >= 4; }
+    static constexpr int v_part(int m) { return NW == 4 ? m : m - 4; }
+    // record pieces: NW = 2: 10, 10, 10, 8 for m 0..3 and 4, 4 for the V
+    // waves; NW = 4: 12, 12, 11, 11
+    static constexpr int rec_lo(int m) {
+        return NW == 4 ? (m < 2 ? 12 * m : 24 + 11 * (m - 2)) : (m < 3 ? 10 * m : m == 3 ? 30 : 38 + 4 * (m - 4));
+    }
+    static constexpr int rec_hi(int m) { return m + 1 == NM ? kPieces : rec_lo(m + 1); }
 };
 
-// Copy piece pc of a chunk's raw v slab (first row at call-local token
-// local0 - 3) into `slab`
+// Copy piece pc of the raw v slab of row part `part` of a chunk (slab row i
+// = call-local token local0 - 3 + part * PART_ROWS + i) into `slab`
 template <int NW>
 __device__ __forceinline__ void issue_slab(const PrefillParams& p, const StateCtx& cx, char* slab, int64_t local0,
-                                           int pc, int lane) {
+                                           int part, int pc, int lane) {
     using SS = StateShape<NW>;
     const int o = pc * 1024 + 16 * lane;
-    if (o < SS::SLAB) {
+    if (o < SS::SLAB_ROWS * SS::SLAB_ROW) {
         const int row = o / SS::SLAB_ROW, g = (o % SS::SLAB_ROW) / 16;
-        const int64_t t = min(max(local0 - 3 + row, (int64_t)0), p.seq_len - 1);
+        const int64_t t = min(max(local0 - 3 + part * SS::PART_ROWS + row, (int64_t)0), p.seq_len - 1);
         const uint16_t* src = static_cast<const uint16_t*>(p.qkv) + ((int64_t)cx.b * p.seq_len + t) * p.conv_dim +
                               2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + 8 * g;
         __builtin_amdgcn_global_load_lds(src, LDS_PTR(slab + pc * 1024), 16, 0, 0);
     }
 }
 
-// Front end of part `part` of the slice's v channels for one chunk from its
-// raw slab -> V^T in the chunk's buffer.  Items of 4 channels x 4 rows, one
-// per lane: N / 4 channel groups x 16 row groups, 64 items per part.
+// Front end of row part `part` of the slice's v channels for one chunk from
+// its raw slab -> V^T in the chunk's buffer.  Items of 4 channels x 4 rows,
+// one per lane: N / 4 channel groups x PART_ROWS / 4 row groups = 64 items.
 template <int NW, bool INTERIOR>
 __device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& cx, const float* Wv, const char* slab,
                                         char* buf, int64_t local0, int part, int lane) {
     using SS = StateShape<NW>;
     constexpr int CG = SS::N / 4;
-    const int item = 64 * part + lane;
-    const int c0 = (item % CG) * 4, tau0 = (item / CG) * 4;
+    static_assert(CG * (SS::PART_ROWS / 4) == 64, "one item per lane");
+    const int c0 = (lane % CG) * 4, rt = (lane / CG) * 4;
+    const int tau0 = part * SS::PART_ROWS + rt;
     const int64_t gc = 2 * (int64_t)p.num_k_heads * kD + (int64_t)cx.h * kD + cx.zcol0 + c0;
     uint2 raw[7];
 #pragma unroll
-    for (int k = 0; k < 7; ++k) raw[k] = *reinterpret_cast<const uint2*>(slab + (tau0 + k) * SS::SLAB_ROW + 2 * c0);
+    for (int k = 0; k < 7; ++k) raw[k] = *reinterpret_cast<const uint2*>(slab + (rt + k) * SS::SLAB_ROW + 2 * c0);
     float w[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -530,30 +503,36 @@ __device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& 
         *reinterpret_cast<bf16x4*>(buf + kBufVt + ((c0 + i) * kVtLd + tau0) * 2) = bf16x4{ub[0][i], ub[1][i], ub[2][i], ub[3][i]};
 }
 
-// O piece o of chunk kc (staged in buf's Q region) -> HBM: 16 bytes per lane
-template <int NW>
-__device__ __forceinline__ void store_out_piece(const PrefillParams& p, const StateCtx& cx, const char* buf,
-                                                int64_t kc, int o, int lane) {
-    using SS = StateShape<NW>;
-    const int off = o * 1024 + 16 * lane;
-    const int row = off / (SS::N * 2), c8 = (off % (SS::N * 2)) / 16;
-    const uint4 v = *reinterpret_cast<const uint4*>(buf + kBufQ + off);
-    const int64_t t = kc * kC - p.start_pos + row;
-    if (t >= 0 && t < p.seq_len)
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) +
-                                  (((int64_t)cx.b * p.seq_len + t) * p.num_v_heads + cx.h) * kD + cx.zcol0 + 8 * c8) = v;
+// O of chunk kc -> out (bf16): lane (i, q) of compute wave w writes columns
+// 16w + 4q .. 16w + 4q + 3 of token 16m + i, one 8-byte store per tile.
+// `obase` points at this lane's columns of call-local token i.
+__device__ __forceinline__ void store_o(const PrefillParams& p, uint16_t* obase, const f32x4 O[4], int64_t kc, int li) {
+    const int64_t row_stride = (int64_t)p.num_v_heads * kD;
+    const int64_t t0 = kc * kC - p.start_pos;
+    uint16_t* o = obase + t0 * row_stride;
+    if (t0 >= 0 && t0 + kC <= p.seq_len) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = __builtin_convertvector(O[m], bf16x4);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int64_t t = t0 + 16 * m + li;
+            if (t >= 0 && t < p.seq_len)
+                *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = __builtin_convertvector(O[m], bf16x4);
+        }
+    }
 }
 
-// Checkpoint slot when the end of chunk kc is a multiple of the checkpoint
-// interval: this compute wave's state slice and (over the compute threads)
-// the conv tails of the workgroup's channels
+// Checkpoint slot of chunk kc, whose end is a multiple of the checkpoint
+// interval (the caller tracks that): this compute wave's state slice and
+// (over the compute threads) the conv tails of the workgroup's channels
 template <int NW>
 __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCtx& cx, const f32x4 S[8], int64_t kc,
                                            int tid) {
     constexpr int NT = 64 * NW, NCH = 2 * kD + 16 * NW;
     const int lq = (tid % 64) / 16;
     const int64_t pe = (kc + 1) * kC;
-    if (p.ckpt_interval > 0 && pe % p.ckpt_interval == 0 && pe <= p.start_pos + p.seq_len) {
+    if (pe <= p.start_pos + p.seq_len) {
         char* slot = p.ckpt_buf + (uint64_t)(pe / p.ckpt_interval - 1) * p.slot_bytes;
         float* rec = reinterpret_cast<float*>(slot + p.conv_slot_bytes);
 #pragma unroll
@@ -566,48 +545,94 @@ __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCt
     }
 }
 
-// Memory wave m's share of one chunk: store the O pieces of chunk jn - 2
-// (staged in buf's Q region) and refill buf with chunk jn: records, raw slab
-// of chunk jn + 1 into slab_next, v front end from `slab`, K^T.
-template <int NW>
-__device__ __forceinline__ void mem_chunk(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf,
-                                          const char* slab, char* slab_next, int jn, bool store_prev, int m, int lane) {
+// vmcnt(n): wait until at most n vector-memory operations of this wave are
+// outstanding (they complete in issue order).  LGKM: also wait for every LDS
+// operation.
+template <int n, bool LGKM = false>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((LGKM ? 0x0070 : 0x0f70) | n);   // expcnt: no wait
+}
+
+// Workgroup barrier without the memory fences of __syncthreads: each wave
+// first waits itself for the operations the others depend on (its LDS reads
+// and writes, its LDS copies), so copies that no other wave reads before the
+// next barrier (a V wave's next slab) stay in flight.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Memory wave M's share of filling buf with chunk jn: its record pieces; for
+// a V wave then the v front end from slab_cur (this wave's raw slab of chunk
+// jn, copied in the previous step) and the copy of chunk jn + 1's slab into
+// slab_next, which may stay in flight across the barrier that follows.
+template <int NW, int M>
+__device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf,
+                                         const char* slab_cur, char* slab_next, int jn, int lane) {
     using SS = StateShape<NW>;
-    const bool fill = jn < sp.nseg;
-    // O pieces of the chunk that last used this buffer, then the same Q pieces
-    if (store_prev)
-        for (int o = m; o < SS::O_PIECES; o += SS::NM) store_out_piece<NW>(sp.p, cx, buf, sp.k0 + jn - 2, o, lane);
-    if (!fill) return;
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the O rows are in registers before the buffer is refilled
+    constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M);
+    if (jn >= sp.nseg) {
+        wait_vm<0, true>();
+        return;
+    }
     const char* krec = key_rec(sp, cx.b, cx.kh, jn);
     const char* vrec = val_rec(sp, cx.b, cx.h, jn);
-    for (int o = m; o < SS::O_PIECES; o += SS::NM) issue_piece(buf, krec, vrec, o, lane);
-    if (m < 2)
-        for (int pc = kPiecesK + 8 * m; pc < kPiecesK + 8 * m + 8; ++pc) issue_piece(buf, krec, vrec, pc, lane);
-    const int ci = SS::copy_index(m);
-    if (ci >= 0) {
-        for (int i = ci; i < SS::OTHER; i += SS::NCOPY) {
-            // other pieces: Q pieces O_PIECES..15, P | AN, scale rows, then the next slab
-            if (i < 16 - SS::O_PIECES) issue_piece(buf, krec, vrec, SS::O_PIECES + i, lane);
-            else if (i < 16 - SS::O_PIECES + 14) issue_piece(buf, krec, vrec, kPiecesPA + (i - (16 - SS::O_PIECES)), lane);
-            else if (jn + 1 < sp.nseg)
-                issue_slab<NW>(sp.p, cx, slab_next, (sp.k0 + jn + 1) * kC - sp.p.start_pos, i - (30 - SS::O_PIECES), lane);
-        }
-    }
-    if (SS::is_v(m)) {
+#pragma unroll
+    for (int pc = LO; pc < HI; ++pc) issue_piece(buf, krec, vrec, pc, lane);
+    if constexpr (SS::is_v(M)) {
+        constexpr int part = SS::v_part(M);
+        wait_vm<HI - LO>();   // the slab copies issued before these pieces have landed
         const int64_t local0 = (sp.k0 + jn) * kC - sp.p.start_pos;
-        if (local0 >= 3 && local0 + kC <= sp.p.seq_len) v_front<NW, true>(sp.p, cx, Wv, slab, buf, local0, SS::v_part(m), lane);
-        else v_front<NW, false>(sp.p, cx, Wv, slab, buf, local0, SS::v_part(m), lane);
-    }
-    if (m < 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        transpose_k(buf, 4 * m, lane);
+        if (local0 >= 3 && local0 + kC <= sp.p.seq_len) v_front<NW, true>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
+        else v_front<NW, false>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
+        if (jn + 1 < sp.nseg) {
+#pragma unroll
+            for (int pc = 0; pc < SS::SLAB_PIECES; ++pc) issue_slab<NW>(sp.p, cx, slab_next, local0 + kC, part, pc, lane);
+            wait_vm<SS::SLAB_PIECES, true>();
+        } else {
+            wait_vm<0, true>();
+        }
+    } else {
+        wait_vm<0, true>();
     }
 }
 
-// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  Per chunk
-// two barriers: E (the chunk's products are done and the next chunk's buffer
-// is filled) and B (the chunk's O rows are staged in its Q region).
+// Memory wave M over the whole segment: the same barriers as the compute
+// waves (two in the prologue, one per chunk).  Two chunks per trip so that
+// each LDS buffer and slab region is a distinct object: the compiler then
+// orders reads of one only after its own copies.  Chunk c's buffer is
+// buf[c % 2] and its raw slab slab[c % 2].
+template <int NW, int M>
+__device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
+                                         char* buf1, char* slab0, char* slab1, int lane) {
+    using SS = StateShape<NW>;
+    if constexpr (SS::is_v(M)) {
+        if (sp.nseg > 0)
+#pragma unroll
+            for (int pc = 0; pc < SS::SLAB_PIECES; ++pc)
+                issue_slab<NW>(sp.p, cx, slab0, sp.k0 * kC - sp.p.start_pos, SS::v_part(M), pc, lane);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    mem_step<NW, M>(sp, cx, Wv, buf0, slab0, slab1, 0, lane);
+    __syncthreads();
+    for (int j = 0; j < sp.nseg; j += 2) {
+        mem_step<NW, M>(sp, cx, Wv, buf1, slab1, slab0, j + 1, lane);
+        lds_barrier();
+        if (j + 1 < sp.nseg) {
+            mem_step<NW, M>(sp, cx, Wv, buf0, slab0, slab1, j + 2, lane);
+            lds_barrier();
+        }
+    }
+    wait_vm<0>();
+}
+
+// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  One
+// barrier per chunk: the chunk's products are done (its buffer may be
+// refilled) and the next chunk's buffer is filled.
 template <int NW>
 __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
     using SS = StateShape<NW>;
@@ -615,8 +640,8 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
     const PrefillParams& p = sp.p;
     __shared__ __attribute__((aligned(16))) char buf0[SS::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[SS::BUF];
-    __shared__ __attribute__((aligned(16))) char slab0[SS::SLAB];   // raw v slabs, per chunk parity
-    __shared__ __attribute__((aligned(16))) char slab1[SS::SLAB];
+    __shared__ __attribute__((aligned(16))) char slab0[SS::NV * SS::SLAB];   // raw v slabs of the V waves,
+    __shared__ __attribute__((aligned(16))) char slab1[SS::NV * SS::SLAB];   // per chunk parity
     __shared__ float Wv[4 * N];                                     // conv taps of the slice's v channels
 
     const int tid = threadIdx.x, lane = tid % 64;
@@ -649,7 +674,7 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
     __syncthreads();
 
     // The two roles run separate loops with the same barriers (two in the
-    // prologue, two per chunk), so their registers do not add up.
+    // prologue, one per chunk), so their registers do not add up.
     if (compute) {
         const float* s_src = sp.first_seg ? p.rec_in : p.rec_out;
         f32x4 S[8];
@@ -657,63 +682,55 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[t][e] = s_src ? s_src[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] : 0.f;
+        // checkpoints every `every` chunks; `phase` counts chunk ends since
+        // the last one (0: this chunk's end is a checkpoint position)
+        const int64_t every = p.ckpt_interval / kC;
+        int64_t phase = every > 0 ? (sp.k0 + 1) % every : 1;
+        // the state loads complete here, so the chunk loop never waits on
+        // the vector-memory counter (its O stores would hold it up)
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         __syncthreads();
         const int cw = 16 * wave + li;
+        uint16_t* obase = static_cast<uint16_t*>(p.out) + ((int64_t)cx.b * p.seq_len * p.num_v_heads + cx.h) * kD +
+                          cx.zcol0 + 16 * wave + 4 * lq + (int64_t)li * p.num_v_heads * kD;
         for (int j = 0; j < sp.nseg; ++j) {
-            char* cur = (j & 1) ? buf1 : buf0;
+            const char* cur = (j & 1) ? buf1 : buf0;
             bf16x4 vv[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
                 vv[mb] = *reinterpret_cast<const bf16x4*>(cur + kBufVt + (cw * kVtLd + 16 * mb + 4 * lq) * 2);
-            f32x4 QS[4], O[4];
-            bf16x8 BD[2];
-            state_products(cur, S, vv, QS, BD, li, lq);
-            out_tile(cur, QS, BD, O, li, lq);
-            // finish O before E (the compiler would otherwise sink it past
-            // the barrier, where the memory waves wait for it)
-            asm volatile("" ::"v"(O[0]), "v"(O[1]), "v"(O[2]), "v"(O[3]));
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();   // E
-            stage_out<N>(cur, O, cw, li, lq);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();   // B
-            checkpoint<NW>(p, cx, S, sp.k0 + j, tid);
+            f32x4 O[4];
+            chunk_products(cur, S, vv, O, li, lq);
+            store_o(p, obase, O, sp.k0 + j, li);
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): every LDS read of this buffer has returned
+            lds_barrier();
+            if (every > 0) {
+                if (phase == 0) checkpoint<NW>(p, cx, S, sp.k0 + j, tid);
+                phase = phase + 1 == every ? 0 : phase + 1;
+            }
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) p.rec_out[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
     } else {
+        // each V wave's slab region: part v_part(m) of the slab arrays
         const int m = wave - NW;
-        // raw slab of chunk 0, then chunk 0 into buf0 (and chunk 1's slab)
-        if (sp.nseg > 0)
-            for (int pc = m; pc < SS::SLAB_PIECES; pc += SS::NM) issue_slab<NW>(p, cx, slab0, sp.k0 * kC - p.start_pos, pc, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        mem_chunk<NW>(sp, cx, Wv, buf0, slab0, slab1, 0, false, m, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // Step j: store O of chunk j - 1 from the other buffer and refill it
-        // with chunk j + 1.  Two chunks per trip so that each LDS buffer is a
-        // distinct object: the compiler then orders reads of one buffer only
-        // after its own copies.  Chunk c's slab lives in slab[c % 2].
-        for (int j = 0; j < sp.nseg; j += 2) {
-            mem_chunk<NW>(sp, cx, Wv, buf1, slab1, slab0, j + 1, j >= 1, m, lane);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();   // E
-            __syncthreads();   // B
-            if (j + 1 < sp.nseg) {
-                mem_chunk<NW>(sp, cx, Wv, buf0, slab0, slab1, j + 2, true, m, lane);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();   // E
-                __syncthreads();   // B
-            }
-        }
-        // O of the last chunk
-        if (sp.nseg > 0) {
-            const char* last = ((sp.nseg - 1) & 1) ? buf1 : buf0;
-            for (int o = m; o < SS::O_PIECES; o += SS::NM) store_out_piece<NW>(p, cx, last, sp.k0 + sp.nseg - 1, o, lane);
+        const int vo = SS::is_v(m) ? SS::v_part(m) * SS::SLAB : 0;
+        char* s0 = slab0 + vo;
+        char* s1 = slab1 + vo;
+        switch (m) {
+            case 0: mem_role<NW, 0>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 1: mem_role<NW, 1>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 2: mem_role<NW, 2>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 3: mem_role<NW, 3>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            default:
+                if constexpr (NW == 2) {
+                    if (m == 4) mem_role<NW, 4>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
+                    else mem_role<NW, 5>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
+                }
+                break;
         }
     }
     if (sp.last_seg) {
