@@ -307,14 +307,17 @@ __device__ __forceinline__ f32x4 ldf4(const char* buf, int off) { return *reinte
 
 // One chunk for this wave's 16 state columns: K S0, R = beta V - beta
 // Gamma n_k (K S0), Delta by blocked substitution with (Q S0)^T in its
-// latency, O^T = (Q S0)^T diag(Gamma n_q) + (P Delta)^T, then the state update
-// S <- exp(gamma_C) S + K^T Delta' (Delta' as bf16 hi + lo).  O comes out
-// before the update, so its stores overlap the update.  Lane (i, q) of O
-// tile m holds token 16m + i, columns 4q..4q+3: a transposed tile comes from
-// the same operand registers with A and B swapped.  LDS operands are
-// requested in three batches, each well ahead of its use.
-__device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], const bf16x4 vv[4], f32x4 O[4], int li,
-                                               int lq) {
+// latency, O^T = (Q S0)^T diag(Gamma n_q) + (P Delta)^T (bf16 into Ob), then
+// the state update S <- exp(gamma_C) S + K^T Delta' (Delta' as bf16 hi +
+// lo).  Lane (i, q) of O tile m holds token 16m + i, columns 4q..4q+3: a
+// transposed tile comes from the same operand registers with A and B
+// swapped.  LDS operands are requested well ahead of their use: K and the
+// substitution's operands first, Q and P next, the K^T fragments of two
+// state tiles as each Q tile is retired.  store_prev() (the previous chunk's
+// O stores) runs inside the substitution, where the wave mostly waits.
+template <class StorePrev>
+__device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], const bf16x4 vv[4], bf16x4 Ob[4], int li,
+                                               int lq, StorePrev&& store_prev) {
     // batch 1: K fragments, the row scales of R (this lane's rows
     // 16m + 4lq + e) and the substitution's A-operand slots (token block k
     // of an AN row sits in granule 4 (k / 2) + lq, half k % 2)
@@ -341,20 +344,27 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) Bs[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 R[4];
+    // K S0 with the four row tiles' accumulation chains interleaved
+    f32x4 KS[4], R[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f32x4 k = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m) KS[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) k = mfma16(ak[m][ks], Bs[ks], k);
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * k[e];
-    }
-    // batch 2: Q and P fragments
+        for (int m = 0; m < 4; ++m) KS[m] = mfma16(ak[m][ks], Bs[ks], KS[m]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[m][e] = sb[m][e] * float(vv[m][e]) - sr[m][e] * KS[m][e];
+    // batch 2: Q and P fragments, the O scales of tokens 16m + li
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) aq[m][ks] = ld8(buf, kBufQ + swz256(16 * m + li, 4 * ks + lq));
+    float so[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) so[m] = *reinterpret_cast<const float*>(buf + kBufTok + 4 * (2 * kC + 16 * m + li));
+    const float eC = *reinterpret_cast<const float*>(buf + kBufTok + 4 * 4 * kC);
     bf16x8 pa[6];
 #pragma unroll
     for (int m = 0, i = 0; m < 4; ++m)
@@ -363,28 +373,24 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
             if (ks == 0 || m >= 2) pa[i++] = ld8(buf + kBufPA, pa_off(0, 16 * m + li, 4 * ks + lq));
     f32x4 Dl[4], QT[4];
     bf16x4 Db[4];
+    bf16x8 akt[8][2];
 #pragma unroll
     for (int m = 0; m < 4; ++m) QT[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     delta_substitution(R, dg, a10, a2x, a3x, a32, Dl, Db, [&](int s) {
         const int m = s / 2, k0 = 2 * (s % 2);
         QT[m] = mfma16(Bs[k0], aq[m][k0], QT[m]);
         QT[m] = mfma16(Bs[k0 + 1], aq[m][k0 + 1], QT[m]);
+        if (s == 2) store_prev();
+        if (s % 2 == 1)   // Q tile m retired: K^T fragments of state tiles 2m, 2m + 1
+#pragma unroll
+            for (int t = 2 * m; t < 2 * m + 2; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) akt[t][ks] = kt_frag(buf, t, ks, li, lq);
     });
-    // batch 3: the scales of O and of the update, K^T fragments of the
-    // update (the second half once the first tiles are under way)
+    // the scales of the update
     f32x4 su[4];
-    float so[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        su[m] = ldf4(buf, kBufTok + 4 * (3 * kC + 16 * m + 4 * lq));
-        so[m] = *reinterpret_cast<const float*>(buf + kBufTok + 4 * (2 * kC + 16 * m + li));
-    }
-    const float eC = *reinterpret_cast<const float*>(buf + kBufTok + 4 * 4 * kC);
-    bf16x8 akt[8][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) akt[t][ks] = kt_frag(buf, t, ks, li, lq);
+    for (int m = 0; m < 4; ++m) su[m] = ldf4(buf, kBufTok + 4 * (3 * kC + 16 * m + 4 * lq));
     const bf16x8 BD[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
 #pragma unroll
     for (int m = 0, i = 0; m < 4; ++m) {
@@ -392,26 +398,17 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             if (ks == 0 || m >= 2) acc = mfma16(BD[ks], pa[i++], acc);
-        O[m] = acc;
+        Ob[m] = __builtin_convertvector(acc, bf16x4);
     }
     bf16x8 BH[2], BL[2];
     split_hi_lo(su, Dl, BH, BL);
+    // the eight state tiles' accumulation chains interleaved
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (t == 2) {
+    for (int t = 0; t < 8; ++t) S[t] *= eC;
 #pragma unroll
-            for (int tt = 4; tt < 8; ++tt)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) akt[tt][ks] = kt_frag(buf, tt, ks, li, lq);
-        }
-        f32x4 acc = S[t] * eC;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            acc = mfma16(akt[t][ks], BH[ks], acc);
-            acc = mfma16(akt[t][ks], BL[ks], acc);
-        }
-        S[t] = acc;
-    }
+        for (int t = 0; t < 8; ++t) S[t] = mfma16(akt[t][st / 2], (st % 2 ? BL : BH)[st / 2], S[t]);
 }
 
 struct StateCtx {
@@ -506,19 +503,18 @@ __device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& 
 // O of chunk kc -> out (bf16): lane (i, q) of compute wave w writes columns
 // 16w + 4q .. 16w + 4q + 3 of token 16m + i, one 8-byte store per tile.
 // `obase` points at this lane's columns of call-local token i.
-__device__ __forceinline__ void store_o(const PrefillParams& p, uint16_t* obase, const f32x4 O[4], int64_t kc, int li) {
+__device__ __forceinline__ void store_o(const PrefillParams& p, uint16_t* obase, const bf16x4 O[4], int64_t kc, int li) {
     const int64_t row_stride = (int64_t)p.num_v_heads * kD;
     const int64_t t0 = kc * kC - p.start_pos;
     uint16_t* o = obase + t0 * row_stride;
     if (t0 >= 0 && t0 + kC <= p.seq_len) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = __builtin_convertvector(O[m], bf16x4);
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = O[m];
     } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int64_t t = t0 + 16 * m + li;
-            if (t >= 0 && t < p.seq_len)
-                *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = __builtin_convertvector(O[m], bf16x4);
+            if (t >= 0 && t < p.seq_len) *reinterpret_cast<bf16x4*>(o + 16 * m * row_stride) = O[m];
         }
     }
 }
@@ -694,15 +690,19 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
         const int cw = 16 * wave + li;
         uint16_t* obase = static_cast<uint16_t*>(p.out) + ((int64_t)cx.b * p.seq_len * p.num_v_heads + cx.h) * kD +
                           cx.zcol0 + 16 * wave + 4 * lq + (int64_t)li * p.num_v_heads * kD;
+        bf16x4 Ob[4];   // O of the previous chunk, stored during the next one
         for (int j = 0; j < sp.nseg; ++j) {
             const char* cur = (j & 1) ? buf1 : buf0;
             bf16x4 vv[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
                 vv[mb] = *reinterpret_cast<const bf16x4*>(cur + kBufVt + (cw * kVtLd + 16 * mb + 4 * lq) * 2);
-            f32x4 O[4];
-            chunk_products(cur, S, vv, O, li, lq);
-            store_o(p, obase, O, sp.k0 + j, li);
+            bf16x4 On[4];
+            chunk_products(cur, S, vv, On, li, lq, [&] {
+                if (j > 0) store_o(p, obase, Ob, sp.k0 + j - 1, li);
+            });
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Ob[m] = On[m];
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): every LDS read of this buffer has returned
             lds_barrier();
             if (every > 0) {
@@ -710,6 +710,7 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
                 phase = phase + 1 == every ? 0 : phase + 1;
             }
         }
+        if (sp.nseg > 0) store_o(p, obase, Ob, sp.k0 + sp.nseg - 1, li);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
