@@ -97,8 +97,8 @@ def time_events(fn, steps, warmup):
 def bench_prefill(args):
     """The prefill call as a user makes it for this shape: with a workspace
     (allocated once, outside the timed region), which selects the two-pass
-    path for B * H_v <= 128.  The fused single-pass kernel (no workspace) is
-    timed beside it for reference."""
+    path.  The fused single-pass kernel (no workspace) is timed beside it for
+    reference."""
     import torch
     from linear_attention_recurrence_causal_amd import gdn, inputs as I
     w = I.WORKLOADS[2]

@@ -113,14 +113,13 @@ gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_
  * The chunked form splits into per-chunk work that does not depend on the
  * state and a short recurrence over chunks that does ("Performance note");
  * with a workspace the first part runs for every chunk in parallel and only
- * the second runs chunk by chunk, which fills the GPU when B * H_v is small.
- * A smaller workspace, down to one chunk's worth (the value for seq_len = 1),
- * is used segment by segment.  With less than that, or NULL, or a head group
- * H_v / H_k above 8, gdn_prefill_chunked runs a fused single-pass kernel that
- * keeps every intermediate on chip; it also does so when B * H_v > 128, where
- * the fused kernel already fills the GPU (the environment variable
- * GDN_PREFILL_PATH=split or =fused overrides this choice).  Both paths
- * compute the same values in the same precision. */
+ * the second runs chunk by chunk, which is the faster path at every batch
+ * size measured.  A smaller workspace, down to one chunk's worth (the value
+ * for seq_len = 1), is used segment by segment.  With less than that, or
+ * NULL, or a head group H_v / H_k above 8, gdn_prefill_chunked runs a fused
+ * single-pass kernel that keeps every intermediate on chip (the environment
+ * variable GDN_PREFILL_PATH=split or =fused overrides the choice).  Both
+ * paths compute the same values in the same precision. */
 gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, uint64_t* bytes);
 
 /* Chunked prefill of seq_len tokens per sequence ("Performance note":

@@ -177,16 +177,13 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     }
 
     // The two-pass path needs at least one chunk of records in the
-    // workspace.  It pays off while the fused kernel's one workgroup per
-    // (sequence, value head) would leave at least half of the 256 CUs idle;
-    // GDN_PREFILL_PATH=split|fused overrides the choice.
+    // workspace; GDN_PREFILL_PATH=split|fused overrides the choice.
     const uint64_t chunk_ws = gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads);
     const bool ws_ok = workspace && chunk_ws > 0 && workspace_bytes >= chunk_ws &&
                        cfg->num_v_heads / cfg->num_k_heads <= 8;
     const char* path_env = getenv("GDN_PREFILL_PATH");
-    const bool force_split = path_env && path_env[0] == 's';
     const bool force_fused = path_env && path_env[0] == 'f';
-    const bool two_pass = ws_ok && !force_fused && (force_split || (int64_t)cfg->batch * cfg->num_v_heads <= 128);
+    const bool two_pass = ws_ok && !force_fused;
     if (two_pass) {
         // only the part a call can use is checked against the other buffers
         const int64_t k_first = start_pos / cfg->chunk;

@@ -61,8 +61,8 @@ def gpu_prefill(G, w, d, seq=slice(None), start_pos=0, conv_in="init", rec_in="i
     whole call in one segment)."""
     c = cfg_of(G, w)
     ws = None if path == "fused" else workspace
-    # a workspace enables the two-pass path; force it where the size-based
-    # choice would take the fused kernel
+    # a workspace selects the two-pass path; "split" keeps it selected even
+    # if the environment asks for the fused kernel
     old_env = os.environ.get("GDN_PREFILL_PATH")
     os.environ["GDN_PREFILL_PATH"] = "split" if path == "split" else "auto"
     cin = d["conv_state"] if conv_in == "init" else conv_in
