@@ -10,7 +10,9 @@
 //   o = S^T q = S'^T q + delta (k . q).
 //
 // Memory-bound by design: the fp32 state (d_k x d_v per head, 64 KiB at 128)
-// is read once and written once; everything else is < 3% of the bytes.
+// is read once and written once; everything else is < 3% of the bytes.  The
+// few front-end inputs are requested before the state, so the conv, norms and
+// gates are done by the time the state arrives.
 // One workgroup owns a (b, h, NCOL-column slice) of S.  Columns of S are
 // independent given (q, k, beta, g), so slicing d_v multiplies parallelism;
 // each slice recomputes the (cheap) conv of its head's q and k channels.
@@ -33,7 +35,7 @@ namespace {
 constexpr int kDecodeThreads = 256;
 
 template <typename IO, int DK, int NCOL>
-__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
     constexpr int NRG = kDecodeThreads / NCQ;     // row groups
@@ -62,7 +64,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParam
     const int cq = tid % NCQ;
     const int rg = tid / NCQ;
 
-    // ---- 1. issue the state loads first (they dominate the bytes)
+    // ---- 1. front-end inputs of the slice's channels: few bytes, requested
+    // first so that they return (in issue order) ahead of the state and the
+    // conv, norms and gates run while the state is still in flight
+    constexpr int CPT = (NCH + kDecodeThreads - 1) / kDecodeThreads;   // channels per thread
+    const bool write_qk_tail = (h % r == 0) && (z == 0);
+    float fin[CPT][8];   // conv state (3), current input, taps (4)
+    int64_t fcs[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int i = tid + k * kDecodeThreads;
+        if (i < NCH) {
+            int64_t c;
+            if (i < DK) c = (int64_t)kh * DK + i;
+            else if (i < 2 * DK) c = (int64_t)p.num_k_heads * DK + (int64_t)kh * DK + (i - DK);
+            else c = 2 * (int64_t)p.num_k_heads * DK + (int64_t)h * dv + col0 + (i - 2 * DK);
+            const int64_t cs = ((int64_t)b * conv_dim + c) * 3;
+            fcs[k] = cs;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) fin[k][j] = p.conv_in ? T::load(p.conv_in, cs + j) : 0.f;
+            fin[k][3] = T::load(p.qkv, (int64_t)b * conv_dim + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fin[k][4 + j] = T::load(p.conv_w, c * 4 + j);
+        }
+    }
+    float gate_a = 0.f, gate_b = 0.f;
+    const int wave = tid / 64, lane = tid % 64;
+    if (wave == 3 && lane == 0) {
+        const int64_t gi = (int64_t)b * p.num_v_heads + h;
+        gate_a = T::load(p.a, gi);
+        gate_b = T::load(p.b, gi);
+    }
+
+    // ---- 2. the state slice (the bytes that matter)
     const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * DK * dv + col0 + cq * 4;
     float4 S[RPT];
     if (p.rec_in) {
@@ -74,45 +108,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParam
         for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    // ---- 2. front end for the channels of this slice
-    const bool write_qk_tail = (h % r == 0) && (z == 0);
-    for (int i = tid; i < NCH; i += kDecodeThreads) {
-        int64_t c;
-        bool write_tail;
-        if (i < DK) {
-            c = (int64_t)kh * DK + i;
-            write_tail = write_qk_tail;
-        } else if (i < 2 * DK) {
-            c = (int64_t)p.num_k_heads * DK + (int64_t)kh * DK + (i - DK);
-            write_tail = write_qk_tail;
-        } else {
-            c = 2 * (int64_t)p.num_k_heads * DK + (int64_t)h * dv + col0 + (i - 2 * DK);
-            write_tail = true;
-        }
-        const int64_t cs = ((int64_t)b * conv_dim + c) * 3;
-        const float s0 = p.conv_in ? T::load(p.conv_in, cs + 0) : 0.f;
-        const float s1 = p.conv_in ? T::load(p.conv_in, cs + 1) : 0.f;
-        const float s2 = p.conv_in ? T::load(p.conv_in, cs + 2) : 0.f;
-        const float x = T::load(p.qkv, (int64_t)b * conv_dim + c);
-        const float w0 = T::load(p.conv_w, c * 4 + 0), w1 = T::load(p.conv_w, c * 4 + 1);
-        const float w2 = T::load(p.conv_w, c * 4 + 2), w3 = T::load(p.conv_w, c * 4 + 3);
-        const float y = fmaf(w3, x, fmaf(w2, s2, fmaf(w1, s1, w0 * s0)));
-        u_s[i] = T::round(silu_f32(y));
-        if (write_tail) {
-            if (p.conv_in) {
-                T::copy(p.conv_out, cs + 0, p.conv_in, cs + 1);
-                T::copy(p.conv_out, cs + 1, p.conv_in, cs + 2);
-            } else {
-                T::store(p.conv_out, cs + 0, 0.f);
-                T::store(p.conv_out, cs + 1, 0.f);
+    // conv + SiLU of the slice's channels (io-rounded) and the carried tails
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int i = tid + k * kDecodeThreads;
+        if (i < NCH) {
+            const float* f = fin[k];
+            const float y = fmaf(f[7], f[3], fmaf(f[6], f[2], fmaf(f[5], f[1], f[4] * f[0])));
+            u_s[i] = T::round(silu_f32(y));
+            if (i >= 2 * DK || write_qk_tail) {
+                T::store(p.conv_out, fcs[k] + 0, f[1]);
+                T::store(p.conv_out, fcs[k] + 1, f[2]);
+                T::store(p.conv_out, fcs[k] + 2, f[3]);
             }
-            T::copy(p.conv_out, cs + 2, p.qkv, (int64_t)b * conv_dim + c);
         }
     }
     __syncthreads();
 
     // ---- 3. norms, k.q and the gates (one wave each, fixed order)
-    const int wave = tid / 64, lane = tid % 64;
     if (wave < 3) {
         float acc = 0.f;
         for (int i = lane; i < DK; i += 64) {
@@ -122,10 +135,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParam
         acc = wave_sum(acc);
         if (lane == 0) scal_s[wave] = acc;
     } else if (lane == 0) {
-        const int64_t gi = (int64_t)b * p.num_v_heads + h;
-        const float av = T::load(p.a, gi), bv = T::load(p.b, gi);
-        scal_s[3] = -expf(p.A_log[h]) * softplus_f32(av + p.dt_bias[h]);
-        beta_s = sigmoid_f32(bv);
+        scal_s[3] = -expf(p.A_log[h]) * softplus_f32(gate_a + p.dt_bias[h]);
+        beta_s = sigmoid_f32(gate_b);
     }
     __syncthreads();
     const float n_q = p.q_scale / sqrtf(scal_s[0] + p.l2_eps);
@@ -199,12 +210,12 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Columns of S per workgroup: all of d_v by default (1536 workgroups on the
-// 32 x 48 head decode, all resident at once; measured fastest against 32 and
-// 64); GDN_DECODE_COLS = 32 / 64 / 128 selects another split.
+// Columns of S per workgroup: 64 by default (3072 workgroups on the 32 x 48
+// head decode; measured fastest against 32 and 128); GDN_DECODE_COLS = 32 /
+// 64 / 128 selects another split.
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
-    int cols = p.head_v_dim;
+    int cols = p.head_v_dim < 64 ? p.head_v_dim : 64;
     if (const char* env = getenv("GDN_DECODE_COLS")) {
         const int v = atoi(env);
         if ((v == 32 || v == 64 || v == 128) && v <= p.head_v_dim) cols = v;

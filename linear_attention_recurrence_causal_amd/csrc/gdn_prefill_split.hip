@@ -119,15 +119,24 @@ __device__ __forceinline__ int64_t qk_channel(int ch, int kh, int Hk) {
 }
 
 // Front end of the q, k channels of a chunk -> LDS rows (4 channels x 8 rows
-// per item, one item per thread)
-template <bool INTERIOR>
-__device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm, int b, int kh, int64_t local0,
-                                           int tid) {
-    static_assert(2 * kD / 4 * 8 == kPrepThreads, "one front-end item per thread");
+// per item, one item per thread).  The raw rows are loaded first (by
+// prep_front_load, at the start of the kernel, so that their latency
+// overlaps the set-up), the conv runs once the taps are in LDS.
+static_assert(2 * kD / 4 * 8 == kPrepThreads, "one front-end item per thread");
+
+__device__ __forceinline__ void prep_front_load(const PrefillParams& p, int b, int kh, int64_t local0, bool interior,
+                                                int tid, uint2 raw[11]) {
     const int ch0 = (tid % 64) * 4, tau0 = (tid / 64) * 8;
     const int64_t gc = qk_channel(ch0, kh, p.num_k_heads);
-    uint2 raw[11];
-    conv_load<INTERIOR>(p, b, gc, local0, tau0, raw);
+    if (interior) conv_load<true>(p, b, gc, local0, tau0, raw);
+    else conv_load<false>(p, b, gc, local0, tau0, raw);
+}
+
+template <bool INTERIOR>
+__device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm, int b, int kh, int64_t local0,
+                                           int tid, const uint2 raw[11]) {
+    const int ch0 = (tid % 64) * 4, tau0 = (tid / 64) * 8;
+    const int64_t gc = qk_channel(ch0, kh, p.num_k_heads);
     float w[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) unpack_bf16x4(*reinterpret_cast<const uint2*>(&sm.Ws[t * 2 * kD + ch0]), w[t]);
@@ -150,6 +159,9 @@ void prep_kernel(SplitParams sp) {
     const int b = grp / Hk, kh = grp % Hk;
     const int64_t local0 = (sp.k0 + j) * kC - p.start_pos;
     char* krec = key_rec(sp, b, kh, j);
+    const bool interior = local0 >= 3 && local0 + kC <= p.seq_len;
+    uint2 raw[11];
+    prep_front_load(p, b, kh, local0, interior, tid, raw);
 
     // ---- set-up: gates of every value head of the group (wave hh: head
     // kh r + hh); conv taps -> LDS; zero the upper tiles of P and AN (the
@@ -173,8 +185,8 @@ void prep_kernel(SplitParams sp) {
     __syncthreads();
 
     // ---- front end of q, k
-    if (local0 >= 3 && local0 + kC <= p.seq_len) prep_front<true>(p, sm, b, kh, local0, tid);
-    else prep_front<false>(p, sm, b, kh, local0, tid);
+    if (interior) prep_front<true>(p, sm, b, kh, local0, tid, raw);
+    else prep_front<false>(p, sm, b, kh, local0, tid, raw);
     __syncthreads();
 
     // ---- Q, K -> key record; L2 norms; raw Gram tiles (registers)
