@@ -146,7 +146,26 @@ def bench_decode(args):
         state["i"] = i + 1
 
     t = time_events(step, n, args.warmup * 8)
-    return w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads)
+    # The 100.7 MB state fits the 256 MB Infinity Cache (MALL), so consecutive
+    # steps may find part of it there.  The same step timed alone after a
+    # 512 MiB read that evicts the cache (with clean lines: a write would
+    # leave write-backs competing with the step) measures it from HBM.
+    flush = torch.ones(1 << 27, device="cuda")
+    total = torch.empty((), device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    evs = []
+    for k in range(32):
+        torch.sum(flush, dim=0, out=total)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        step()
+        e1.record(s)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    flushed = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+    del flush, total
+    return w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads), flushed[len(flushed) // 2]
 
 
 def cpu_baseline(inp, tokens):
@@ -227,7 +246,7 @@ def main():
     }
     if not args.no_decode:
         print("bench: decode", file=sys.stderr, flush=True)
-        wd, td, bd = bench_decode(args)
+        wd, td, bd, tf = bench_decode(args)
         rec["decode"] = {
             "workload": "Qwen3.6-27B-shaped GDN layer decode step, B=32, 256 consecutive steps",
             "us_per_step": td * 1e6, "tokens_per_s": wd.batch / td, "bytes_per_step": bd,
@@ -236,6 +255,10 @@ def main():
                          "frac": bd / td / HBM_PEAK_BYTES,
                          "traffic": profiled_traffic("decode_step_kernel_qwen36-27b_decode_b32.md",
                                                      DECODE_SOURCES)},
+            "mall_flushed": {"what": "median of 32 single steps, each after a 512 MiB read that "
+                                     "evicts the 256 MB Infinity Cache",
+                             "us_per_step": tf * 1e6, "achieved": bd / tf / 1e9, "unit": "GB/s",
+                             "frac": bd / tf / HBM_PEAK_BYTES},
         }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
