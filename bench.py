@@ -10,6 +10,8 @@ prefill tokens/s; the fused single-pass kernel is timed beside it.  The same run
 one-token decode step of the Qwen3.6-27B-shaped decode workload (B=32, 256
 consecutive steps, state ~N(0, 0.05)) and reports its HBM bandwidth, and
 times the fp64 CPU oracle on a bounded sample of the prefill workload.
+The multi-token decode step (4 tokens per sequence per call) is timed on the
+decode workload too.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -168,6 +170,33 @@ def bench_decode(args):
     return w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads), flushed[len(flushed) // 2]
 
 
+def bench_decode_multi(args, T=4):
+    """The multi-token step on the same decode workload: T tokens per sequence
+    per call (a speculative-decoding verify step), no snapshots."""
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[1]
+    d = {k: (None if v is None else v.cuda()) for k, v in I.generate(w).items()}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    S = d["rec_state"].clone()
+    cs = [d["conv_state"].clone(), torch.empty_like(d["conv_state"])]
+    out = torch.empty(w.batch, T, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    n = w.decode_steps // T
+    toks = [tuple(d[k][i * T:(i + 1) * T].transpose(0, 1).contiguous() for k in ("dec_qkv", "dec_a", "dec_b"))
+            for i in range(n)]
+    state = {"i": 0}
+
+    def call():
+        i = state["i"]
+        qkv, a, b = toks[i % n]
+        gdn.decode_multi(cfg, qkv, a, b, d["conv_w"], d["A_log"], d["dt_bias"], cs[i % 2], S, out=out,
+                         conv_state_out=cs[(i + 1) % 2], rec_state_out=S)
+        state["i"] = i + 1
+
+    t = time_events(call, n, args.warmup * 4)
+    return w, T, t
+
+
 def cpu_baseline(inp, tokens):
     from linear_attention_recurrence_causal_amd import inputs as I
     from oracle import oracle as O
@@ -260,6 +289,11 @@ def main():
                              "us_per_step": tf * 1e6, "achieved": bd / tf / 1e9, "unit": "GB/s",
                              "frac": bd / tf / HBM_PEAK_BYTES},
         }
+        wm, T, tm = bench_decode_multi(args)
+        rec["decode_multi"] = {
+            "workload": f"the same decode workload, {T} tokens per sequence per call (verify step)",
+            "us_per_call": tm * 1e6, "tokens_per_s": wm.batch * T / tm,
+            "speedup_vs_single_steps": T * td / tm}
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)

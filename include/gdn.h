@@ -164,6 +164,28 @@ gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a
                            const float* rec_state_in, float* rec_state_out, void* out,
                            void* stream);
 
+/* T = num_tokens consecutive decode tokens per sequence in one call, for
+ * multi-token verification in speculative decoding: the same rule as T
+ * calls of gdn_decode_step ("Delta rule", "State"), and bit for bit the same
+ * results, with the state read and written once per call instead of once per
+ * token.
+ *   num_tokens     T, 1 .. 8
+ *   qkv            [B, T, conv_dim] io; a, b [B, T, H_v] io
+ *   out            [B, T, H_v, d_v] io
+ *   conv_state_out, rec_state_out: the states after the last token
+ *   rec_snapshots  [T, B, H_v, d_k, d_v] fp32, or NULL: the recurrent state
+ *                  after each token (roll back to an accepted prefix of t + 1
+ *                  tokens by resuming from snapshot t); 16-byte aligned
+ *   conv_snapshots [T, B, conv_dim, K-1] io, or NULL: the conv tail after
+ *                  each token
+ * The other arguments are those of gdn_decode_step.  The snapshots must not
+ * overlap any other buffer.  GDN_EINVAL for T outside 1 .. 8. */
+gdn_status gdn_decode_multi(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
+                            const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
+                            const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
+                            float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
+                            void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

@@ -225,12 +225,15 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
-gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a, const void* b,
-                           const void* conv_w, const float* A_log, const float* dt_bias,
-                           const void* conv_state_in, void* conv_state_out,
-                           const float* rec_state_in, float* rec_state_out, void* out,
-                           void* stream) {
+// One or several tokens per sequence through the decode kernel (T = 1 is
+// gdn_decode_step); snapshots are optional.
+static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
+                                const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
+                                const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
+                                float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
+                                void* stream) {
     if (gdn_status s = check_config(cfg)) return s;
+    if (num_tokens < 1 || num_tokens > gdn::kMaxDecodeTokens) return GDN_EINVAL;
     // the recurrent states move in 16-byte vectors; everything else needs its
     // element alignment
     const uintptr_t ea = cfg->io_dtype == GDN_BF16 ? 2 : 4;
@@ -238,27 +241,36 @@ gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a
         if (!p || !aligned_to(p, ea)) return GDN_EINVAL;
     if (!A_log || !dt_bias || !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4)) return GDN_EINVAL;
     if (!rec_state_out || !aligned16(rec_state_out) || !aligned16(rec_state_in) ||
-        !aligned_to(conv_state_in, ea))
+        !aligned_to(conv_state_in, ea) || !aligned16(rec_snapshots) || !aligned_to(conv_snapshots, ea))
         return GDN_EINVAL;
     if (cfg->conv_kernel != 4 || !gdn::decode_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype))
         return GDN_EUNSUPPORTED;
 
-    const int64_t B = cfg->batch, Hv = cfg->num_v_heads;
+    const int64_t B = cfg->batch, Hv = cfg->num_v_heads, T = num_tokens;
     const int64_t cd = conv_dim_of(cfg);
     const int ios = io_size(cfg->io_dtype);
     const uint64_t conv_state_bytes = (uint64_t)B * cd * 3 * ios;
     const uint64_t rec_bytes = (uint64_t)B * Hv * cfg->head_k_dim * cfg->head_v_dim * 4;
-    const Range r_qkv = range_of(qkv, (uint64_t)B * cd * ios);
+    const Range r_qkv = range_of(qkv, (uint64_t)B * T * cd * ios);
+    const Range r_a = range_of(a, (uint64_t)B * T * Hv * ios);
+    const Range r_b = range_of(b, (uint64_t)B * T * Hv * ios);
     const Range r_cin = range_of(conv_state_in, conv_state_in ? conv_state_bytes : 0);
     const Range r_cout = range_of(conv_state_out, conv_state_bytes);
     const Range r_rin = range_of(rec_state_in, rec_state_in ? rec_bytes : 0);
     const Range r_rout = range_of(rec_state_out, rec_bytes);
-    const Range r_out = range_of(out, (uint64_t)B * Hv * cfg->head_v_dim * ios);
+    const Range r_out = range_of(out, (uint64_t)B * T * Hv * cfg->head_v_dim * ios);
+    const Range r_rs = range_of(rec_snapshots, rec_snapshots ? T * rec_bytes : 0);
+    const Range r_cs = range_of(conv_snapshots, conv_snapshots ? T * conv_state_bytes : 0);
     if (overlap(r_cout, r_cin) || overlap(r_cout, r_qkv) || overlap(r_cout, r_out)) return GDN_EALIAS;
     if (rec_state_in && rec_state_in != rec_state_out && overlap(r_rin, r_rout)) return GDN_EALIAS;
     if (overlap(r_out, r_qkv) || overlap(r_out, r_rout) || overlap(r_out, r_cin) || overlap(r_out, r_rin))
         return GDN_EALIAS;
     if (overlap(r_rout, r_qkv) || overlap(r_rout, r_cout)) return GDN_EALIAS;
+    // the snapshots are outputs of their own
+    for (const Range& w : {r_rs, r_cs})
+        for (const Range& o : {r_qkv, r_a, r_b, r_cin, r_cout, r_rin, r_rout, r_out})
+            if (overlap(w, o)) return GDN_EALIAS;
+    if (overlap(r_rs, r_cs)) return GDN_EALIAS;
 
     gdn::DecodeParams p{};
     p.qkv = qkv;
@@ -272,6 +284,8 @@ gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a
     p.rec_in = rec_state_in;
     p.rec_out = rec_state_out;
     p.out = out;
+    p.rec_snap = rec_snapshots;
+    p.conv_snap = conv_snapshots;
     p.conv_dim = cd;
     p.batch = cfg->batch;
     p.num_k_heads = cfg->num_k_heads;
@@ -279,10 +293,29 @@ gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a
     p.head_k_dim = cfg->head_k_dim;
     p.head_v_dim = cfg->head_v_dim;
     p.io_dtype = cfg->io_dtype;
+    p.num_tokens = num_tokens;
     p.q_scale = cfg->q_scale;
     p.l2_eps = cfg->l2_eps;
     const hipError_t e = gdn::launch_decode_step(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a, const void* b,
+                           const void* conv_w, const float* A_log, const float* dt_bias,
+                           const void* conv_state_in, void* conv_state_out,
+                           const float* rec_state_in, float* rec_state_out, void* out,
+                           void* stream) {
+    return decode_tokens(cfg, 1, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out, rec_state_in,
+                         rec_state_out, out, nullptr, nullptr, stream);
+}
+
+gdn_status gdn_decode_multi(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
+                            const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
+                            const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
+                            float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
+                            void* stream) {
+    return decode_tokens(cfg, num_tokens, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out,
+                         rec_state_in, rec_state_out, out, rec_snapshots, conv_snapshots, stream);
 }
 
 }  // extern "C"

@@ -34,8 +34,12 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <typename IO, int DK, int NCOL>
-__global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_step_kernel(DecodeParams p) {
+// MAXT: tokens per call the kernel is built for (1: the one-token step,
+// whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
+// multi-token step).  The arithmetic per token is the same in both, so T
+// tokens in one call equal T one-token calls bit for bit.
+template <typename IO, int DK, int NCOL, int MAXT>
+__global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
     constexpr int NRG = kDecodeThreads / NCQ;     // row groups
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_ste
     static_assert(RPT * NRG == DK && NCQ * NRG == kDecodeThreads, "bad decode tiling");
     constexpr int NCH = 2 * DK + NCOL;            // conv channels this slice needs
     constexpr int NWAVES = kDecodeThreads / 64;
-    constexpr int RG_PER_WAVE = 64 / NCQ;
+    constexpr int CPT = (NCH + kDecodeThreads - 1) / kDecodeThreads;   // channels per thread
 
     __shared__ float u_s[NCH];                    // conv+SiLU outputs (io-rounded)
     __shared__ float red_s[2][NWAVES][NCOL];      // cross-wave partial sums
@@ -60,16 +64,21 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_ste
     const int dv = p.head_v_dim;
     const int64_t conv_dim = p.conv_dim;
     const int col0 = z * NCOL;
-
+    const int ntok = MAXT == 1 ? 1 : p.num_tokens;   // the one-token kernel runs straight through
+    float* const rec_snap = MAXT == 1 ? nullptr : p.rec_snap;
+    void* const conv_snap = MAXT == 1 ? nullptr : p.conv_snap;
     const int cq = tid % NCQ;
     const int rg = tid / NCQ;
+    const int wave = tid / 64, lane = tid % 64;
 
-    // ---- 1. front-end inputs of the slice's channels: few bytes, requested
-    // first so that they return (in issue order) ahead of the state and the
-    // conv, norms and gates run while the state is still in flight
-    constexpr int CPT = (NCH + kDecodeThreads - 1) / kDecodeThreads;   // channels per thread
+    // ---- 1. front-end inputs of the slice's channels for every token: few
+    // bytes, requested first so that they return (in issue order) ahead of
+    // the state, and token 0's conv, norms and gates run while the state is
+    // still in flight
     const bool write_qk_tail = (h % r == 0) && (z == 0);
-    float fin[CPT][8];   // conv state (3), current input, taps (4)
+    float hist[CPT][3];              // the last three pre-conv inputs (carried conv state)
+    float taps[CPT][4];
+    float xin[CPT][MAXT];
     int64_t fcs[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -82,22 +91,30 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_ste
             const int64_t cs = ((int64_t)b * conv_dim + c) * 3;
             fcs[k] = cs;
 #pragma unroll
-            for (int j = 0; j < 3; ++j) fin[k][j] = p.conv_in ? T::load(p.conv_in, cs + j) : 0.f;
-            fin[k][3] = T::load(p.qkv, (int64_t)b * conv_dim + c);
+            for (int j = 0; j < 3; ++j) hist[k][j] = p.conv_in ? T::load(p.conv_in, cs + j) : 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fin[k][4 + j] = T::load(p.conv_w, c * 4 + j);
+            for (int t = 0; t < MAXT; ++t)
+                if (t < ntok) xin[k][t] = T::load(p.qkv, ((int64_t)b * ntok + t) * conv_dim + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) taps[k][j] = T::load(p.conv_w, c * 4 + j);
         }
     }
-    float gate_a = 0.f, gate_b = 0.f;
-    const int wave = tid / 64, lane = tid % 64;
+    float gate_a[MAXT], gate_b[MAXT];
     if (wave == 3 && lane == 0) {
-        const int64_t gi = (int64_t)b * p.num_v_heads + h;
-        gate_a = T::load(p.a, gi);
-        gate_b = T::load(p.b, gi);
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t)
+            if (t < ntok) {
+                const int64_t gi = ((int64_t)b * ntok + t) * p.num_v_heads + h;
+                gate_a[t] = T::load(p.a, gi);
+                gate_b[t] = T::load(p.b, gi);
+            }
     }
+    const float neg_A = -expf(p.A_log[h]), dt_h = p.dt_bias[h];
 
-    // ---- 2. the state slice (the bytes that matter)
+    // ---- 2. the state slice (the bytes that matter), kept in registers for
+    // all the tokens
     const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * DK * dv + col0 + cq * 4;
+    const int64_t state_elems = (int64_t)p.batch * p.num_v_heads * DK * dv;
     float4 S[RPT];
     if (p.rec_in) {
 #pragma unroll
@@ -108,105 +125,136 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 ? 7 : 1) void decode_ste
         for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    // conv + SiLU of the slice's channels (io-rounded) and the carried tails
+    for (int t = 0; t < ntok; ++t) {
+        // conv + SiLU of the slice's channels (io-rounded); the carried tail
+        // moves one token on (to this token's conv snapshot, and after the
+        // last token to conv_out)
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        const int i = tid + k * kDecodeThreads;
-        if (i < NCH) {
-            const float* f = fin[k];
-            const float y = fmaf(f[7], f[3], fmaf(f[6], f[2], fmaf(f[5], f[1], f[4] * f[0])));
-            u_s[i] = T::round(silu_f32(y));
-            if (i >= 2 * DK || write_qk_tail) {
-                T::store(p.conv_out, fcs[k] + 0, f[1]);
-                T::store(p.conv_out, fcs[k] + 1, f[2]);
-                T::store(p.conv_out, fcs[k] + 2, f[3]);
+        for (int k = 0; k < CPT; ++k) {
+            const int i = tid + k * kDecodeThreads;
+            if (i < NCH) {
+                float x = xin[k][0];
+#pragma unroll
+                for (int tt = 1; tt < MAXT; ++tt)
+                    if (tt == t) x = xin[k][tt];
+                const float y = fmaf(taps[k][3], x, fmaf(taps[k][2], hist[k][2],
+                                                         fmaf(taps[k][1], hist[k][1], taps[k][0] * hist[k][0])));
+                u_s[i] = T::round(silu_f32(y));
+                hist[k][0] = hist[k][1];
+                hist[k][1] = hist[k][2];
+                hist[k][2] = x;
+                if (i >= 2 * DK || write_qk_tail) {
+                    if (conv_snap) {
+                        const int64_t cs = (int64_t)t * p.batch * conv_dim * 3 + fcs[k];
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) T::store(conv_snap, cs + j, hist[k][j]);
+                    }
+                    if (t == ntok - 1)
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) T::store(p.conv_out, fcs[k] + j, hist[k][j]);
+                }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- 3. norms, k.q and the gates (one wave each, fixed order)
-    if (wave < 3) {
-        float acc = 0.f;
-        for (int i = lane; i < DK; i += 64) {
-            const float qv = u_s[i], kv = u_s[DK + i];
-            acc += wave == 0 ? qv * qv : (wave == 1 ? kv * kv : qv * kv);
+        // ---- 3. norms, k.q and the gates (one wave each, fixed order)
+        if (wave < 3) {
+            float acc = 0.f;
+            for (int i = lane; i < DK; i += 64) {
+                const float qv = u_s[i], kv = u_s[DK + i];
+                acc += wave == 0 ? qv * qv : (wave == 1 ? kv * kv : qv * kv);
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) scal_s[wave] = acc;
+        } else if (lane == 0) {
+            float ga = gate_a[0], gb = gate_b[0];
+#pragma unroll
+            for (int tt = 1; tt < MAXT; ++tt)
+                if (tt == t) { ga = gate_a[tt]; gb = gate_b[tt]; }
+            scal_s[3] = neg_A * softplus_f32(ga + dt_h);
+            beta_s = sigmoid_f32(gb);
         }
-        acc = wave_sum(acc);
-        if (lane == 0) scal_s[wave] = acc;
-    } else if (lane == 0) {
-        scal_s[3] = -expf(p.A_log[h]) * softplus_f32(gate_a + p.dt_bias[h]);
-        beta_s = sigmoid_f32(gate_b);
-    }
-    __syncthreads();
-    const float n_q = p.q_scale / sqrtf(scal_s[0] + p.l2_eps);
-    const float n_k = 1.0f / sqrtf(scal_s[1] + p.l2_eps);
-    const float kq = scal_s[2] * n_q * n_k;        // k_hat . q_hat
-    const float decay = expf(scal_s[3]);
-    const float beta = beta_s;
+        __syncthreads();
+        const float n_q = p.q_scale / sqrtf(scal_s[0] + p.l2_eps);
+        const float n_k = 1.0f / sqrtf(scal_s[1] + p.l2_eps);
+        const float kq = scal_s[2] * n_q * n_k;        // k_hat . q_hat
+        const float decay = expf(scal_s[3]);
+        const float beta = beta_s;
 
-    // ---- 4. S' = exp(g) S; partial S'^T k and S'^T q over this thread's rows
-    float kv[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};
-    float krow[RPT];
+        // ---- 4. S' = exp(g) S; partial S'^T k and S'^T q over this thread's rows
+        float kv[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};
+        float krow[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * NRG;
-        const float kk = u_s[DK + row] * n_k;
-        const float qq = u_s[row] * n_q;
-        krow[i] = kk;
-        S[i].x *= decay; S[i].y *= decay; S[i].z *= decay; S[i].w *= decay;
-        kv[0] = fmaf(S[i].x, kk, kv[0]); kv[1] = fmaf(S[i].y, kk, kv[1]);
-        kv[2] = fmaf(S[i].z, kk, kv[2]); kv[3] = fmaf(S[i].w, kk, kv[3]);
-        oq[0] = fmaf(S[i].x, qq, oq[0]); oq[1] = fmaf(S[i].y, qq, oq[1]);
-        oq[2] = fmaf(S[i].z, qq, oq[2]); oq[3] = fmaf(S[i].w, qq, oq[3]);
-    }
-    // reduce over the row groups of this wave (lanes differing in the rg bits)
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * NRG;
+            const float kk = u_s[DK + row] * n_k;
+            const float qq = u_s[row] * n_q;
+            krow[i] = kk;
+            S[i].x *= decay; S[i].y *= decay; S[i].z *= decay; S[i].w *= decay;
+            kv[0] = fmaf(S[i].x, kk, kv[0]); kv[1] = fmaf(S[i].y, kk, kv[1]);
+            kv[2] = fmaf(S[i].z, kk, kv[2]); kv[3] = fmaf(S[i].w, kk, kv[3]);
+            oq[0] = fmaf(S[i].x, qq, oq[0]); oq[1] = fmaf(S[i].y, qq, oq[1]);
+            oq[2] = fmaf(S[i].z, qq, oq[2]); oq[3] = fmaf(S[i].w, qq, oq[3]);
+        }
+        // reduce over the row groups of this wave (lanes differing in the rg bits)
 #pragma unroll
-    for (int m = NCQ; m < 64; m <<= 1) {
+        for (int m = NCQ; m < 64; m <<= 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kv[j] += __shfl_xor(kv[j], m, 64);
-            oq[j] += __shfl_xor(oq[j], m, 64);
+            for (int j = 0; j < 4; ++j) {
+                kv[j] += __shfl_xor(kv[j], m, 64);
+                oq[j] += __shfl_xor(oq[j], m, 64);
+            }
+        }
+        if (lane < NCQ) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                red_s[0][wave][cq * 4 + j] = kv[j];
+                red_s[1][wave][cq * 4 + j] = oq[j];
+            }
+        }
+        __syncthreads();
+
+        // ---- 5. delta and o per column
+        if (tid < NCOL) {
+            float skv = 0.f, soq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) { skv += red_s[0][w][tid]; soq += red_s[1][w][tid]; }
+            const float vv = u_s[2 * DK + tid];
+            const float d = beta * (vv - skv);
+            delta_s[tid] = d;
+            const int64_t oi = (((int64_t)b * ntok + t) * p.num_v_heads + h) * dv + col0 + tid;
+            T::store(p.out, oi, fmaf(d, kq, soq));
+        }
+        __syncthreads();
+
+        // ---- 6. S = S' + k delta^T (this token's snapshot, if asked for)
+        const float4 dl = *reinterpret_cast<const float4*>(&delta_s[cq * 4]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            S[i].x = fmaf(krow[i], dl.x, S[i].x); S[i].y = fmaf(krow[i], dl.y, S[i].y);
+            S[i].z = fmaf(krow[i], dl.z, S[i].z); S[i].w = fmaf(krow[i], dl.w, S[i].w);
+        }
+        if (rec_snap) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                *reinterpret_cast<float4*>(rec_snap + t * state_elems + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
         }
     }
-    if (lane < NCQ) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            red_s[0][wave][cq * 4 + j] = kv[j];
-            red_s[1][wave][cq * 4 + j] = oq[j];
-        }
-    }
-    (void)RG_PER_WAVE;
-    __syncthreads();
 
-    // ---- 5. delta and o per column
-    if (tid < NCOL) {
-        float skv = 0.f, soq = 0.f;
+    // ---- 7. the state, once
 #pragma unroll
-        for (int w = 0; w < NWAVES; ++w) { skv += red_s[0][w][tid]; soq += red_s[1][w][tid]; }
-        const float vv = u_s[2 * DK + tid];
-        const float d = beta * (vv - skv);
-        delta_s[tid] = d;
-        const int64_t oi = ((int64_t)b * p.num_v_heads + h) * dv + col0 + tid;
-        T::store(p.out, oi, fmaf(d, kq, soq));
-    }
-    __syncthreads();
-
-    // ---- 6. S = S' + k delta^T, written once
-    const float4 dl = *reinterpret_cast<const float4*>(&delta_s[cq * 4]);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        float4 s = S[i];
-        s.x = fmaf(krow[i], dl.x, s.x); s.y = fmaf(krow[i], dl.y, s.y);
-        s.z = fmaf(krow[i], dl.z, s.z); s.w = fmaf(krow[i], dl.w, s.w);
-        *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = s;
-    }
+    for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
 }
 
 template <typename IO, int DK, int NCOL>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
-    hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL>), grid, dim3(kDecodeThreads), 0, stream, p);
+    if (p.num_tokens == 1 && !p.rec_snap && !p.conv_snap)
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1>), grid, dim3(kDecodeThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens>), grid, dim3(kDecodeThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 

@@ -6,10 +6,12 @@
 
 namespace gdn {
 
+constexpr int kMaxDecodeTokens = 8;   // tokens per multi-token decode call
+
 struct DecodeParams {
-    const void* qkv;        // [B, conv_dim] io
-    const void* a;          // [B, H_v] io
-    const void* b;          // [B, H_v] io
+    const void* qkv;        // [B, T, conv_dim] io
+    const void* a;          // [B, T, H_v] io
+    const void* b;          // [B, T, H_v] io
     const void* conv_w;     // [conv_dim, 4] io
     const float* A_log;     // [H_v]
     const float* dt_bias;   // [H_v]
@@ -17,9 +19,12 @@ struct DecodeParams {
     void* conv_out;         // [B, conv_dim, 3] io
     const float* rec_in;    // [B, H_v, d_k, d_v] or null (zeros)
     float* rec_out;         // [B, H_v, d_k, d_v]
-    void* out;              // [B, H_v, d_v] io
+    void* out;              // [B, T, H_v, d_v] io
+    float* rec_snap;        // [T, B, H_v, d_k, d_v] state after each token, or null
+    void* conv_snap;        // [T, B, conv_dim, 3] io conv tail after each token, or null
     int64_t conv_dim;
     int32_t batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, io_dtype;
+    int32_t num_tokens;     // T, 1 .. kMaxDecodeTokens
     float q_scale, l2_eps;
 };
 

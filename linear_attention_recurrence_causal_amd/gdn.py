@@ -58,6 +58,9 @@ _lib.gdn_prefill_chunked.argtypes = [_CFG, _I64, _I64, _P, _P, _P, _P, _P, _P, _
                                      _P, _U64, _I64, _P, _U64, _P]
 _lib.gdn_prefill_chunked.restype = ctypes.c_int32
 _lib.gdn_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.gdn_decode_multi.argtypes = [_CFG, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P]
+_lib.gdn_decode_multi.restype = ctypes.c_int32
 _lib.gdn_decode_step.restype = ctypes.c_int32
 
 lib = _lib
@@ -231,3 +234,52 @@ def decode_step(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=No
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_step")
     return out, conv_state_out, rec_state_out
+
+
+MAX_DECODE_TOKENS = 8
+
+
+def decode_multi(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
+                 rec_state_in=None, *, out=None, conv_state_out=None, rec_state_out=None,
+                 rec_snapshots=None, conv_snapshots=None, snapshots=False, stream=None):
+    """T consecutive tokens per sequence in one call (qkv [B, T, conv_dim]);
+    returns (out [B, T, H_v, d_v], conv_state_out, rec_state_out,
+    rec_snapshots, conv_snapshots).  ``snapshots=True`` allocates the
+    per-token state snapshots ([T, B, H_v, d_k, d_v] and [T, B, conv_dim,
+    K-1]); otherwise they are None unless passed in."""
+    B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
+    io = cfg.torch_io
+    if qkv.dim() != 3:
+        raise ValueError(f"qkv must be [B, T, conv_dim], got {tuple(qkv.shape)}")
+    T = qkv.shape[1]
+    _check(qkv, "qkv", (B, T, cfg.conv_dim), io)
+    _check(a, "a", (B, T, Hv), io)
+    _check(b, "b", (B, T, Hv), io)
+    _check(conv_w, "conv_w", (cfg.conv_dim, cfg.conv_kernel), io)
+    _check(A_log, "A_log", (Hv,), torch.float32)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _check(conv_state_in, "conv_state_in", (B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
+    dev = qkv.device
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    if rec_state_out is None:
+        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if snapshots and rec_snapshots is None:
+        rec_snapshots = torch.empty((T, B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if snapshots and conv_snapshots is None:
+        conv_snapshots = torch.empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    _check(out, "out", (B, T, Hv, dv), io)
+    _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
+    _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
+    _check(rec_snapshots, "rec_snapshots", (T, B, Hv, dk, dv), torch.float32, True)
+    _check(conv_snapshots, "conv_snapshots", (T, B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    st = _lib.gdn_decode_multi(ctypes.byref(cfg.c()), T, _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out),
+                               _ptr(rec_state_in), _ptr(rec_state_out), _ptr(out), _ptr(rec_snapshots),
+                               _ptr(conv_snapshots), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_multi")
+    return out, conv_state_out, rec_state_out, rec_snapshots, conv_snapshots

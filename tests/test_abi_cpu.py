@@ -166,3 +166,28 @@ def test_decode_rejects_bad_arguments(G):
     assert call(cfg(G), cin=P(FAKE * 7)) == G.GDN_EALIAS
     # a partial overlap of the recurrent states is refused, exact equality is in place
     assert call(cfg(G), rin=P(FAKE * 8 + 256)) == G.GDN_EALIAS
+
+
+def test_decode_multi_rejects_bad_arguments(G):
+    P = ctypes.c_void_p
+    f = G.lib.gdn_decode_multi
+    def call(c, T=4, **over):
+        args = dict(qkv=P(FAKE), a=P(FAKE * 2), b=P(FAKE * 3), conv_w=P(FAKE * 4),
+                    A_log=P(FAKE * 5), dt_bias=P(FAKE * 6), cin=None, cout=P(FAKE * 7),
+                    rin=None, rout=P(FAKE * 8), out=P(FAKE * 9), rsnap=None, csnap=None, stream=None)
+        args.update(over)
+        return f(ctypes.byref(c.c()), T, *args.values())
+    assert call(cfg(G), T=0) == G.GDN_EINVAL
+    assert call(cfg(G), T=G.MAX_DECODE_TOKENS + 1) == G.GDN_EINVAL
+    assert call(cfg(G), T=-3) == G.GDN_EINVAL
+    assert call(cfg(G), qkv=None) == G.GDN_EINVAL
+    assert call(cfg(G), rsnap=P(FAKE * 10 + 8)) == G.GDN_EINVAL      # snapshots need 16 bytes
+    assert call(cfg(G, io_dtype=G.GDN_BF16), csnap=P(FAKE * 11 + 1)) == G.GDN_EINVAL
+    assert call(cfg(G, head_k_dim=96)) == G.GDN_EUNSUPPORTED
+    # the token-major inputs span T tokens: out starting one token into qkv overlaps it
+    c = cfg(G)
+    assert call(c, T=4, out=P(FAKE + c.conv_dim * 2)) == G.GDN_EALIAS
+    # snapshots overlapping an input or each other
+    assert call(c, rsnap=P(FAKE * 8)) == G.GDN_EALIAS
+    assert call(c, csnap=P(FAKE * 3)) == G.GDN_EALIAS
+    assert call(c, rsnap=P(FAKE * 12), csnap=P(FAKE * 12 + 1024)) == G.GDN_EALIAS
