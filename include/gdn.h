@@ -145,7 +145,13 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
  *                 NULL / 0 selects the fused path.
  * With seq_len == 0 only the states are copied (qkv, a, b, out may be NULL).
  * The conv+SiLU output is rounded to the io dtype before the L2 norm, as the
- * stream it comes from is stored in that dtype. */
+ * stream it comes from is stored in that dtype.
+ * The diagonal 16x16 blocks of (I + A)^-1 are formed by forward substitution
+ * (the "direct solve" of the Qwen3.6-27B PR, "Known limitations and
+ * follow-ups").  On the two-pass path the environment variable
+ * GDN_DIAG_SOLVE=neumann selects the product form of the Neumann series
+ * instead (the faster-style variant the same passage names), read at each
+ * call; it is less accurate where keys nearly coincide. */
 gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
                                const void* qkv, const void* a, const void* b, const void* conv_w,
                                const float* A_log, const float* dt_bias,

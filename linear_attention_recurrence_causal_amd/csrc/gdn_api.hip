@@ -220,6 +220,10 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     p.num_v_heads = cfg->num_v_heads;
     p.q_scale = cfg->q_scale;
     p.l2_eps = cfg->l2_eps;
+    // GDN_DIAG_SOLVE=neumann: two-pass path, diagonal-block inverses by the
+    // Neumann product instead of substitution
+    const char* solve_env = getenv("GDN_DIAG_SOLVE");
+    p.diag_neumann = solve_env && solve_env[0] == 'n';
     const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream))
                                   : gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;

@@ -321,6 +321,50 @@ __device__ __forceinline__ void diag_solve(SM& sm, int lane) {
         sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
 }
 
+// fp32 16x16 product on v_mfma_f32_16x16x4_f32 in the accumulator layout:
+// lane l = (n = l % 16, q = l / 16), element e holds M[4q + e][n].  Step s
+// takes reduction index 4q + s, so the A operand is element s of the left
+// factor's transpose and the B operand element s of the right factor.
+__device__ __forceinline__ f32x4 mm16_f32(f32x4 leftT, f32x4 right, f32x4 acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(leftT[s], right[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// The same diagonal-block inverse as diag_solve, by the faster form the
+// Qwen3.6-27B PR names beside the direct solve ("Known limitations and
+// follow-ups"): with X = -A_mm strictly lower triangular, X^16 = 0 and
+//   (I + A_mm)^-1 = sum_{k<16} X^k = (I + X)(I + X^2)(I + X^4)(I + X^8),
+// four squarings and three multiply-adds instead of a 15-step dependent
+// chain.  One wave per block m.  Every factor is a polynomial in X, so the
+// factors commute; each is kept with its transpose for use as a left
+// factor.  Exact in exact arithmetic; in fp32 the powers X^k can be far
+// larger than the inverse (keys that nearly coincide, beta near 1, slow
+// decay), and their rounding then survives the cancellation.
+template <class SM>
+__device__ __forceinline__ void diag_neumann(SM& sm, int m, int lane) {
+    const int n = lane % 16, q = lane / 16;
+    const float* At = sm.AdT + m * 16 * kXLd;   // At[i * kXLd + r] = A_mm[r][i]
+    f32x4 X, XT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        X[e] = -At[n * kXLd + 4 * q + e];
+        XT[e] = -At[(4 * q + e) * kXLd + n];
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 X2 = mm16_f32(XT, X, z), X2T = mm16_f32(X, XT, z);
+    const f32x4 X4 = mm16_f32(X2T, X2, z), X4T = mm16_f32(X2, X2T, z);
+    f32x4 R = mm16_f32(X4T, X4, z);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R[e] += 4 * q + e == n ? 1.f : 0.f;
+    R = mm16_f32(X4T, R, R);
+    R = mm16_f32(X2T, R, R);
+    R = mm16_f32(XT, R, R);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        sm.AN[(16 * m + 4 * q + e) * kKtLd + pos(16 * m + n)] = __bf16(4 * q + e > n ? R[e] : 0.f);
+}
+
 // Blocked forward substitution for Delta of one wave's 16 columns:
 // (I + A) Delta = R over the four 16-row blocks, Y_m = R_m - sum_{k<m} A_mk
 // Delta_k, Delta_m = Y_m + N_mm Y_m.  The fp32 accumulator carries R and Y

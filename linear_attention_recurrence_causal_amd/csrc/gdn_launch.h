@@ -47,6 +47,7 @@ struct PrefillParams {
     int64_t seq_len, start_pos, conv_dim;
     int32_t batch, num_k_heads, num_v_heads;
     float q_scale, l2_eps;
+    int32_t diag_neumann;   // two-pass path: diagonal-block inverses by the Neumann product
 };
 
 bool decode_supported(int head_k_dim, int head_v_dim, int io_dtype);

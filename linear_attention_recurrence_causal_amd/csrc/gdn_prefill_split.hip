@@ -147,6 +147,7 @@ __device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm,
     for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
 }
 
+template <bool NEUMANN>
 __global__ __launch_bounds__(kPrepThreads)
 void prep_kernel(SplitParams sp) {
     const PrefillParams& p = sp.p;
@@ -222,10 +223,15 @@ void prep_kernel(SplitParams sp) {
             if (lane == 0) sm.tokS[4][0] = expf(sm.gam[hh][kC - 1]);
         }
         __syncthreads();
-        if (wave == 0) {
-            diag_solve<true>(hv, lane);
+        // diagonal inverses on wave 0 (substitution) or waves 0..3 (one
+        // block each, Neumann product) while the other waves copy P and the
+        // row scales
+        constexpr int kSolveWaves = NEUMANN ? 4 : 1;
+        if (wave < kSolveWaves) {
+            if (NEUMANN) diag_neumann(hv, wave, lane);
+            else diag_solve<true>(hv, lane);
         } else {
-            for (int e = tid - 64; e < kC * 8 + kTokBytes / 16; e += kPrepThreads - 64) {
+            for (int e = tid - 64 * kSolveWaves; e < kC * 8 + kTokBytes / 16; e += kPrepThreads - 64 * kSolveWaves) {
                 if (e < kC * 8) copy16(vrec + kRecP + (e >> 3) * 128 + 16 * (e & 7), sm.Ps + (e >> 3) * kKtLd + 8 * (e & 7));
                 else copy16(vrec + kRecTok + 16 * (e - kC * 8), &sm.tokS[0][0] + 4 * (e - kC * 8));
             }
@@ -815,7 +821,9 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         sp.k0 = k0;
         sp.nseg = (int32_t)n;
         sp.last_seg = k0 + n == k_end;
-        hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(p.batch * p.num_k_heads * n)), dim3(kPrepThreads), 0, stream, sp);
+        const dim3 grid((unsigned)(p.batch * p.num_k_heads * n));
+        if (p.diag_neumann) hipLaunchKernelGGL(prep_kernel<true>, grid, dim3(kPrepThreads), 0, stream, sp);
+        else hipLaunchKernelGGL(prep_kernel<false>, grid, dim3(kPrepThreads), 0, stream, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_any(sp, stream);

@@ -59,6 +59,7 @@ class Workload:
     dt_std: float = 0.1
     conv_std: float = 1.0
     rec_std: float = 0.05
+    key_common: float = 0.0  # weight of one shared direction per (sequence, key head) in k
 
     @property
     def conv_dim(self) -> int:
@@ -95,6 +96,15 @@ def slow_decay(w: Workload) -> Workload:
 def extreme_gates(w: Workload) -> Workload:
     """a, b shifted to about +-30 so softplus / sigmoid sit in their tails."""
     return w.with_(ab_std=1.0, a_shift=30.0, b_shift=-30.0, name=w.name + "-extreme")
+
+
+def coincident_keys(w: Workload) -> Workload:
+    """Keys that nearly coincide (a shared direction of weight 10 against unit
+    noise in every k channel, cosine about 0.99 after conv and norm), beta
+    near 1 (b shifted by +8) and slow decay: the intra-chunk matrix A then
+    has entries near 1 and its powers grow binomially, the hard case of a
+    series form of (I + A)^-1."""
+    return slow_decay(w).with_(key_common=10.0, b_shift=8.0, name=w.name + "-coincident")
 
 
 def _randn(gen, shape, std, dtype):
@@ -136,6 +146,11 @@ def generate(w: Workload, seed: int | None = None) -> dict:
         dec_qkv = _randn(gen, (S, B, w.conv_dim), w.qkv_std, io)
         dec_a = (_randn(gen, (S, B, Hv), w.ab_std, torch.float32) + w.a_shift).to(io)
         dec_b = (_randn(gen, (S, B, Hv), w.ab_std, torch.float32) + w.b_shift).to(io)
+    if w.key_common:
+        # drawn last, so the other inputs match the workload without it
+        kd = w.num_k_heads * w.head_k_dim
+        base = _randn(gen, (B, 1, kd), w.key_common, torch.float32)
+        qkv[:, :, kd:2 * kd] = (qkv[:, :, kd:2 * kd].float() + base).to(io)
     return dict(qkv=qkv, a=a, b=b_, conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
                 conv_state=conv_state, rec_state=rec_state, dec_qkv=dec_qkv, dec_a=dec_a,
                 dec_b=dec_b)
