@@ -11,7 +11,8 @@ one-token decode step of the Qwen3.6-27B-shaped decode workload (B=32, 256
 consecutive steps, state ~N(0, 0.05)) and reports its HBM bandwidth, and
 times the fp64 CPU oracle on a bounded sample of the prefill workload.
 The multi-token decode step (4 tokens per sequence per call) is timed on the
-decode workload too.
+decode workload too, and so is the output gate (RMSNormGated with z): on its
+own over the prefill output shape, and fused into the decode step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -197,6 +198,63 @@ def bench_decode_multi(args, T=4):
     return w, T, t
 
 
+def bench_output_gate(args):
+    """The output gate (RMSNormGated of the core output with z) standalone on
+    the prefill output shape [16384, 48, 128] bf16, and fused into the decode
+    step of the decode workload (y only, no ungated out)."""
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[2]
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    gen = torch.Generator().manual_seed(5)
+    o = torch.randn((w.seq_len, w.num_v_heads, 128), generator=gen).to(torch.bfloat16).cuda()
+    gi = I.gate_inputs(w, (w.seq_len,))
+    z, nw = gi["z"].cuda(), gi["norm_w"].cuda()
+    y = torch.empty_like(o)
+    t = time_events(lambda: gdn.output_gate(cfg, o, z, nw, y=y), args.steps * 4, args.warmup)
+    gate_bytes = 3 * o.numel() * 2 + 128 * 2
+    del o, z, y
+
+    wd = I.WORKLOADS[1]
+    d = {k: (None if v is None else v.cuda()) for k, v in I.generate(wd).items()}
+    cfgd = gdn.Config(batch=wd.batch, num_k_heads=wd.num_k_heads, num_v_heads=wd.num_v_heads)
+    gd = I.gate_inputs(wd, (wd.decode_steps, wd.batch))
+    zd, nwd = gd["z"].cuda(), gd["norm_w"].cuda()
+    S = d["rec_state"].clone()
+    cs = [d["conv_state"].clone(), torch.empty_like(d["conv_state"])]
+    yd = torch.empty(wd.batch, 1, wd.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    n = wd.decode_steps
+    toks = [tuple(d[k][i:i + 1].transpose(0, 1).contiguous() for k in ("dec_qkv", "dec_a", "dec_b"))
+            + (zd[i].unsqueeze(1).contiguous(),) for i in range(n)]
+    state = {"i": 0}
+
+    def step():
+        i = state["i"]
+        qkv, a, b, zz = toks[i % n]
+        gdn.decode_gated(cfgd, qkv, a, b, d["conv_w"], d["A_log"], d["dt_bias"], zz, nwd, cs[i % 2], S,
+                         y=yd, conv_state_out=cs[(i + 1) % 2], rec_state_out=S)
+        state["i"] = i + 1
+
+    td = time_events(step, n, args.warmup * 8)
+    dec_bytes = decode_bytes(wd.batch, wd.num_k_heads, wd.num_v_heads) + wd.batch * wd.num_v_heads * 128 * 2
+    return {
+        "standalone": {"workload": "gdn_output_gate on a [16384, 48, 128] bf16 core output",
+                       "us_per_call": t * 1e6,
+                       "roofline": {"kernel": "output_gate_kernel", "bound": "hbm",
+                                    "achieved": gate_bytes / t / 1e9, "peak": HBM_PEAK_BYTES / 1e9,
+                                    "unit": "GB/s", "frac": gate_bytes / t / HBM_PEAK_BYTES,
+                                    "bytes_per_launch": gate_bytes}},
+        "fused_decode": {"workload": "gdn_decode_gated, B=32 decode workload, 256 consecutive steps, "
+                                    "y only",
+                         "us_per_step": td * 1e6, "tokens_per_s": wd.batch / td,
+                         "bytes_per_step": dec_bytes,
+                         "roofline": {"kernel": "decode_step_kernel (gated, 128 columns per workgroup)",
+                                      "bound": "hbm", "achieved": dec_bytes / td / 1e9,
+                                      "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
+                                      "frac": dec_bytes / td / HBM_PEAK_BYTES}},
+    }
+
+
 def cpu_baseline(inp, tokens):
     from linear_attention_recurrence_causal_amd import inputs as I
     from oracle import oracle as O
@@ -294,6 +352,8 @@ def main():
             "workload": f"the same decode workload, {T} tokens per sequence per call (verify step)",
             "us_per_call": tm * 1e6, "tokens_per_s": wm.batch * T / tm,
             "speedup_vs_single_steps": T * td / tm}
+        print("bench: output gate", file=sys.stderr, flush=True)
+        rec["output_gate"] = bench_output_gate(args)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)

@@ -192,6 +192,42 @@ gdn_status gdn_decode_multi(const gdn_config* cfg, int32_t num_tokens, const voi
                             float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
                             void* stream);
 
+/* gdn_decode_multi with the output gate of gdn_output_gate fused in: y is
+ * formed per token and value head from the fp32 core output before it is
+ * rounded, by a workgroup that owns all d_v columns of its head.
+ *   out        [B, T, H_v, d_v] io, or NULL to write only y
+ *   z          [B, T, H_v, d_v] io, the gate input
+ *   norm_w     [d_v] io
+ *   gate_eps   >= 0, finite
+ *   y          [B, T, H_v, d_v] io, the gated output (required); must not
+ *              overlap any other buffer
+ * The other arguments and the T-token semantics are those of
+ * gdn_decode_multi; out, states and snapshots are bitwise those of
+ * gdn_decode_multi run with all d_v columns per workgroup (the environment
+ * variable GDN_DECODE_COLS = d_v), whose row sums are taken in the same
+ * order.  Supported: d_v in {32, 64, 128}. */
+gdn_status gdn_decode_gated(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
+                            const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
+                            const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
+                            float* rec_state_out, void* out, const void* z, const void* norm_w, float gate_eps,
+                            void* y, float* rec_snapshots, void* conv_snapshots, void* stream);
+
+/* Output gate of the block ("Output": RMSNormGated of the core output with
+ * the gate z, before out_proj), per token and value head over d_v:
+ *   y = norm_w * o / sqrt(mean(o^2) + eps) * silu(z)
+ * in fp32, rounded once to the io dtype.
+ *   num_tokens  rows of the token axis (B * L for a prefill output,
+ *               B * T for a decode output), >= 0
+ *   o, z, y     [num_tokens, H_v, d_v] io, 16-byte aligned; y may equal o
+ *               or z exactly (in place), no other overlap
+ *   norm_w      [d_v] io, 16-byte aligned
+ *   eps         >= 0, finite (the models use 1e-6)
+ * Supported: d_v in {32, 64, 128}, io GDN_F32 or GDN_BF16.  Only
+ * cfg->num_v_heads, head_v_dim and io_dtype are used (the rest of cfg must
+ * still be valid). */
+gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void* o, const void* z,
+                           const void* norm_w, float eps, void* y, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

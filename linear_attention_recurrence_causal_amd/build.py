@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill.hip", "gdn_prefill_split.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_gate.hip", "gdn_prefill.hip", "gdn_prefill_split.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 

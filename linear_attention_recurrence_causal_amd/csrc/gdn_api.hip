@@ -229,20 +229,36 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
+// Output gate arguments of a decode call (y == NULL: no gate).
+struct DecodeGate {
+    const void* z = nullptr;
+    const void* norm_w = nullptr;
+    float eps = 0.f;
+    void* y = nullptr;
+};
+
 // One or several tokens per sequence through the decode kernel (T = 1 is
-// gdn_decode_step); snapshots are optional.
+// gdn_decode_step); snapshots and the output gate are optional.  With the
+// gate, out may be NULL.
 static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
                                 const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
                                 const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
                                 float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
-                                void* stream) {
+                                const DecodeGate& gate, void* stream) {
     if (gdn_status s = check_config(cfg)) return s;
     if (num_tokens < 1 || num_tokens > gdn::kMaxDecodeTokens) return GDN_EINVAL;
     // the recurrent states move in 16-byte vectors; everything else needs its
     // element alignment
     const uintptr_t ea = cfg->io_dtype == GDN_BF16 ? 2 : 4;
-    for (const void* p : {qkv, a, b, conv_w, (const void*)conv_state_out, (const void*)out})
+    const bool gated = gate.y != nullptr;
+    for (const void* p : {qkv, a, b, conv_w, (const void*)conv_state_out})
         if (!p || !aligned_to(p, ea)) return GDN_EINVAL;
+    if ((!out && !gated) || !aligned_to(out, ea)) return GDN_EINVAL;
+    if (gated) {
+        for (const void* p : {gate.z, gate.norm_w, (const void*)gate.y})
+            if (!p || !aligned_to(p, ea)) return GDN_EINVAL;
+        if (!std::isfinite(gate.eps) || gate.eps < 0.f) return GDN_EINVAL;
+    }
     if (!A_log || !dt_bias || !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4)) return GDN_EINVAL;
     if (!rec_state_out || !aligned16(rec_state_out) || !aligned16(rec_state_in) ||
         !aligned_to(conv_state_in, ea) || !aligned16(rec_snapshots) || !aligned_to(conv_snapshots, ea))
@@ -262,7 +278,9 @@ static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const
     const Range r_cout = range_of(conv_state_out, conv_state_bytes);
     const Range r_rin = range_of(rec_state_in, rec_state_in ? rec_bytes : 0);
     const Range r_rout = range_of(rec_state_out, rec_bytes);
-    const Range r_out = range_of(out, (uint64_t)B * T * Hv * cfg->head_v_dim * ios);
+    const uint64_t out_bytes = (uint64_t)B * T * Hv * cfg->head_v_dim * ios;
+    const Range r_out = range_of(out, out ? out_bytes : 0);
+    const Range r_y = range_of(gate.y, gated ? out_bytes : 0);
     const Range r_rs = range_of(rec_snapshots, rec_snapshots ? T * rec_bytes : 0);
     const Range r_cs = range_of(conv_snapshots, conv_snapshots ? T * conv_state_bytes : 0);
     if (overlap(r_cout, r_cin) || overlap(r_cout, r_qkv) || overlap(r_cout, r_out)) return GDN_EALIAS;
@@ -275,6 +293,14 @@ static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const
         for (const Range& o : {r_qkv, r_a, r_b, r_cin, r_cout, r_rin, r_rout, r_out})
             if (overlap(w, o)) return GDN_EALIAS;
     if (overlap(r_rs, r_cs)) return GDN_EALIAS;
+    if (gated) {
+        const Range r_z = range_of(gate.z, out_bytes);
+        const Range r_w = range_of(gate.norm_w, (uint64_t)cfg->head_v_dim * ios);
+        for (const Range& o : {r_qkv, r_a, r_b, r_cin, r_cout, r_rin, r_rout, r_out, r_rs, r_cs, r_z, r_w})
+            if (overlap(r_y, o)) return GDN_EALIAS;
+        for (const Range& w : {r_out, r_cout, r_rout, r_rs, r_cs})
+            if (overlap(w, r_z) || overlap(w, r_w)) return GDN_EALIAS;
+    }
 
     gdn::DecodeParams p{};
     p.qkv = qkv;
@@ -290,6 +316,10 @@ static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const
     p.out = out;
     p.rec_snap = rec_snapshots;
     p.conv_snap = conv_snapshots;
+    p.gate_z = gate.z;
+    p.gate_w = gate.norm_w;
+    p.gate_y = gate.y;
+    p.gate_eps = gate.eps;
     p.conv_dim = cd;
     p.batch = cfg->batch;
     p.num_k_heads = cfg->num_k_heads;
@@ -310,7 +340,7 @@ gdn_status gdn_decode_step(const gdn_config* cfg, const void* qkv, const void* a
                            const float* rec_state_in, float* rec_state_out, void* out,
                            void* stream) {
     return decode_tokens(cfg, 1, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out, rec_state_in,
-                         rec_state_out, out, nullptr, nullptr, stream);
+                         rec_state_out, out, nullptr, nullptr, DecodeGate{}, stream);
 }
 
 gdn_status gdn_decode_multi(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
@@ -319,7 +349,55 @@ gdn_status gdn_decode_multi(const gdn_config* cfg, int32_t num_tokens, const voi
                             float* rec_state_out, void* out, float* rec_snapshots, void* conv_snapshots,
                             void* stream) {
     return decode_tokens(cfg, num_tokens, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out,
-                         rec_state_in, rec_state_out, out, rec_snapshots, conv_snapshots, stream);
+                         rec_state_in, rec_state_out, out, rec_snapshots, conv_snapshots, DecodeGate{}, stream);
+}
+
+gdn_status gdn_decode_gated(const gdn_config* cfg, int32_t num_tokens, const void* qkv, const void* a,
+                            const void* b, const void* conv_w, const float* A_log, const float* dt_bias,
+                            const void* conv_state_in, void* conv_state_out, const float* rec_state_in,
+                            float* rec_state_out, void* out, const void* z, const void* norm_w, float gate_eps,
+                            void* y, float* rec_snapshots, void* conv_snapshots, void* stream) {
+    if (!y) return GDN_EINVAL;
+    if (gdn_status s = check_config(cfg)) return s;
+    if (!gdn::gate_supported(cfg->head_v_dim, cfg->io_dtype)) return GDN_EUNSUPPORTED;
+    DecodeGate gate;
+    gate.z = z;
+    gate.norm_w = norm_w;
+    gate.eps = gate_eps;
+    gate.y = y;
+    return decode_tokens(cfg, num_tokens, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out,
+                         rec_state_in, rec_state_out, out, rec_snapshots, conv_snapshots, gate, stream);
+}
+
+gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void* o, const void* z,
+                           const void* norm_w, float eps, void* y, void* stream) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (num_tokens < 0 || !std::isfinite(eps) || eps < 0.f) return GDN_EINVAL;
+    if (!gdn::gate_supported(cfg->head_v_dim, cfg->io_dtype)) return GDN_EUNSUPPORTED;
+    const int64_t rows = num_tokens * cfg->num_v_heads;
+    // the grid (at least 64 rows per workgroup) stays below 2^31 workgroups
+    if (num_tokens > ((int64_t)1 << 36) / cfg->num_v_heads) return GDN_EUNSUPPORTED;
+    if (!norm_w || !aligned16(norm_w)) return GDN_EINVAL;
+    if (rows > 0 && (!o || !z || !y)) return GDN_EINVAL;
+    if (!aligned16(o) || !aligned16(z) || !aligned16(y)) return GDN_EINVAL;
+    const int ios = io_size(cfg->io_dtype);
+    const uint64_t bytes = (uint64_t)rows * cfg->head_v_dim * ios;
+    const Range r_o = range_of(o, bytes), r_z = range_of(z, bytes), r_y = range_of(y, bytes);
+    const Range r_w = range_of(norm_w, (uint64_t)cfg->head_v_dim * ios);
+    // in place over o or z is allowed (each element is read before it is written)
+    if ((y != o && overlap(r_y, r_o)) || (y != z && overlap(r_y, r_z)) || overlap(r_y, r_w)) return GDN_EALIAS;
+
+    gdn::GateParams p{};
+    p.o = o;
+    p.z = z;
+    p.norm_w = norm_w;
+    p.y = y;
+    p.rows = rows;
+    p.head_v_dim = cfg->head_v_dim;
+    p.io_dtype = cfg->io_dtype;
+    p.eps = eps;
+    const hipError_t e = gdn::launch_output_gate(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
 }  // extern "C"

@@ -89,12 +89,6 @@ __device__ __forceinline__ void unpack_bf16x4(uint2 raw, float x[4]) {
     x[3] = bf16_bits_to_f32(raw.y >> 16);
 }
 
-// SiLU with the hardware exp2 and reciprocal (about 2 ulp of fp32; the
-// result is rounded to bf16 right after).
-__device__ __forceinline__ float silu_fast(float y) {
-    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
-}
-
 // Pre-conv inputs of channels gc..gc+3 at call-local token t < 0: the
 // carried conv state for t >= -3 (zeros for a new request), else zeros.
 __device__ __forceinline__ void load_x4_state(const PrefillParams& p, int b, int64_t t, int64_t gc,

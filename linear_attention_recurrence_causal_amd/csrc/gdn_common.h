@@ -68,6 +68,12 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + ex
 
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
 
+// SiLU with the hardware exp2 and reciprocal (about 2 ulp of fp32), for
+// results that are rounded to bf16 or scaled further right after.
+__device__ __forceinline__ float silu_fast(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
+
 // Wave-wide (64 lanes) butterfly sum; every lane gets the total.  The order of
 // additions is fixed, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -17,6 +17,11 @@
 // independent given (q, k, beta, g), so slicing d_v multiplies parallelism;
 // each slice recomputes the (cheap) conv of its head's q and k channels.
 //
+// With the output gate (GATE; "Output": RMSNormGated(o, z), per token and
+// head over d_v) a workgroup owns all d_v columns of its head, so the row's
+// sum of squares stays on chip and y = w o / sqrt(mean(o^2) + eps) silu(z)
+// is formed from the fp32 o before any rounding.
+//
 // Thread layout (256 threads): thread = (cq, rg), cq = column quad (4
 // consecutive fp32 columns = one 16-byte load), rg = row group; thread owns
 // rows rg, rg + NRG, ... so that for each row step the whole workgroup reads
@@ -37,9 +42,10 @@ constexpr int kDecodeThreads = 256;
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
 // whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
 // multi-token step).  The arithmetic per token is the same in both, so T
-// tokens in one call equal T one-token calls bit for bit.
-template <typename IO, int DK, int NCOL, int MAXT>
-__global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) void decode_step_kernel(DecodeParams p) {
+// tokens in one call equal T one-token calls bit for bit.  GATE: also write
+// the gated output (NCOL must be d_v).
+template <typename IO, int DK, int NCOL, int MAXT, bool GATE>
+__global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))) void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
     constexpr int NRG = kDecodeThreads / NCQ;     // row groups
@@ -54,6 +60,7 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) vo
     __shared__ __align__(16) float delta_s[NCOL];
     __shared__ float scal_s[4];                   // n_q, n_k, k.q (unnormalised), g
     __shared__ float beta_s;
+    __shared__ float gsum_s[NWAVES];              // gate: per-wave sums of o^2
 
     const int tid = threadIdx.x;
     const int z = blockIdx.x;                     // column slice
@@ -110,6 +117,14 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) vo
             }
     }
     const float neg_A = -expf(p.A_log[h]), dt_h = p.dt_bias[h];
+    // gate inputs of this thread's column (threads tid < NCOL = d_v)
+    float zin[MAXT], gw = 0.f;
+    if (GATE && tid < NCOL) {
+        gw = T::load(p.gate_w, tid);
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t)
+            if (t < ntok) zin[t] = T::load(p.gate_z, (((int64_t)b * ntok + t) * p.num_v_heads + h) * dv + tid);
+    }
 
     // ---- 2. the state slice (the bytes that matter), kept in registers for
     // all the tokens
@@ -215,6 +230,8 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) vo
         __syncthreads();
 
         // ---- 5. delta and o per column
+        const int64_t oi = (((int64_t)b * ntok + t) * p.num_v_heads + h) * dv + col0 + tid;
+        float o = 0.f;
         if (tid < NCOL) {
             float skv = 0.f, soq = 0.f;
 #pragma unroll
@@ -222,10 +239,26 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) vo
             const float vv = u_s[2 * DK + tid];
             const float d = beta * (vv - skv);
             delta_s[tid] = d;
-            const int64_t oi = (((int64_t)b * ntok + t) * p.num_v_heads + h) * dv + col0 + tid;
-            T::store(p.out, oi, fmaf(d, kq, soq));
+            o = fmaf(d, kq, soq);
+            if (!GATE || p.out) T::store(p.out, oi, o);
+        }
+        if (GATE) {
+            // sum of o^2 over the head's d_v columns (waves 0 .. NCOL/64)
+            const float sq = wave_sum(o * o);
+            if (lane == 0) gsum_s[wave] = sq;
         }
         __syncthreads();
+        if (GATE && tid < NCOL) {
+            float ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < (NCOL + 63) / 64; ++w) ss += gsum_s[w];
+            float zt = zin[0];
+#pragma unroll
+            for (int tt = 1; tt < MAXT; ++tt)
+                if (tt == t) zt = zin[tt];
+            const float inv = 1.0f / sqrtf(ss * (1.0f / NCOL) + p.gate_eps);
+            T::store(p.gate_y, oi, gw * (o * inv) * silu_f32(zt));
+        }
 
         // ---- 6. S = S' + k delta^T (this token's snapshot, if asked for)
         const float4 dl = *reinterpret_cast<const float4*>(&delta_s[cq * 4]);
@@ -247,31 +280,39 @@ __global__ __launch_bounds__(kDecodeThreads, NCOL == 64 && MAXT == 1 ? 7 : 1) vo
         *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
 }
 
-template <typename IO, int DK, int NCOL>
+template <typename IO, int DK, int NCOL, bool GATE>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
     if (p.num_tokens == 1 && !p.rec_snap && !p.conv_snap)
-        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1>), grid, dim3(kDecodeThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1, GATE>), grid, dim3(kDecodeThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens>), grid, dim3(kDecodeThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens, GATE>), grid, dim3(kDecodeThreads),
+                           0, stream, p);
     return hipGetLastError();
 }
 
 // Columns of S per workgroup: 64 by default (3072 workgroups on the 32 x 48
 // head decode; measured fastest against 32 and 128); GDN_DECODE_COLS = 32 /
-// 64 / 128 selects another split.
+// 64 / 128 selects another split.  The gated step takes all d_v columns.
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
+    if (p.gate_y) {
+        switch (p.head_v_dim) {
+            case 32: return launch_typed<IO, DK, 32, true>(p, stream);
+            case 64: return launch_typed<IO, DK, 64, true>(p, stream);
+            case 128: return launch_typed<IO, DK, 128, true>(p, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     int cols = p.head_v_dim < 64 ? p.head_v_dim : 64;
     if (const char* env = getenv("GDN_DECODE_COLS")) {
         const int v = atoi(env);
         if ((v == 32 || v == 64 || v == 128) && v <= p.head_v_dim) cols = v;
     }
     switch (cols) {
-        case 32: return launch_typed<IO, DK, 32>(p, stream);
-        case 64: return launch_typed<IO, DK, 64>(p, stream);
-        case 128: return launch_typed<IO, DK, 128>(p, stream);
+        case 32: return launch_typed<IO, DK, 32, false>(p, stream);
+        case 64: return launch_typed<IO, DK, 64, false>(p, stream);
+        case 128: return launch_typed<IO, DK, 128, false>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -22,10 +22,14 @@ struct DecodeParams {
     void* out;              // [B, T, H_v, d_v] io
     float* rec_snap;        // [T, B, H_v, d_k, d_v] state after each token, or null
     void* conv_snap;        // [T, B, conv_dim, 3] io conv tail after each token, or null
+    const void* gate_z;     // [B, T, H_v, d_v] io gate input, with gate_y
+    const void* gate_w;     // [d_v] io norm weight, with gate_y
+    void* gate_y;           // [B, T, H_v, d_v] io gated output, or null (no gate)
     int64_t conv_dim;
     int32_t batch, num_k_heads, num_v_heads, head_k_dim, head_v_dim, io_dtype;
     int32_t num_tokens;     // T, 1 .. kMaxDecodeTokens
     float q_scale, l2_eps;
+    float gate_eps;
 };
 
 struct PrefillParams {
@@ -49,6 +53,20 @@ struct PrefillParams {
     float q_scale, l2_eps;
     int32_t diag_neumann;   // two-pass path: diagonal-block inverses by the Neumann product
 };
+
+// Output gate: rows = tokens x H_v rows of d_v elements.
+struct GateParams {
+    const void* o;          // [rows, d_v] io
+    const void* z;          // [rows, d_v] io
+    const void* norm_w;     // [d_v] io
+    void* y;                // [rows, d_v] io (may equal o or z exactly)
+    int64_t rows;
+    int32_t head_v_dim, io_dtype;
+    float eps;
+};
+
+bool gate_supported(int head_v_dim, int io_dtype);
+hipError_t launch_output_gate(const GateParams& p, hipStream_t stream);
 
 bool decode_supported(int head_k_dim, int head_v_dim, int io_dtype);
 hipError_t launch_decode_step(const DecodeParams& p, hipStream_t stream);

@@ -62,6 +62,11 @@ _lib.gdn_decode_multi.argtypes = [_CFG, ctypes.c_int32, _P, _P, _P, _P, _P, _P, 
                                   _P]
 _lib.gdn_decode_multi.restype = ctypes.c_int32
 _lib.gdn_decode_step.restype = ctypes.c_int32
+_lib.gdn_decode_gated.argtypes = [_CFG, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_float, _P, _P, _P, _P]
+_lib.gdn_decode_gated.restype = ctypes.c_int32
+_lib.gdn_output_gate.argtypes = [_CFG, _I64, _P, _P, _P, ctypes.c_float, _P, _P]
+_lib.gdn_output_gate.restype = ctypes.c_int32
 
 lib = _lib
 
@@ -283,3 +288,80 @@ def decode_multi(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=N
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_multi")
     return out, conv_state_out, rec_state_out, rec_snapshots, conv_snapshots
+
+
+GATE_EPS = 1e-6
+
+
+def output_gate(cfg: Config, o, z, norm_w, eps: float = GATE_EPS, *, y=None, stream=None):
+    """RMSNormGated of the core output: y = norm_w * o / sqrt(mean(o^2) + eps)
+    * silu(z) per token and value head over d_v.  o, z: [..., H_v, d_v] (any
+    leading token axes, contiguous); y may be o or z (in place).  Returns y."""
+    Hv, dv = cfg.num_v_heads, cfg.head_v_dim
+    io = cfg.torch_io
+    if o is None or o.dim() < 2 or tuple(o.shape[-2:]) != (Hv, dv):
+        raise ValueError(f"o must be [..., {Hv}, {dv}]")
+    shape = tuple(o.shape)
+    rows = o.numel() // (Hv * dv)
+    _check(o, "o", shape, io)
+    _check(z, "z", shape, io)
+    _check(norm_w, "norm_w", (dv,), io)
+    if y is None:
+        y = torch.empty(shape, dtype=io, device=o.device)
+    _check(y, "y", shape, io)
+    st = _lib.gdn_output_gate(ctypes.byref(cfg.c()), rows, _ptr(o), _ptr(z), _ptr(norm_w), eps, _ptr(y),
+                              _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_output_gate")
+    return y
+
+
+def decode_gated(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, z, norm_w, conv_state_in=None,
+                 rec_state_in=None, *, eps: float = GATE_EPS, y=None, out=None, want_out=False,
+                 conv_state_out=None, rec_state_out=None, rec_snapshots=None, conv_snapshots=None,
+                 snapshots=False, stream=None):
+    """decode_multi with the output gate fused in (qkv [B, T, conv_dim], z
+    [B, T, H_v, d_v]); returns (y, out, conv_state_out, rec_state_out,
+    rec_snapshots, conv_snapshots).  The ungated out is written only if
+    passed in or ``want_out``; otherwise it is None."""
+    B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
+    io = cfg.torch_io
+    if qkv.dim() != 3:
+        raise ValueError(f"qkv must be [B, T, conv_dim], got {tuple(qkv.shape)}")
+    T = qkv.shape[1]
+    _check(qkv, "qkv", (B, T, cfg.conv_dim), io)
+    _check(a, "a", (B, T, Hv), io)
+    _check(b, "b", (B, T, Hv), io)
+    _check(conv_w, "conv_w", (cfg.conv_dim, cfg.conv_kernel), io)
+    _check(A_log, "A_log", (Hv,), torch.float32)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _check(z, "z", (B, T, Hv, dv), io)
+    _check(norm_w, "norm_w", (dv,), io)
+    _check(conv_state_in, "conv_state_in", (B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
+    dev = qkv.device
+    if y is None:
+        y = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+    if out is None and want_out:
+        out = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    if rec_state_out is None:
+        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if snapshots and rec_snapshots is None:
+        rec_snapshots = torch.empty((T, B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if snapshots and conv_snapshots is None:
+        conv_snapshots = torch.empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    _check(y, "y", (B, T, Hv, dv), io)
+    _check(out, "out", (B, T, Hv, dv), io, True)
+    _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
+    _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
+    _check(rec_snapshots, "rec_snapshots", (T, B, Hv, dk, dv), torch.float32, True)
+    _check(conv_snapshots, "conv_snapshots", (T, B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    st = _lib.gdn_decode_gated(ctypes.byref(cfg.c()), T, _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out),
+                               _ptr(rec_state_in), _ptr(rec_state_out), _ptr(out), _ptr(z), _ptr(norm_w),
+                               eps, _ptr(y), _ptr(rec_snapshots), _ptr(conv_snapshots), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_gated")
+    return y, out, conv_state_out, rec_state_out, rec_snapshots, conv_snapshots

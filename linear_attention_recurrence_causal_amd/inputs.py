@@ -156,6 +156,17 @@ def generate(w: Workload, seed: int | None = None) -> dict:
                 dec_b=dec_b)
 
 
+def gate_inputs(w: Workload, lead: tuple, seed: int | None = None) -> dict:
+    """Inputs of the output gate for core outputs [*lead, H_v, d_v]: z ~ N(0, 1)
+    and norm_w ~ N(1, 0.1) (model norm weights start at one), both io dtype.
+    Their own generator (seed + 7919), so the layer's inputs are unchanged."""
+    seed = (w.seed if seed is None else seed) + 7919
+    gen = torch.Generator().manual_seed(seed)
+    z = _randn(gen, tuple(lead) + (w.num_v_heads, w.head_v_dim), 1.0, w.io_dtype)
+    norm_w = (_randn(gen, (w.head_v_dim,), 0.1, torch.float32) + 1.0).to(w.io_dtype)
+    return dict(z=z, norm_w=norm_w)
+
+
 def to_numpy_io(t: torch.Tensor | None):
     """io tensor -> numpy: bf16 as its uint16 bit pattern, fp32 as float32."""
     if t is None:

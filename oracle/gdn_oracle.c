@@ -33,6 +33,8 @@
  *              the d_k x d_v recurrent state per value head.
  *   checkpoints ([QPR] "Summary"): the recurrent state and conv tail after
  *              every absolute position that is a multiple of the interval.
+ *   output gate ([GDN] "Output"): RMSNormGated of the core output with z,
+ *              applied to given o, z and norm weights (oracle_output_gate).
  *
  * Every quantity is carried in fp64.  The only rounding to a narrower type
  * is the optional rounding of the conv+SiLU output to bf16 (round to
@@ -115,6 +117,22 @@ void oracle_l2_normalize(double* x, int64_t n, double eps, double scale) {
     for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
     const double inv = scale / sqrt(ss + eps);
     for (int64_t i = 0; i < n; ++i) x[i] *= inv;
+}
+
+/* Output gate of [GDN] "Output": RMSNormGated(core output, z), per row of n
+ * channels (one token and value head over d_v):
+ *   y = w * o / sqrt(mean(o^2) + eps) * silu(z)
+ * The page names the gated norm beside a plain norm written (1 + w) * x; the
+ * gated one is read as scaling by w itself.  rows x n arrays, row-major. */
+void oracle_output_gate(int64_t rows, int64_t n, const double* o, const double* z, const double* w,
+                        double eps, double* y) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* orow = o + r * n;
+        double ss = 0.0;
+        for (int64_t j = 0; j < n; ++j) ss += orow[j] * orow[j];
+        const double inv = 1.0 / sqrt(ss / (double)n + eps);
+        for (int64_t j = 0; j < n; ++j) y[r * n + j] = w[j] * orow[j] * inv * oracle_silu(z[r * n + j]);
+    }
 }
 
 /* g of [GDN] "Discretisation" */

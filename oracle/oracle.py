@@ -66,6 +66,8 @@ def lib():
             getattr(_lib, name).restype = ctypes.c_double
         _lib.oracle_l2_normalize.argtypes = [P, ctypes.c_int64, ctypes.c_double, ctypes.c_double]
         _lib.oracle_l2_normalize.restype = None
+        _lib.oracle_output_gate.argtypes = [ctypes.c_int64, ctypes.c_int64, P, P, P, ctypes.c_double, P]
+        _lib.oracle_output_gate.restype = None
         _lib.oracle_gate_g.argtypes = [ctypes.c_double] * 3
         _lib.oracle_gate_g.restype = ctypes.c_double
         _lib.oracle_num_threads.restype = ctypes.c_int
@@ -261,4 +263,18 @@ def gate_g(A_log: float, a: float, dt_bias: float) -> float:
 def l2_normalize(x, eps: float = 1e-6, scale: float = 1.0):
     y = np.array(x, dtype=np.float64, copy=True).ravel()
     lib().oracle_l2_normalize(_ptr(y), y.size, float(eps), float(scale))
+    return y
+
+
+def output_gate(o, z, w, eps: float = 1e-6):
+    """RMSNormGated over the last axis: y = w * o / sqrt(mean(o^2) + eps) *
+    silu(z), fp64.  o, z [..., n] (any numbers; io tensors converted by the
+    caller), w [n]."""
+    o = np.ascontiguousarray(o, np.float64)
+    z = np.ascontiguousarray(z, np.float64)
+    w = np.ascontiguousarray(w, np.float64)
+    n = o.shape[-1]
+    assert z.shape == o.shape and w.shape == (n,)
+    y = np.zeros_like(o)
+    lib().oracle_output_gate(o.size // n if n else 0, n, _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(y))
     return y

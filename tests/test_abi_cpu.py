@@ -191,3 +191,53 @@ def test_decode_multi_rejects_bad_arguments(G):
     assert call(c, rsnap=P(FAKE * 8)) == G.GDN_EALIAS
     assert call(c, csnap=P(FAKE * 3)) == G.GDN_EALIAS
     assert call(c, rsnap=P(FAKE * 12), csnap=P(FAKE * 12 + 1024)) == G.GDN_EALIAS
+
+
+def test_output_gate_rejects_bad_arguments(G):
+    P = ctypes.c_void_p
+    f = G.lib.gdn_output_gate
+    def call(c, n=16, eps=1e-6, **over):
+        args = dict(o=P(FAKE), z=P(FAKE * 2), w=P(FAKE * 3))
+        args.update({k: v for k, v in over.items() if k in ("o", "z", "w")})
+        y = over.get("y", P(FAKE * 4))
+        return f(ctypes.byref(c.c()), n, args["o"], args["z"], args["w"], eps, y, None)
+    c = cfg(G, io_dtype=G.GDN_BF16)
+    assert call(c, n=-1) == G.GDN_EINVAL
+    assert call(c, eps=-1e-6) == G.GDN_EINVAL
+    assert call(c, eps=float("nan")) == G.GDN_EINVAL
+    assert call(c, o=None) == G.GDN_EINVAL
+    assert call(c, w=None) == G.GDN_EINVAL
+    assert call(c, o=P(FAKE + 2)) == G.GDN_EINVAL              # 16-byte alignment
+    assert call(c, y=P(FAKE * 4 + 8)) == G.GDN_EINVAL
+    assert call(cfg(G, head_v_dim=96)) == G.GDN_EUNSUPPORTED
+    assert call(cfg(G, io_dtype=7)) == G.GDN_EINVAL
+    # in place is exact equality only; a shifted y overlaps o, and y over the weights
+    assert call(c, y=P(FAKE + 256)) == G.GDN_EALIAS
+    assert call(c, y=P(FAKE * 2 + 4096)) == G.GDN_EALIAS
+    assert call(c, n=1, y=P(FAKE * 3)) == G.GDN_EALIAS
+
+
+def test_decode_gated_rejects_bad_arguments(G):
+    P = ctypes.c_void_p
+    f = G.lib.gdn_decode_gated
+    def call(c, T=2, eps=1e-6, **over):
+        args = dict(qkv=P(FAKE), a=P(FAKE * 2), b=P(FAKE * 3), conv_w=P(FAKE * 4),
+                    A_log=P(FAKE * 5), dt_bias=P(FAKE * 6), cin=None, cout=P(FAKE * 7),
+                    rin=None, rout=P(FAKE * 8), out=P(FAKE * 9), z=P(FAKE * 10), w=P(FAKE * 11),
+                    eps=eps, y=P(FAKE * 12), rsnap=None, csnap=None, stream=None)
+        args.update(over)
+        return f(ctypes.byref(c.c()), T, *args.values())
+    c = cfg(G)
+    assert call(c, y=None) == G.GDN_EINVAL
+    assert call(c, z=None) == G.GDN_EINVAL
+    assert call(c, w=None) == G.GDN_EINVAL
+    assert call(c, eps=-1.0) == G.GDN_EINVAL
+    assert call(c, T=0) == G.GDN_EINVAL
+    assert call(c, qkv=None) == G.GDN_EINVAL
+    assert call(cfg(G, head_v_dim=96)) == G.GDN_EUNSUPPORTED
+    # y is an output of its own; z and the weights are inputs no output may overlap
+    assert call(c, y=P(FAKE * 9 + 64)) == G.GDN_EALIAS
+    assert call(c, y=P(FAKE * 10)) == G.GDN_EALIAS
+    assert call(c, y=P(FAKE * 11)) == G.GDN_EALIAS
+    assert call(c, z=P(FAKE * 8)) == G.GDN_EALIAS
+    assert call(c, w=P(FAKE * 9)) == G.GDN_EALIAS

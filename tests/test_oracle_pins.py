@@ -129,6 +129,50 @@ def test_l2norm_hand_case_and_zero(oracle_lib):
     assert np.allclose(y2, 0.5 * y, rtol=1e-15)
 
 
+# ---------------------------------------------------------------- output gate
+
+def test_output_gate_hand_case(oracle_lib):
+    """[GDN] "Output", RMSNormGated: o = (3, 4), eps = 0, w = 1: mean(o^2) =
+    25/2, so o / rms = (3, 4) sqrt(2) / 5; with z = 50 (silu(50) = 50 (1 -
+    e^-50 + ...)) y = (30 sqrt 2, 40 sqrt 2) to 1e-15."""
+    y = oracle_lib.output_gate([[3.0, 4.0]], [[50.0, 50.0]], [1.0, 1.0], eps=0.0)
+    assert y[0, 0] == pytest.approx(30 * math.sqrt(2.0), rel=1e-15)
+    assert y[0, 1] == pytest.approx(40 * math.sqrt(2.0), rel=1e-15)
+    # z = 0 closes the gate, w scales each channel on its own
+    assert np.all(oracle_lib.output_gate([[3.0, 4.0]], [[0.0, 0.0]], [1.0, 1.0]) == 0.0)
+    y2 = oracle_lib.output_gate([[3.0, 4.0]], [[50.0, 50.0]], [2.0, -0.5], eps=0.0)
+    assert y2[0, 0] == pytest.approx(60 * math.sqrt(2.0), rel=1e-15)
+    assert y2[0, 1] == pytest.approx(-20 * math.sqrt(2.0), rel=1e-15)
+
+
+def test_output_gate_mean_not_sum_and_scale_invariance(oracle_lib):
+    """A constant row c (n channels, eps = 0) normalises to sign(c) for every
+    n, which holds for the mean of squares only; o -> a o with eps -> a^2
+    eps leaves y unchanged."""
+    for n in (2, 32, 128):
+        for c in (0.01, -3.0, 700.0):
+            y = oracle_lib.output_gate(np.full((1, n), c), np.full((1, n), 60.0), np.ones(n), eps=0.0)
+            assert np.allclose(y, math.copysign(60.0, c), rtol=1e-14)
+    rng = np.random.default_rng(5)
+    o, z, w = rng.standard_normal((6, 128)), rng.standard_normal((6, 128)), rng.standard_normal(128)
+    for a in (1e-3, 7.0):
+        assert rel(oracle_lib.output_gate(a * o, z, w, eps=1e-6 * a * a),
+                   oracle_lib.output_gate(o, z, w, eps=1e-6)) < 1e-14
+
+
+def test_output_gate_matches_torch_rms_norm(oracle_lib):
+    """The textbook RMSNorm of torch (fp64, weight w, the same eps) times
+    torch's SiLU of z, on random rows of 32, 64 and 128 channels."""
+    rng = np.random.default_rng(6)
+    for n in (32, 64, 128):
+        o = rng.standard_normal((40, n)) * rng.uniform(0.01, 10.0, (40, 1))
+        z, w = 3 * rng.standard_normal((40, n)), rng.standard_normal(n)
+        to = lambda x: torch.from_numpy(np.ascontiguousarray(x))
+        want = (torch.nn.functional.rms_norm(to(o), (n,), to(w), eps=1e-6)
+                * torch.nn.functional.silu(to(z))).numpy()
+        assert rel(oracle_lib.output_gate(o, z, w, eps=1e-6), want) < 1e-14
+
+
 # ---------------------------------------------------------------- front end
 
 def small_workload(**kw):
