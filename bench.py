@@ -80,6 +80,7 @@ def profiled_traffic(profile: str, sources):
 PREFILL_SOURCES = ("gdn_prefill_split.hip", "gdn_chunk_common.h", "gdn_api.hip")
 FUSED_SOURCES = ("gdn_prefill.hip", "gdn_chunk_common.h")
 DECODE_SOURCES = ("gdn_decode.hip",)
+GATE_SOURCES = ("gdn_gate.hip",)
 
 
 def time_events(fn, steps, warmup):
@@ -243,6 +244,8 @@ def bench_output_gate(args):
                        "roofline": {"kernel": "output_gate_kernel", "bound": "hbm",
                                     "achieved": gate_bytes / t / 1e9, "peak": HBM_PEAK_BYTES / 1e9,
                                     "unit": "GB/s", "frac": gate_bytes / t / HBM_PEAK_BYTES,
+                                    "traffic": profiled_traffic("output_gate_kernel_qwen36-27b_prefill_16k.md",
+                                                                GATE_SOURCES),
                                     "bytes_per_launch": gate_bytes}},
         "fused_decode": {"workload": "gdn_decode_gated, B=32 decode workload, 256 consecutive steps, "
                                     "y only",
@@ -251,7 +254,9 @@ def bench_output_gate(args):
                          "roofline": {"kernel": "decode_step_kernel (gated, 128 columns per workgroup)",
                                       "bound": "hbm", "achieved": dec_bytes / td / 1e9,
                                       "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
-                                      "frac": dec_bytes / td / HBM_PEAK_BYTES}},
+                                      "frac": dec_bytes / td / HBM_PEAK_BYTES,
+                                      "traffic": profiled_traffic("decode_gated_qwen36-27b_decode_b32.md",
+                                                                  DECODE_SOURCES)}},
     }
 
 
