@@ -12,7 +12,8 @@ consecutive steps, state ~N(0, 0.05)) and reports its HBM bandwidth, and
 times the fp64 CPU oracle on a bounded sample of the prefill workload.
 The multi-token decode step (4 tokens per sequence per call) is timed on the
 decode workload too, and so is the output gate (RMSNormGated with z): on its
-own over the prefill output shape, and fused into the decode step.
+own over the prefill output shape, and fused into the decode step.  The
+varlen prefill is timed on a serving-like mix of eight sequences.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -260,6 +261,58 @@ def bench_output_gate(args):
     }
 
 
+def bench_varlen(args):
+    """The varlen prefill on a serving-like mix: eight sequences of 1 to 4096
+    tokens (11,381 in all), some continuing from checkpoint positions, with
+    the Qwen3.6-27B heads; the same sequences as eight single calls for
+    comparison."""
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    lens = [4096, 1, 1000, 3000, 17, 2048, 64, 555]
+    starts = [0, 4096, 0, 8192, 100, 0, 64, 4000]
+    w = I.Workload("varlen-mix", batch=len(lens), seq_len=max(lens), num_k_heads=16, num_v_heads=48,
+                   init_state=True, seed=1005)
+    inp = I.generate(w)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    qkv = torch.cat([inp["qkv"][i, :n] for i, n in enumerate(lens)]).cuda()
+    a = torch.cat([inp["a"][i, :n] for i, n in enumerate(lens)]).cuda()
+    b = torch.cat([inp["b"][i, :n] for i, n in enumerate(lens)]).cuda()
+    d = {k: inp[k].cuda() for k in ("conv_w", "A_log", "dt_bias", "conv_state", "rec_state")}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=16, num_v_heads=48)
+    out = torch.empty(cu[-1], 48, 128, dtype=torch.bfloat16, device="cuda")
+    conv = torch.empty_like(d["conv_state"])
+    S = torch.empty_like(d["rec_state"])
+    ws = torch.empty(gdn.prefill_varlen_workspace_bytes(cfg, cu, starts), dtype=torch.uint8, device="cuda")
+    t = time_events(lambda: gdn.prefill_varlen(cfg, cu, starts, qkv, a, b, d["conv_w"], d["A_log"], d["dt_bias"],
+                                               d["conv_state"], d["rec_state"], out=out, conv_state_out=conv,
+                                               rec_state_out=S, workspace=ws), args.steps, args.warmup)
+    c1 = gdn.Config(batch=1, num_k_heads=16, num_v_heads=48)
+    singles = []
+    for i, n in enumerate(lens):
+        sl = slice(cu[i], cu[i + 1])
+        ws1 = torch.empty(max(gdn.prefill_workspace_bytes(c1, n), 256), dtype=torch.uint8, device="cuda")
+        singles.append((qkv[sl].unsqueeze(0), a[sl].unsqueeze(0), b[sl].unsqueeze(0),
+                        d["conv_state"][i:i + 1].contiguous(), d["rec_state"][i:i + 1].contiguous(),
+                        out[sl].unsqueeze(0), conv[i:i + 1].contiguous(), S[i:i + 1].contiguous(), ws1, starts[i]))
+
+    def all_singles():
+        for q, aa, bb, cs, rs, o, co, so, ws1, st in singles:
+            gdn.prefill_chunked(c1, q, aa, bb, d["conv_w"], d["A_log"], d["dt_bias"], cs, rs, start_pos=st,
+                                out=o, conv_state_out=co, rec_state_out=so, workspace=ws1)
+
+    t1 = time_events(all_singles, max(2, args.steps // 4), 1)
+    tokens = cu[-1]
+    flops = prefill_flops_per_token_head() * tokens * 48
+    return {"workload": f"gdn_prefill_varlen, 8 sequences of {lens} tokens from positions {starts}, 16/48 heads",
+            "us_per_call": t * 1e6, "tokens_per_s": tokens / t,
+            "roofline": {"kernel": "prep_kernel_varlen + state_kernel<4, VarlenParams>", "bound": "mfma",
+                         "achieved": flops / t / 1e12, "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / t / BF16_PEAK_FLOPS},
+            "single_calls_us": t1 * 1e6, "speedup_vs_single_calls": t1 / t}
+
+
 def cpu_baseline(inp, tokens):
     from linear_attention_recurrence_causal_amd import inputs as I
     from oracle import oracle as O
@@ -359,6 +412,8 @@ def main():
             "speedup_vs_single_steps": T * td / tm}
         print("bench: output gate", file=sys.stderr, flush=True)
         rec["output_gate"] = bench_output_gate(args)
+    print("bench: varlen prefill", file=sys.stderr, flush=True)
+    rec["prefill_varlen"] = bench_varlen(args)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)

@@ -160,6 +160,65 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
                                void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* Workspace for gdn_prefill_varlen (host only): the bytes with which every
+ * group of up to 64 sequences runs each pass once,
+ *   max over groups of (sequences of the group) * (chunks its longest
+ *   sequence spans) * (H_k * 32768 + H_v * 17664).
+ * cu_seqlens, start_pos: host arrays as for gdn_prefill_varlen. */
+gdn_status gdn_prefill_varlen_workspace_bytes(const gdn_config* cfg, const int64_t* cu_seqlens,
+                                              const int64_t* start_pos, uint64_t* bytes);
+
+/* Chunked prefill of B = cfg->batch sequences of different lengths and
+ * start positions in one call, packed along the token axis (continuous
+ * batching; the Qwen3.6-27B PR lists batching past one sequence and prefix
+ * caching under "Known limitations and follow-ups" and "Summary").  Per
+ * sequence the result is bit for bit that of gdn_prefill_chunked with that
+ * sequence alone (same start_pos, same checkpoints).
+ *   cu_seqlens   (host) [B + 1] int64, cu_seqlens[0] = 0, non-decreasing:
+ *                sequence i owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1
+ *                (T = cu_seqlens[B] tokens in all; empty sequences allowed,
+ *                they copy their states)
+ *   start_pos    (host) [B] int64 >= 0: absolute position of each
+ *                sequence's first token (chunk boundaries at absolute
+ *                multiples of 64, as in gdn_prefill_chunked)
+ *   qkv          [T, conv_dim] io, 16-byte aligned; a, b [T, H_v] io
+ *   out          [T, H_v, d_v] io, 16-byte aligned
+ *   conv_state_in/out [B, conv_dim, K-1], rec_state_in/out [B, H_v, d_k, d_v]:
+ *                per sequence, as in gdn_prefill_chunked (NULL inputs =
+ *                new requests)
+ *   ckpt_buf, ckpt_buf_bytes, ckpt_interval: slots laid out as in
+ *                gdn_state_checkpoint with batch B; sequence i writes its
+ *                part of slot j for every position (j+1)*interval in
+ *                (start_pos[i], start_pos[i] + len_i] and leaves the others
+ *                alone.  The buffer must hold the furthest slot any
+ *                sequence writes.
+ *   workspace    required (this path is two-pass only): at least one chunk
+ *                of records for the largest group of sequences,
+ *                min(B, 64) * (H_k * 32768 + H_v * 17664) bytes, else
+ *                GDN_ESPACE; gdn_prefill_varlen_workspace_bytes gives the
+ *                size that runs every group in one segment.
+ * Supported: as gdn_prefill_chunked's two-pass path (bf16 io, d = 128,
+ * H_v / H_k <= 8). */
+gdn_status gdn_prefill_varlen(const gdn_config* cfg, const int64_t* cu_seqlens, const int64_t* start_pos,
+                              const void* qkv, const void* a, const void* b, const void* conv_w,
+                              const float* A_log, const float* dt_bias, const void* conv_state_in,
+                              void* conv_state_out, const float* rec_state_in, float* rec_state_out, void* out,
+                              void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+
+/* Prefix-cache lookup (host only): for a request of which the first
+ * cached_tokens tokens are known (a prefix hit), the checkpoint to resume
+ * from -- the slot of the largest multiple of interval not above
+ * cached_tokens -- and the offsets of sequence seq_index's conv tail and
+ * recurrent state inside ckpt_buf (layout of gdn_state_checkpoint with
+ * cfg->batch sequences).  Resume with start_pos = entry->position and the
+ * tokens from there on.  entry->slot = -1 (position 0, offsets 0) when no
+ * checkpoint lies in the prefix: start a new request.  Whether the slot
+ * was written is the caller's bookkeeping ("Summary" of the Qwen3.6-27B
+ * PR: recurrent and conv checkpoints for prefix reuse). */
+gdn_status gdn_ckpt_lookup(const gdn_config* cfg, int64_t interval, int64_t cached_tokens, int32_t seq_index,
+                           gdn_ckpt_entry* entry);
+
 /* One recurrent decode step: one new token per sequence ("Delta rule").
  *   qkv [B, conv_dim], a, b [B, H_v], out [B, H_v, d_v] (io dtype); the
  *   other arguments as in gdn_prefill_chunked.  conv_state_out must not

@@ -369,6 +369,163 @@ gdn_status gdn_decode_gated(const gdn_config* cfg, int32_t num_tokens, const voi
                          rec_state_in, rec_state_out, out, rec_snapshots, conv_snapshots, gate, stream);
 }
 
+// Checks cu_seqlens / start_pos of a varlen call (host arrays) and returns
+// the number of chunks the largest group of sequences spans per sequence
+// and the workspace bytes with which every group runs in one segment.
+static gdn_status varlen_shape(const gdn_config* cfg, const int64_t* cu_seqlens, const int64_t* start_pos,
+                               uint64_t* ws_all) {
+    if (!cu_seqlens || !start_pos || cu_seqlens[0] != 0) return GDN_EINVAL;
+    const int G = gdn::prefill_varlen_group();
+    uint64_t need = 0;
+    for (int g0 = 0; g0 < cfg->batch; g0 += G) {
+        const int n = cfg->batch - g0 < G ? cfg->batch - g0 : G;
+        int64_t max_n = 0;
+        for (int i = g0; i < g0 + n; ++i) {
+            const int64_t len = cu_seqlens[i + 1] - cu_seqlens[i], st = start_pos[i];
+            if (len < 0 || st < 0 || st > ((int64_t)1 << 50) || len > ((int64_t)1 << 40)) return GDN_EINVAL;
+            const int64_t chunks = len > 0 ? (st + len - 1) / cfg->chunk + 1 - st / cfg->chunk : 0;
+            if (chunks > max_n) max_n = chunks;
+        }
+        const uint64_t g = (uint64_t)max_n * gdn::prefill_split_chunk_bytes(n, cfg->num_k_heads, cfg->num_v_heads);
+        if (g > need) need = g;
+    }
+    *ws_all = need;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_varlen_workspace_bytes(const gdn_config* cfg, const int64_t* cu_seqlens,
+                                              const int64_t* start_pos, uint64_t* bytes) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (!bytes) return GDN_EINVAL;
+    uint64_t all = 0;
+    if (gdn_status s = varlen_shape(cfg, cu_seqlens, start_pos, &all)) return s;
+    *bytes = all;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_varlen(const gdn_config* cfg, const int64_t* cu_seqlens, const int64_t* start_pos,
+                              const void* qkv, const void* a, const void* b, const void* conv_w,
+                              const float* A_log, const float* dt_bias, const void* conv_state_in,
+                              void* conv_state_out, const float* rec_state_in, float* rec_state_out, void* out,
+                              void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (ckpt_interval < 0 || (ckpt_interval > 0 && ckpt_interval % cfg->chunk != 0)) return GDN_EINVAL;
+    uint64_t ws_all = 0;
+    if (gdn_status s = varlen_shape(cfg, cu_seqlens, start_pos, &ws_all)) return s;
+    const int64_t B = cfg->batch, T = cu_seqlens[B], Hv = cfg->num_v_heads;
+    const uintptr_t ea = cfg->io_dtype == GDN_BF16 ? 2 : 4;
+    if (!conv_w || !aligned_to(conv_w, ea) || !conv_state_out || !aligned_to(conv_state_out, ea))
+        return GDN_EINVAL;
+    if (!A_log || !dt_bias || !rec_state_out || !aligned_to(A_log, 4) || !aligned_to(dt_bias, 4) ||
+        !aligned_to(rec_state_out, 4))
+        return GDN_EINVAL;
+    if (T > 0 && (!qkv || !a || !b || !out)) return GDN_EINVAL;
+    if (!aligned16(qkv) || !aligned16(out) || !aligned_to(a, ea) || !aligned_to(b, ea)) return GDN_EINVAL;
+    if (!aligned_to(conv_state_in, ea) || !aligned_to(rec_state_in, 4) || !aligned_to(ckpt_buf, 256) ||
+        !workspace || !aligned_to(workspace, 256))
+        return GDN_EINVAL;
+    if (!gdn::prefill_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype, cfg->conv_kernel,
+                                cfg->chunk))
+        return GDN_EUNSUPPORTED;
+    if (cfg->num_v_heads / cfg->num_k_heads > 8) return GDN_EUNSUPPORTED;
+    if (B > 0 && workspace_bytes < gdn::prefill_varlen_group_bytes((int)B, cfg->num_k_heads, cfg->num_v_heads))
+        return GDN_ESPACE;
+
+    const int64_t cd = conv_dim_of(cfg);
+    const int ios = io_size(cfg->io_dtype);
+    const uint64_t conv_state_bytes = (uint64_t)B * cd * (cfg->conv_kernel - 1) * ios;
+    const uint64_t rec_bytes = (uint64_t)B * Hv * cfg->head_k_dim * cfg->head_v_dim * 4;
+    const Range r_qkv = range_of(qkv, (uint64_t)T * cd * ios);
+    const Range r_a = range_of(a, (uint64_t)T * Hv * ios), r_b = range_of(b, (uint64_t)T * Hv * ios);
+    const Range r_cin = range_of(conv_state_in, conv_state_in ? conv_state_bytes : 0);
+    const Range r_cout = range_of(conv_state_out, conv_state_bytes);
+    const Range r_rin = range_of(rec_state_in, rec_state_in ? rec_bytes : 0);
+    const Range r_rout = range_of(rec_state_out, rec_bytes);
+    const Range r_out = range_of(out, (uint64_t)T * Hv * cfg->head_v_dim * ios);
+    if (rec_state_in && rec_state_in != rec_state_out && overlap(r_rin, r_rout)) return GDN_EALIAS;
+    for (const Range& w : {r_cout, r_out, r_rout})
+        for (const Range& o : {r_qkv, r_a, r_b, r_cin})
+            if (overlap(w, o)) return GDN_EALIAS;
+    if (overlap(r_cout, r_out) || overlap(r_cout, r_rout) || overlap(r_out, r_rout) || overlap(r_out, r_rin) ||
+        overlap(r_cout, r_rin))
+        return GDN_EALIAS;
+
+    // checkpoints: each sequence emits its own slots; the buffer spans the
+    // furthest one
+    uint64_t ck_need = 0;
+    int64_t ck_count = 0;
+    for (int64_t i = 0; i < B; ++i) {
+        const Plan pl = checkpoint_plan(cfg, start_pos[i], cu_seqlens[i + 1] - cu_seqlens[i], ckpt_interval);
+        ck_count += pl.count;
+        if (pl.buffer_bytes > ck_need) ck_need = pl.buffer_bytes;
+    }
+    const Plan plan0 = checkpoint_plan(cfg, 0, 0, ckpt_interval);
+    const Range r_ck = range_of(ckpt_buf, ck_count > 0 ? ck_need : 0);
+    if (ck_count > 0) {
+        if (!ckpt_buf) return GDN_EINVAL;
+        if (ckpt_buf_bytes < ck_need) return GDN_ESPACE;
+        for (const Range& o : {r_qkv, r_a, r_b, r_cin, r_cout, r_rin, r_rout, r_out})
+            if (overlap(r_ck, o)) return GDN_EALIAS;
+    }
+    const Range r_ws = range_of(workspace, ws_all < workspace_bytes ? ws_all : workspace_bytes);
+    for (const Range& o : {r_qkv, r_a, r_b, r_cin, r_cout, r_rin, r_rout, r_out, r_ck})
+        if (overlap(r_ws, o)) return GDN_EALIAS;
+
+    gdn::PrefillParams p{};
+    p.qkv = qkv;
+    p.a = a;
+    p.b = b;
+    p.conv_w = conv_w;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.conv_in = conv_state_in;
+    p.conv_out = conv_state_out;
+    p.rec_in = rec_state_in;
+    p.rec_out = rec_state_out;
+    p.out = out;
+    p.ckpt_buf = ck_count > 0 ? static_cast<char*>(ckpt_buf) : nullptr;
+    p.slot_bytes = plan0.slot_bytes;
+    p.conv_slot_bytes = plan0.conv_bytes;
+    p.ckpt_interval = ck_count > 0 ? ckpt_interval : 0;
+    p.seq_len = 0;
+    p.start_pos = 0;
+    p.conv_dim = cd;
+    p.batch = cfg->batch;
+    p.num_k_heads = cfg->num_k_heads;
+    p.num_v_heads = cfg->num_v_heads;
+    p.q_scale = cfg->q_scale;
+    p.l2_eps = cfg->l2_eps;
+    const char* solve_env = getenv("GDN_DIAG_SOLVE");
+    p.diag_neumann = solve_env && solve_env[0] == 'n';
+    if (B == 0) return GDN_OK;
+    const hipError_t e = gdn::launch_prefill_varlen(p, cu_seqlens, start_pos, workspace, workspace_bytes,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_ckpt_lookup(const gdn_config* cfg, int64_t interval, int64_t cached_tokens, int32_t seq_index,
+                           gdn_ckpt_entry* entry) {
+    if (gdn_status s = check_config(cfg)) return s;
+    if (!entry || interval <= 0 || interval % cfg->chunk != 0 || cached_tokens < 0 || seq_index < 0 ||
+        seq_index >= cfg->batch)
+        return GDN_EINVAL;
+    const Plan pl = checkpoint_plan(cfg, 0, 0, interval);
+    const int64_t position = cached_tokens / interval * interval;
+    entry->position = position;
+    if (position == 0) {
+        entry->slot = -1;
+        entry->conv_offset = entry->rec_offset = 0;
+        return GDN_OK;
+    }
+    entry->slot = position / interval - 1;
+    const uint64_t base = (uint64_t)entry->slot * pl.slot_bytes;
+    entry->conv_offset = base + (uint64_t)seq_index * conv_dim_of(cfg) * (cfg->conv_kernel - 1) * io_size(cfg->io_dtype);
+    entry->rec_offset = base + pl.conv_bytes +
+                        (uint64_t)seq_index * cfg->num_v_heads * cfg->head_k_dim * cfg->head_v_dim * 4;
+    return GDN_OK;
+}
+
 gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void* o, const void* z,
                            const void* norm_w, float eps, void* y, void* stream) {
     if (gdn_status s = check_config(cfg)) return s;

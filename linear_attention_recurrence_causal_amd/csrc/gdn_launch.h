@@ -81,4 +81,14 @@ uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads);
 bool prefill_split_supported(const PrefillParams& p);
 hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream);
 
+// Varlen two-pass path: p.batch sequences packed along the token axis
+// (cu_seqlens[p.batch + 1], start_pos[p.batch], host arrays; p.seq_len and
+// p.start_pos unused).  Sequences run in groups of prefill_varlen_group();
+// the workspace must hold one chunk of records for a group
+// (prefill_varlen_group_bytes) and is used in segments beyond that.
+int prefill_varlen_group();
+uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads);
+hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqlens, const int64_t* start_pos,
+                                 void* ws, uint64_t ws_bytes, hipStream_t stream);
+
 }  // namespace gdn

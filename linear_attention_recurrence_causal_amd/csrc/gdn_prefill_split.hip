@@ -28,6 +28,8 @@
 // segments through rec_state_out.  Every value the state kernel consumes is
 // bit-identical to what the fused kernel computes in LDS, so the two paths
 // agree to the last bit up to the compiler's instruction choice.
+#include <type_traits>
+
 #include "gdn_chunk_common.h"
 
 namespace gdn {
@@ -60,15 +62,63 @@ struct SplitParams {
     int32_t nseg;        // chunks in the segment
     int32_t first_seg;   // state comes from rec_in (else from rec_out)
     int32_t last_seg;    // write the final conv tail
+    int32_t rec_stride;  // chunk records per (sequence, head) in the workspace
+    int32_t rec_batch;   // sequences with records in the workspace
 };
 
-__device__ __forceinline__ char* key_rec(const SplitParams& s, int b, int kh, int j) {
-    return s.ws + (((int64_t)b * s.p.num_k_heads + kh) * s.nseg + j) * kKeyRec;
+// Records of record-sequence rb (the sequence's index among those of the
+// launch), head and chunk j of the segment
+__device__ __forceinline__ char* key_rec(const SplitParams& s, int rb, int kh, int j) {
+    return s.ws + (((int64_t)rb * s.p.num_k_heads + kh) * s.rec_stride + j) * kKeyRec;
 }
 
-__device__ __forceinline__ char* val_rec(const SplitParams& s, int b, int h, int j) {
-    return s.ws + (int64_t)s.p.batch * s.p.num_k_heads * s.nseg * kKeyRec +
-           (((int64_t)b * s.p.num_v_heads + h) * s.nseg + j) * kValRec;
+__device__ __forceinline__ char* val_rec(const SplitParams& s, int rb, int h, int j) {
+    return s.ws + (int64_t)s.rec_batch * s.p.num_k_heads * s.rec_stride * kKeyRec +
+           (((int64_t)rb * s.p.num_v_heads + h) * s.rec_stride + j) * kValRec;
+}
+
+// ---- sequences of different lengths and start positions in one call
+// (token-packed inputs and outputs, cu_seqlens).  One launch covers up to
+// kVarlenGroup sequences, described in its kernel arguments; a segment is a
+// run of chunks at the same offset j0 from each sequence's first chunk.
+constexpr int kVarlenGroup = 64;
+
+struct SeqDesc {
+    int64_t tok0;    // first token of the sequence in the packed arrays
+    int64_t start;   // absolute position of that token
+    int64_t len;     // tokens of the sequence in this call
+};
+
+struct VarlenParams {
+    SplitParams sp;      // shared fields; per-sequence ones come from seq[]
+    int64_t j0;          // the segment's first chunk, relative to each sequence's first
+    int32_t b0, nb;      // sequences b0 .. b0 + nb - 1 of the call
+    SeqDesc seq[kVarlenGroup];
+};
+
+// The view of sequence b (entry i of the launch) as a one-sequence-per-row
+// call: token-indexed pointers are shifted so that the kernels' row index
+// b * len + t lands on token tok0 + t; state, conv-state and checkpoint
+// arrays keep their index b.
+__device__ __forceinline__ SplitParams seq_view(const VarlenParams& v, int i, int b) {
+    SplitParams s = v.sp;
+    const SeqDesc d = v.seq[i];
+    const int64_t kf = d.start / kC;
+    const int64_t n = d.len > 0 ? (d.start + d.len - 1) / kC + 1 - kf : 0;
+    const int64_t shift = d.tok0 - (int64_t)b * d.len;
+    const PrefillParams& p = v.sp.p;
+    s.p.qkv = static_cast<const uint16_t*>(p.qkv) + shift * p.conv_dim;
+    s.p.a = static_cast<const uint16_t*>(p.a) + shift * p.num_v_heads;
+    s.p.b = static_cast<const uint16_t*>(p.b) + shift * p.num_v_heads;
+    s.p.out = static_cast<uint16_t*>(p.out) + shift * p.num_v_heads * kD;
+    s.p.seq_len = d.len;
+    s.p.start_pos = d.start;
+    s.k0 = kf + v.j0;
+    const int64_t left = n - v.j0;
+    s.nseg = left <= 0 ? 0 : (int32_t)(left < v.sp.rec_stride ? left : v.sp.rec_stride);
+    s.first_seg = v.j0 == 0;
+    s.last_seg = v.j0 + v.sp.rec_stride >= n;
+    return s;
 }
 
 // Byte offset of 16-byte granule g of row `row` in the state kernel's LDS
@@ -147,19 +197,16 @@ __device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm,
     for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
 }
 
+// Chunk j of the segment for sequence b (record-sequence rb) and key head kh
 template <bool NEUMANN>
-__global__ __launch_bounds__(kPrepThreads)
-void prep_kernel(SplitParams sp) {
+__device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, int kh, int j) {
     const PrefillParams& p = sp.p;
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int li = lane % 16, lq = lane / 16;
     const int Hk = p.num_k_heads, r = p.num_v_heads / Hk;
-    const int j = blockIdx.x % sp.nseg;
-    const int grp = blockIdx.x / sp.nseg;
-    const int b = grp / Hk, kh = grp % Hk;
     const int64_t local0 = (sp.k0 + j) * kC - p.start_pos;
-    char* krec = key_rec(sp, b, kh, j);
+    char* krec = key_rec(sp, rb, kh, j);
     const bool interior = local0 >= 3 && local0 + kC <= p.seq_len;
     uint2 raw[11];
     prep_front_load(p, b, kh, local0, interior, tid, raw);
@@ -214,7 +261,7 @@ void prep_kernel(SplitParams sp) {
     // ---- per value head of the group: masks, row scales, diagonal
     // inverses -> value record
     for (int hh = 0; hh < r; ++hh) {
-        char* vrec = val_rec(sp, b, kh * r + hh, j);
+        char* vrec = val_rec(sp, rb, kh * r + hh, j);
         PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, sm.Ps, sm.AN, sm.AdT, sm.tokS};
         mask_pair(hv, wave, gk[0], gq[0], lane);
         if (wave < 2) mask_pair(hv, 8 + wave, gk[1], gq[1], lane);
@@ -241,6 +288,28 @@ void prep_kernel(SplitParams sp) {
             copy16(vrec + kRecAN + (e >> 3) * 128 + 16 * (e & 7), sm.AN + (e >> 3) * kKtLd + 8 * (e & 7));
         if (hh + 1 < r) __syncthreads();
     }
+}
+
+template <bool NEUMANN>
+__global__ __launch_bounds__(kPrepThreads)
+void prep_kernel(SplitParams sp) {
+    const int j = blockIdx.x % sp.rec_stride;
+    const int grp = blockIdx.x / sp.rec_stride;
+    const int b = grp / sp.p.num_k_heads, kh = grp % sp.p.num_k_heads;
+    prep_body<NEUMANN>(sp, b, b, kh, j);
+}
+
+// Varlen: blockIdx = (entry i, key head, chunk j of the segment); entries
+// whose sequence has fewer chunks left leave at once
+template <bool NEUMANN>
+__global__ __launch_bounds__(kPrepThreads)
+void prep_kernel_varlen(VarlenParams vp) {
+    const int j = blockIdx.x % vp.sp.rec_stride;
+    const int grp = blockIdx.x / vp.sp.rec_stride;
+    const int i = grp / vp.sp.p.num_k_heads, kh = grp % vp.sp.p.num_k_heads;
+    const SplitParams sp = seq_view(vp, i, vp.b0 + i);
+    if (j >= sp.nseg) return;
+    prep_body<NEUMANN>(sp, vp.b0 + i, i, kh, j);
 }
 
 // ============================================================ state kernel
@@ -430,7 +499,7 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
 }
 
 struct StateCtx {
-    int b, kh, h, zcol0;
+    int b, rb, kh, h, zcol0;   // rb: the sequence's index among the launch's records
     bool owns_qk_tail;
     int64_t s_base;
 };
@@ -592,8 +661,8 @@ __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& 
         wait_vm<0, true>();
         return;
     }
-    const char* krec = key_rec(sp, cx.b, cx.kh, jn);
-    const char* vrec = val_rec(sp, cx.b, cx.h, jn);
+    const char* krec = key_rec(sp, cx.rb, cx.kh, jn);
+    const char* vrec = val_rec(sp, cx.rb, cx.h, jn);
 #pragma unroll
     for (int pc = LO; pc < HI; ++pc) issue_piece(buf, krec, vrec, pc, lane);
     if constexpr (SS::is_v(M)) {
@@ -647,11 +716,23 @@ __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& 
 // Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  One
 // barrier per chunk: the chunk's products are done (its buffer may be
 // refilled) and the next chunk's buffer is filled.
-template <int NW>
-__global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
+__device__ __forceinline__ const SplitParams& base_of(const SplitParams& s) { return s; }
+__device__ __forceinline__ const SplitParams& base_of(const VarlenParams& v) { return v.sp; }
+
+// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  One
+// barrier per chunk: the chunk's products are done (its buffer may be
+// refilled) and the next chunk's buffer is filled.  KP = SplitParams (one
+// call's sequences share length and start) or VarlenParams (a group of
+// sequences of their own; a sequence with no chunk in this segment is done,
+// its state and conv tail written by the segment that held its last chunk,
+// except in the first segment, where a sequence of no tokens copies its
+// states).
+template <int NW, class KP>
+__global__ __launch_bounds__(512) void state_kernel(KP kp) {
+    constexpr bool VARLEN = std::is_same<KP, VarlenParams>::value;
     using SS = StateShape<NW>;
     constexpr int N = SS::N, NCH = 2 * kD + N;
-    const PrefillParams& p = sp.p;
+    const PrefillParams& p0 = base_of(kp).p;
     __shared__ __attribute__((aligned(16))) char buf0[SS::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[SS::BUF];
     __shared__ __attribute__((aligned(16))) char slab0[SS::NV * SS::SLAB];   // raw v slabs of the V waves,
@@ -662,23 +743,39 @@ __global__ __launch_bounds__(512) void state_kernel(SplitParams sp) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: role branches stay scalar
     const int li = lane % 16, lq = lane / 16;
     const bool compute = wave < NW;
-    // workgroup -> (b, key head, member); the r * SPLIT members of one
-    // (b, key head) share a blockIdx % 8, so the round-robin dispatch puts
-    // them on one XCD and its L2, where their common key records stay
-    const int r = p.num_v_heads / p.num_k_heads;
+    // workgroup -> (sequence, key head, member); the r * SPLIT members of
+    // one (sequence, key head) share a blockIdx % 8, so the round-robin
+    // dispatch puts them on one XCD and its L2, where their common key
+    // records stay
+    const int r = p0.num_v_heads / p0.num_k_heads;
     const int M = r * SS::SPLIT;
-    const int NG = p.batch * p.num_k_heads;
+    int entries, b0 = 0;
+    if constexpr (VARLEN) {
+        entries = kp.nb;
+        b0 = kp.b0;
+    } else {
+        entries = p0.batch;
+    }
+    const int NG = entries * p0.num_k_heads;
     const int bid = blockIdx.x;
     const int grp = (bid / 8 / M) * 8 + bid % 8;
     const int member = (bid / 8) % M;
     if (grp >= NG) return;
     StateCtx cx;
-    cx.b = grp / p.num_k_heads;
-    cx.kh = grp % p.num_k_heads;
+    cx.rb = grp / p0.num_k_heads;
+    cx.b = b0 + cx.rb;
+    cx.kh = grp % p0.num_k_heads;
     cx.h = cx.kh * r + member / SS::SPLIT;
     cx.zcol0 = (member % SS::SPLIT) * N;
     cx.owns_qk_tail = member == 0;
-    cx.s_base = ((int64_t)cx.b * p.num_v_heads + cx.h) * kD * kD + cx.zcol0 + 16 * (compute ? wave : 0) + li;
+    cx.s_base = ((int64_t)cx.b * p0.num_v_heads + cx.h) * kD * kD + cx.zcol0 + 16 * (compute ? wave : 0) + li;
+    SplitParams view;
+    if constexpr (VARLEN) {
+        view = seq_view(kp, cx.rb, cx.b);
+        if (view.nseg == 0 && !view.first_seg) return;
+    }
+    const SplitParams& sp = VARLEN ? view : base_of(kp);
+    const PrefillParams& p = sp.p;
 
     for (int e = tid; e < 4 * N; e += 512) {
         const int t = e / N, c = e % N;
@@ -764,7 +861,7 @@ hipError_t launch_state(const SplitParams& sp, hipStream_t stream) {
     const int r = sp.p.num_v_heads / sp.p.num_k_heads;
     const int ng = sp.p.batch * sp.p.num_k_heads;
     const int blocks = ((ng + 7) / 8) * 8 * r * StateShape<NW>::SPLIT;
-    hipLaunchKernelGGL((state_kernel<NW>), dim3(blocks), dim3(512), 0, stream, sp);
+    hipLaunchKernelGGL((state_kernel<NW, SplitParams>), dim3(blocks), dim3(512), 0, stream, sp);
     return hipGetLastError();
 }
 
@@ -784,6 +881,15 @@ int state_waves(const PrefillParams& p) {
 
 hipError_t launch_state_any(const SplitParams& sp, hipStream_t stream) {
     return state_waves(sp.p) == 4 ? launch_state<4>(sp, stream) : launch_state<2>(sp, stream);
+}
+
+template <int NW>
+hipError_t launch_state_varlen(const VarlenParams& vp, hipStream_t stream) {
+    const int r = vp.sp.p.num_v_heads / vp.sp.p.num_k_heads;
+    const int ng = vp.nb * vp.sp.p.num_k_heads;
+    const int blocks = ((ng + 7) / 8) * 8 * r * StateShape<NW>::SPLIT;
+    hipLaunchKernelGGL((state_kernel<NW, VarlenParams>), dim3(blocks), dim3(512), 0, stream, vp);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -816,10 +922,12 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         sp.last_seg = 1;
         return launch_state_any(sp, stream);
     }
+    sp.rec_batch = p.batch;
     for (int64_t k0 = k_first; k0 < k_end; k0 += max_seg) {
         const int64_t n = k_end - k0 < max_seg ? k_end - k0 : max_seg;
         sp.k0 = k0;
         sp.nseg = (int32_t)n;
+        sp.rec_stride = (int32_t)n;
         sp.last_seg = k0 + n == k_end;
         const dim3 grid((unsigned)(p.batch * p.num_k_heads * n));
         if (p.diag_neumann) hipLaunchKernelGGL(prep_kernel<true>, grid, dim3(kPrepThreads), 0, stream, sp);
@@ -829,6 +937,56 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         e = launch_state_any(sp, stream);
         if (e != hipSuccess) return e;
         sp.first_seg = 0;
+    }
+    return hipSuccess;
+}
+
+uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads) {
+    return prefill_split_chunk_bytes(num_seqs < kVarlenGroup ? num_seqs : kVarlenGroup, num_k_heads, num_v_heads);
+}
+
+int prefill_varlen_group() { return kVarlenGroup; }
+
+// Sequences of one call in groups of kVarlenGroup; per group, segments of
+// as many chunks per sequence as the workspace holds for the whole group.
+hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqlens, const int64_t* start_pos,
+                                 void* ws, uint64_t ws_bytes, hipStream_t stream) {
+    for (int g0 = 0; g0 < p.batch; g0 += kVarlenGroup) {
+        const int G = p.batch - g0 < kVarlenGroup ? p.batch - g0 : kVarlenGroup;
+        VarlenParams vp{};
+        vp.sp.p = p;
+        vp.sp.ws = static_cast<char*>(ws);
+        vp.sp.rec_batch = G;
+        vp.b0 = g0;
+        vp.nb = G;
+        int64_t max_n = 0;
+        for (int i = 0; i < G; ++i) {
+            const int64_t t0 = cu_seqlens[g0 + i], len = cu_seqlens[g0 + i + 1] - t0, st = start_pos[g0 + i];
+            vp.seq[i] = SeqDesc{t0, st, len};
+            const int64_t n = len > 0 ? (st + len - 1) / kC + 1 - st / kC : 0;
+            if (n > max_n) max_n = n;
+        }
+        int64_t seg = (int64_t)(ws_bytes / prefill_split_chunk_bytes(G, p.num_k_heads, p.num_v_heads));
+        const int64_t grid_cap = ((int64_t)1 << 30) / ((int64_t)G * p.num_k_heads);
+        if (seg > max_n) seg = max_n;
+        if (seg > grid_cap) seg = grid_cap;
+        if (seg < 1) seg = 1;
+        vp.sp.rec_stride = (int32_t)seg;
+        PrefillParams pg = p;
+        pg.batch = G;
+        const int nw = state_waves(pg);
+        for (int64_t j0 = 0; j0 == 0 || j0 < max_n; j0 += seg) {
+            vp.j0 = j0;
+            if (max_n > 0) {
+                const dim3 grid((unsigned)(G * p.num_k_heads * seg));
+                if (p.diag_neumann) hipLaunchKernelGGL(prep_kernel_varlen<true>, grid, dim3(kPrepThreads), 0, stream, vp);
+                else hipLaunchKernelGGL(prep_kernel_varlen<false>, grid, dim3(kPrepThreads), 0, stream, vp);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+            const hipError_t e = nw == 4 ? launch_state_varlen<4>(vp, stream) : launch_state_varlen<2>(vp, stream);
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -67,6 +67,14 @@ _lib.gdn_decode_gated.argtypes = [_CFG, ctypes.c_int32, _P, _P, _P, _P, _P, _P, 
 _lib.gdn_decode_gated.restype = ctypes.c_int32
 _lib.gdn_output_gate.argtypes = [_CFG, _I64, _P, _P, _P, ctypes.c_float, _P, _P]
 _lib.gdn_output_gate.restype = ctypes.c_int32
+_I64P = ctypes.POINTER(_I64)
+_lib.gdn_prefill_varlen_workspace_bytes.argtypes = [_CFG, _I64P, _I64P, ctypes.POINTER(_U64)]
+_lib.gdn_prefill_varlen_workspace_bytes.restype = ctypes.c_int32
+_lib.gdn_prefill_varlen.argtypes = [_CFG, _I64P, _I64P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _U64, _I64, _P, _U64, _P]
+_lib.gdn_prefill_varlen.restype = ctypes.c_int32
+_lib.gdn_ckpt_lookup.argtypes = [_CFG, _I64, _I64, ctypes.c_int32, ctypes.POINTER(CkptEntry)]
+_lib.gdn_ckpt_lookup.restype = ctypes.c_int32
 
 lib = _lib
 
@@ -365,3 +373,85 @@ def decode_gated(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, z, norm_w, conv
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_gated")
     return y, out, conv_state_out, rec_state_out, rec_snapshots, conv_snapshots
+
+
+def _i64_array(xs):
+    xs = [int(x) for x in xs]
+    return (_I64 * max(1, len(xs)))(*xs)
+
+
+def prefill_varlen_workspace_bytes(cfg: Config, cu_seqlens, start_pos) -> int:
+    n = _U64(0)
+    st = _lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(cfg.c()), _i64_array(cu_seqlens),
+                                                 _i64_array(start_pos), ctypes.byref(n))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_varlen_workspace_bytes")
+    return n.value
+
+
+def prefill_varlen(cfg: Config, cu_seqlens, start_pos, qkv, a, b, conv_w, A_log, dt_bias,
+                   conv_state_in=None, rec_state_in=None, *, ckpt_interval: int = 0, ckpt_buf=None,
+                   out=None, conv_state_out=None, rec_state_out=None, workspace="auto", stream=None):
+    """cfg.batch sequences packed along the token axis: cu_seqlens [B + 1] and
+    start_pos [B] are host sequences of ints; qkv [T, conv_dim], a, b [T, H_v];
+    returns (out [T, H_v, d_v], conv_state_out, rec_state_out).
+    ``workspace``: "auto" allocates prefill_varlen_workspace_bytes, else a
+    contiguous uint8 device tensor (at least one chunk per sequence of a
+    group of 64)."""
+    B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
+    cu = [int(x) for x in cu_seqlens]
+    sp = [int(x) for x in start_pos]
+    if len(cu) != B + 1 or len(sp) != B:
+        raise ValueError(f"cu_seqlens needs {B + 1} entries and start_pos {B}")
+    T = cu[-1]
+    io = cfg.torch_io
+    _check(qkv, "qkv", (T, cfg.conv_dim), io)
+    _check(a, "a", (T, Hv), io)
+    _check(b, "b", (T, Hv), io)
+    _check(conv_w, "conv_w", (cfg.conv_dim, cfg.conv_kernel), io)
+    _check(A_log, "A_log", (Hv,), torch.float32)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32)
+    _check(conv_state_in, "conv_state_in", (B, cfg.conv_dim, cfg.conv_kernel - 1), io, True)
+    _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
+    dev = qkv.device
+    if out is None:
+        out = torch.empty((T, Hv, dv), dtype=io, device=dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+    if rec_state_out is None:
+        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(out, "out", (T, Hv, dv), io)
+    _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
+    _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
+    ck_bytes = 0
+    if ckpt_buf is not None:
+        if not ckpt_buf.is_cuda or not ckpt_buf.is_contiguous():
+            raise ValueError("ckpt_buf must be a contiguous device tensor")
+        ck_bytes = ckpt_buf.numel() * ckpt_buf.element_size()
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a uint8 device tensor")
+        ws = max(prefill_varlen_workspace_bytes(cfg, cu, sp), 256)
+        wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev)
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws, wsbuf = workspace.numel() * workspace.element_size(), workspace
+    st = _lib.gdn_prefill_varlen(
+        ctypes.byref(cfg.c()), _i64_array(cu), _i64_array(sp), _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+        _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(rec_state_in),
+        _ptr(rec_state_out), _ptr(out), _ptr(ckpt_buf), ck_bytes, ckpt_interval, _ptr(wsbuf), ws,
+        _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_varlen")
+    return out, conv_state_out, rec_state_out
+
+
+def ckpt_lookup(cfg: Config, interval: int, cached_tokens: int, seq_index: int = 0) -> CkptEntry:
+    """The checkpoint to resume a request from after a prefix hit of
+    ``cached_tokens`` tokens (slot -1: none, start a new request)."""
+    e = CkptEntry()
+    st = _lib.gdn_ckpt_lookup(ctypes.byref(cfg.c()), interval, cached_tokens, seq_index, ctypes.byref(e))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_ckpt_lookup")
+    return e

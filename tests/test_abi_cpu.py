@@ -241,3 +241,75 @@ def test_decode_gated_rejects_bad_arguments(G):
     assert call(c, y=P(FAKE * 11)) == G.GDN_EALIAS
     assert call(c, z=P(FAKE * 8)) == G.GDN_EALIAS
     assert call(c, w=P(FAKE * 9)) == G.GDN_EALIAS
+
+
+def test_varlen_workspace_bytes_and_lookup(G):
+    """Host-only helpers of the varlen path: workspace sizes per group of 64
+    sequences, and the prefix-cache lookup's slot, position and offsets."""
+    c = cfg(G, batch=3)
+    per1 = 16 * 32768 + 48 * 17664
+    # lengths 100 (start 0: 2 chunks), 0, 4096 (start 5: 65 chunks)
+    assert G.prefill_varlen_workspace_bytes(c, [0, 100, 100, 4196], [0, 64, 5]) == 3 * 65 * per1
+    assert G.prefill_varlen_workspace_bytes(c, [0, 0, 0, 0], [0, 0, 0]) == 0
+    # 70 sequences of one chunk: two groups, 64 and 6
+    c70 = cfg(G, batch=70)
+    assert G.prefill_varlen_workspace_bytes(c70, list(range(0, 71)), [0] * 70) == 64 * per1
+    with pytest.raises(G.GdnError):
+        G.prefill_varlen_workspace_bytes(c, [1, 100, 100, 200], [0, 0, 0])     # cu_seqlens[0] != 0
+    with pytest.raises(G.GdnError):
+        G.prefill_varlen_workspace_bytes(c, [0, 100, 50, 200], [0, 0, 0])     # decreasing
+    with pytest.raises(G.GdnError):
+        G.prefill_varlen_workspace_bytes(c, [0, 1, 2, 3], [0, -1, 0])         # negative start
+    # lookup: slot of the largest multiple of the interval within the prefix
+    conv_bytes = 3 * c.conv_dim * 3 * 2
+    rec_bytes = 3 * 48 * 128 * 128 * 4
+    slot_bytes = ((conv_bytes + 255) // 256) * 256 + rec_bytes
+    e = G.ckpt_lookup(c, 4096, 10000, 2)
+    assert (e.slot, e.position) == (1, 8192)
+    assert e.conv_offset == slot_bytes + 2 * c.conv_dim * 3 * 2
+    assert e.rec_offset == slot_bytes + ((conv_bytes + 255) // 256) * 256 + 2 * 48 * 128 * 128 * 4
+    assert (G.ckpt_lookup(c, 4096, 8192, 0).slot, G.ckpt_lookup(c, 4096, 8191, 0).slot) == (1, 0)
+    e = G.ckpt_lookup(c, 4096, 4095, 0)
+    assert (e.slot, e.position, e.conv_offset, e.rec_offset) == (-1, 0, 0, 0)
+    # the lookup agrees with the plan of the call that wrote the slot
+    ents, _ = G.state_checkpoint(c, 0, 3 * 4096, 4096)
+    for ent in ents:
+        e = G.ckpt_lookup(c, 4096, ent.position, 0)
+        assert (e.slot, e.position, e.conv_offset, e.rec_offset) == (ent.slot, ent.position, ent.conv_offset,
+                                                                    ent.rec_offset)
+    for bad in (dict(interval=100), dict(interval=0), dict(cached=-1), dict(seq=3), dict(seq=-1)):
+        args = dict(interval=4096, cached=5000, seq=0)
+        args.update(bad)
+        with pytest.raises(G.GdnError):
+            G.ckpt_lookup(c, args["interval"], args["cached"], args["seq"])
+
+
+def test_varlen_rejects_bad_arguments(G):
+    P = ctypes.c_void_p
+    f = G.lib.gdn_prefill_varlen
+    arr = lambda xs: (ctypes.c_int64 * len(xs))(*xs)
+    def call(c, cu=(0, 100, 300), st=(0, 64), ws_bytes=1 << 30, ck_bytes=0, interval=0, **over):
+        args = dict(qkv=P(FAKE), a=P(FAKE * 2), b=P(FAKE * 3), conv_w=P(FAKE * 4), A_log=P(FAKE * 5),
+                    dt_bias=P(FAKE * 6), cin=None, cout=P(FAKE * 7), rin=None, rout=P(FAKE * 8),
+                    out=P(FAKE * 9), ck=None, ws=P(FAKE * 10))
+        args.update(over)
+        return f(ctypes.byref(c.c()), arr(cu), arr(st), args["qkv"], args["a"], args["b"], args["conv_w"],
+                 args["A_log"], args["dt_bias"], args["cin"], args["cout"], args["rin"], args["rout"],
+                 args["out"], args["ck"], ck_bytes, interval, args["ws"], ws_bytes, None)
+    c = cfg(G, batch=2)
+    assert call(c, cu=(5, 100, 300)) == G.GDN_EINVAL                  # cu_seqlens[0] != 0
+    assert call(c, cu=(0, 300, 100)) == G.GDN_EINVAL                  # decreasing
+    assert call(c, st=(0, -64)) == G.GDN_EINVAL
+    assert call(c, ws=None) == G.GDN_EINVAL                           # two-pass only
+    assert call(c, ws=P(FAKE * 10 + 16)) == G.GDN_EINVAL              # 256-byte workspace alignment
+    assert call(c, qkv=P(FAKE + 2)) == G.GDN_EINVAL
+    assert call(c, interval=100) == G.GDN_EINVAL
+    assert call(c, ws_bytes=2 * (16 * 32768 + 48 * 17664) - 1) == G.GDN_ESPACE
+    assert call(c, interval=64) == G.GDN_EINVAL                       # checkpoints need a buffer
+    assert call(c, interval=64, ck=P(FAKE * 11), ck_bytes=256) == G.GDN_ESPACE
+    assert call(cfg(G, batch=2, io_dtype=G.GDN_F32)) == G.GDN_EUNSUPPORTED
+    assert call(cfg(G, batch=2, num_k_heads=4, num_v_heads=48)) == G.GDN_EUNSUPPORTED   # group of 12
+    # outputs over the packed inputs, the workspace over an output
+    assert call(c, out=P(FAKE + 4096)) == G.GDN_EALIAS
+    assert call(c, cout=P(FAKE * 3)) == G.GDN_EALIAS
+    assert call(c, ws=P(FAKE * 9)) == G.GDN_EALIAS
