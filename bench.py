@@ -47,6 +47,13 @@ def prefill_bytes(B, L, Hk, Hv, d=128) -> int:
     return B * L * (conv_dim * 2 + Hv * 2 * 2 + Hv * d * 2) + 2 * B * Hv * d * d * 4
 
 
+def varlen_bytes(tokens, B, Hk, Hv, d=128) -> int:
+    """HBM floor of a varlen call with initial states: read qkv, a, b, write
+    o; read and write every sequence's recurrent state and conv tail."""
+    conv_dim = 2 * Hk * d + Hv * d
+    return tokens * (conv_dim * 2 + Hv * 2 * 2 + Hv * d * 2) + 2 * B * (Hv * d * d * 4 + conv_dim * 3 * 2)
+
+
 def decode_bytes(B, Hk, Hv, d=128) -> int:
     """Per decode step: state read + write, qkv, conv state in + out, o, a, b,
     conv taps, A_log and dt_bias."""
@@ -309,7 +316,9 @@ def bench_varlen(args):
             "us_per_call": t * 1e6, "tokens_per_s": tokens / t,
             "roofline": {"kernel": "prep_kernel_varlen + state_kernel<4, VarlenParams>", "bound": "mfma",
                          "achieved": flops / t / 1e12, "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
-                         "frac": flops / t / BF16_PEAK_FLOPS},
+                         "frac": flops / t / BF16_PEAK_FLOPS,
+                         "traffic": profiled_traffic("prefill_varlen_serving_mix.md", PREFILL_SOURCES),
+                         "hbm_floor_bytes_per_launch": varlen_bytes(tokens, len(lens), 16, 48)},
             "single_calls_us": t1 * 1e6, "speedup_vs_single_calls": t1 / t}
 
 
