@@ -265,6 +265,8 @@ static gdn_status decode_tokens(const gdn_config* cfg, int32_t num_tokens, const
         return GDN_EINVAL;
     if (cfg->conv_kernel != 4 || !gdn::decode_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype))
         return GDN_EUNSUPPORTED;
+    // grid (d_v / columns, H_v, B): the y and z dimensions stay within 65535
+    if (cfg->batch > 65535 || cfg->num_v_heads > 65535) return GDN_EUNSUPPORTED;
 
     const int64_t B = cfg->batch, Hv = cfg->num_v_heads, T = num_tokens;
     const int64_t cd = conv_dim_of(cfg);
