@@ -85,7 +85,7 @@ def profiled_traffic(profile: str, sources):
     return float(fields["traffic_bytes_per_launch"])
 
 
-PREFILL_SOURCES = ("gdn_prefill_split.hip", "gdn_chunk_common.h", "gdn_api.hip")
+PREFILL_SOURCES = ("gdn_prefill_split.hip", "gdn_chunk_common.h")
 FUSED_SOURCES = ("gdn_prefill.hip", "gdn_chunk_common.h")
 DECODE_SOURCES = ("gdn_decode.hip",)
 GATE_SOURCES = ("gdn_gate.hip",)
