@@ -313,3 +313,26 @@ def test_varlen_rejects_bad_arguments(G):
     assert call(c, out=P(FAKE + 4096)) == G.GDN_EALIAS
     assert call(c, cout=P(FAKE * 3)) == G.GDN_EALIAS
     assert call(c, ws=P(FAKE * 9)) == G.GDN_EALIAS
+
+
+def test_empty_batches_enqueue_nothing(G):
+    """B = 0 (and a gate over no rows) is a valid call that returns GDN_OK
+    without launching anything, so it runs here without a GPU."""
+    P = ctypes.c_void_p
+    c0 = cfg(G, batch=0)
+    st = G.lib.gdn_decode_step(ctypes.byref(c0.c()), P(FAKE), P(FAKE * 2), P(FAKE * 3), P(FAKE * 4),
+                               P(FAKE * 5), P(FAKE * 6), None, P(FAKE * 7), None, P(FAKE * 8), P(FAKE * 9),
+                               None)
+    assert st == G.GDN_OK
+    for ws, wsb in ((None, 0), (P(FAKE * 10), 1 << 30)):
+        st = G.lib.gdn_prefill_chunked(ctypes.byref(c0.c()), 100, 0, P(FAKE), P(FAKE * 2), P(FAKE * 3),
+                                       P(FAKE * 4), P(FAKE * 5), P(FAKE * 6), None, P(FAKE * 7), None,
+                                       P(FAKE * 8), P(FAKE * 9), None, 0, 0, ws, wsb, None)
+        assert st == G.GDN_OK
+    arr = (ctypes.c_int64 * 1)(0)
+    st = G.lib.gdn_prefill_varlen(ctypes.byref(c0.c()), arr, arr, None, None, None, P(FAKE * 4), P(FAKE * 5),
+                                  P(FAKE * 6), None, P(FAKE * 7), None, P(FAKE * 8), None, None, 0, 0,
+                                  P(FAKE * 10), 1 << 30, None)
+    assert st == G.GDN_OK
+    st = G.lib.gdn_output_gate(ctypes.byref(cfg(G).c()), 0, None, None, P(FAKE * 3), 1e-6, None, None)
+    assert st == G.GDN_OK
