@@ -44,16 +44,17 @@ constexpr int kDecodeThreads = 256;
 // multi-token step).  The arithmetic per token is the same in both, so T
 // tokens in one call equal T one-token calls bit for bit.  GATE: also write
 // the gated output (NCOL must be d_v).
-template <typename IO, int DK, int NCOL, int MAXT, bool GATE>
-__global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))) void decode_step_kernel(DecodeParams p) {
+template <typename IO, int DK, int NCOL, int MAXT, bool GATE, int THREADS = kDecodeThreads>
+__global__ __launch_bounds__(THREADS, MAXT > 1 ? 1 : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
+void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
-    constexpr int NRG = kDecodeThreads / NCQ;     // row groups
+    constexpr int NRG = THREADS / NCQ;            // row groups
     constexpr int RPT = DK / NRG;                 // rows per thread
-    static_assert(RPT * NRG == DK && NCQ * NRG == kDecodeThreads, "bad decode tiling");
+    static_assert(RPT * NRG == DK && NCQ * NRG == THREADS, "bad decode tiling");
     constexpr int NCH = 2 * DK + NCOL;            // conv channels this slice needs
-    constexpr int NWAVES = kDecodeThreads / 64;
-    constexpr int CPT = (NCH + kDecodeThreads - 1) / kDecodeThreads;   // channels per thread
+    constexpr int NWAVES = THREADS / 64;
+    constexpr int CPT = (NCH + THREADS - 1) / THREADS;   // channels per thread
 
     __shared__ float u_s[NCH];                    // conv+SiLU outputs (io-rounded)
     __shared__ float red_s[2][NWAVES][NCOL];      // cross-wave partial sums
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
     __shared__ float scal_s[4];                   // n_q, n_k, k.q (unnormalised), g
     __shared__ float beta_s;
     __shared__ float gsum_s[NWAVES];              // gate: per-wave sums of o^2
+    __shared__ float gzw_s[GATE ? MAXT : 1][GATE ? NCOL : 1];   // gate: w silu(z) per token and column
 
     const int tid = threadIdx.x;
     const int z = blockIdx.x;                     // column slice
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
     int64_t fcs[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        const int i = tid + k * kDecodeThreads;
+        const int i = tid + k * THREADS;
         if (i < NCH) {
             int64_t c;
             if (i < DK) c = (int64_t)kh * DK + i;
@@ -140,13 +142,21 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
         for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
+    // the gate factors w silu(z) go to LDS once, so that no gate input stays
+    // in a register through the state arithmetic
+    if (GATE && tid < NCOL) {
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t)
+            if (t < ntok) gzw_s[t][tid] = gw * silu_f32(zin[t]);
+    }
+
     for (int t = 0; t < ntok; ++t) {
         // conv + SiLU of the slice's channels (io-rounded); the carried tail
         // moves one token on (to this token's conv snapshot, and after the
         // last token to conv_out)
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
-            const int i = tid + k * kDecodeThreads;
+            const int i = tid + k * THREADS;
             if (i < NCH) {
                 float x = xin[k][0];
 #pragma unroll
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
             }
             acc = wave_sum(acc);
             if (lane == 0) scal_s[wave] = acc;
-        } else if (lane == 0) {
+        } else if (wave == 3 && lane == 0) {   // the lane that loaded the gates
             float ga = gate_a[0], gb = gate_b[0];
 #pragma unroll
             for (int tt = 1; tt < MAXT; ++tt)
@@ -252,12 +262,8 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
             float ss = 0.f;
 #pragma unroll
             for (int w = 0; w < (NCOL + 63) / 64; ++w) ss += gsum_s[w];
-            float zt = zin[0];
-#pragma unroll
-            for (int tt = 1; tt < MAXT; ++tt)
-                if (tt == t) zt = zin[tt];
             const float inv = 1.0f / sqrtf(ss * (1.0f / NCOL) + p.gate_eps);
-            T::store(p.gate_y, oi, gw * (o * inv) * silu_f32(zt));
+            T::store(p.gate_y, oi, (o * inv) * gzw_s[t][tid]);
         }
 
         // ---- 6. S = S' + k delta^T (this token's snapshot, if asked for)
@@ -280,14 +286,19 @@ __global__ __launch_bounds__(kDecodeThreads, MAXT > 1 ? 1 : (NCOL == 64 && !GATE
         *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
 }
 
+// 128-column workgroups (the gated step's, and GDN_DECODE_COLS=128) take 512
+// threads, so that each thread holds as few state rows as in the 64-column
+// step and the CU keeps more waves resident; gated and ungated 128-column
+// steps then sum their rows in the same order.
 template <typename IO, int DK, int NCOL, bool GATE>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+    constexpr int TH = NCOL == 128 ? 512 : kDecodeThreads;
     dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
     if (p.num_tokens == 1 && !p.rec_snap && !p.conv_snap)
-        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1, GATE>), grid, dim3(kDecodeThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1, GATE, TH>), grid, dim3(TH), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens, GATE>), grid, dim3(kDecodeThreads),
-                           0, stream, p);
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens, GATE, TH>), grid, dim3(TH), 0, stream,
+                           p);
     return hipGetLastError();
 }
 
