@@ -22,7 +22,8 @@
 // sum of squares stays on chip and y = w o / sqrt(mean(o^2) + eps) silu(z)
 // is formed from the fp32 o before any rounding.
 //
-// Thread layout (256 threads): thread = (cq, rg), cq = column quad (4
+// Thread layout (256 threads, 512 for 128-column slices): thread = (cq, rg),
+// cq = column quad (4
 // consecutive fp32 columns = one 16-byte load), rg = row group; thread owns
 // rows rg, rg + NRG, ... so that for each row step the whole workgroup reads
 // NRG full row segments with 16-byte coalesced loads.  S' lives in registers
