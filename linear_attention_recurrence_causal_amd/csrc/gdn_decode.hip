@@ -41,8 +41,9 @@ namespace {
 constexpr int kDecodeThreads = 256;
 
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
-// whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
-// multi-token step).  The arithmetic per token is the same in both, so T
+// whose 64-column split fits seven waves per SIMD; 4 and kMaxDecodeTokens:
+// the multi-token step, the smaller build for T <= 4, whose token arrays
+// take fewer registers).  The arithmetic per token is the same in both, so T
 // tokens in one call equal T one-token calls bit for bit.  GATE: also write
 // the gated output (NCOL must be d_v).
 template <typename IO, int DK, int NCOL, int MAXT, bool GATE, int THREADS = kDecodeThreads>
@@ -297,6 +298,8 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
     if (p.num_tokens == 1 && !p.rec_snap && !p.conv_snap)
         hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1, GATE, TH>), grid, dim3(TH), 0, stream, p);
+    else if (p.num_tokens <= 4)
+        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 4, GATE, TH>), grid, dim3(TH), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens, GATE, TH>), grid, dim3(TH), 0, stream,
                            p);
