@@ -41,13 +41,12 @@ namespace {
 constexpr int kDecodeThreads = 256;
 
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
-// whose 64-column split fits seven waves per SIMD; 4 and kMaxDecodeTokens:
-// the multi-token step, the smaller build for T <= 4, whose token arrays
-// take fewer registers).  The arithmetic per token is the same in both, so T
+// whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
+// multi-token step, four waves per SIMD, its tokens' inputs parked in LDS).  The arithmetic per token is the same in both, so T
 // tokens in one call equal T one-token calls bit for bit.  GATE: also write
 // the gated output (NCOL must be d_v).
 template <typename IO, int DK, int NCOL, int MAXT, bool GATE, int THREADS = kDecodeThreads>
-__global__ __launch_bounds__(THREADS, MAXT > 1 ? 1 : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
+__global__ __launch_bounds__(THREADS, MAXT > 1 ? 4 : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
 void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
@@ -65,6 +64,8 @@ void decode_step_kernel(DecodeParams p) {
     __shared__ float beta_s;
     __shared__ float gsum_s[NWAVES];              // gate: per-wave sums of o^2
     __shared__ float gzw_s[GATE ? MAXT : 1][GATE ? NCOL : 1];   // gate: w silu(z) per token and column
+    __shared__ float xin_s[MAXT > 1 ? MAXT : 1][MAXT > 1 ? NCH : 1];   // multi-token: pre-conv inputs
+    __shared__ float gab_s[MAXT > 1 ? MAXT : 1][2];                    // multi-token: gate inputs a, b
 
     const int tid = threadIdx.x;
     const int z = blockIdx.x;                     // column slice
@@ -152,6 +153,26 @@ void decode_step_kernel(DecodeParams p) {
             if (t < ntok) gzw_s[t][tid] = gw * silu_f32(zin[t]);
     }
 
+    // the multi-token step parks its tokens' inputs in LDS, so that they do
+    // not stay in registers through the state arithmetic
+    if (MAXT > 1) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int i = tid + k * THREADS;
+            if (i < NCH)
+#pragma unroll
+                for (int t = 0; t < MAXT; ++t)
+                    if (t < ntok) xin_s[t][i] = xin[k][t];
+        }
+        if (wave == 3 && lane == 0)
+#pragma unroll
+            for (int t = 0; t < MAXT; ++t)
+                if (t < ntok) {
+                    gab_s[t][0] = gate_a[t];
+                    gab_s[t][1] = gate_b[t];
+                }
+    }
+
     for (int t = 0; t < ntok; ++t) {
         // conv + SiLU of the slice's channels (io-rounded); the carried tail
         // moves one token on (to this token's conv snapshot, and after the
@@ -160,10 +181,7 @@ void decode_step_kernel(DecodeParams p) {
         for (int k = 0; k < CPT; ++k) {
             const int i = tid + k * THREADS;
             if (i < NCH) {
-                float x = xin[k][0];
-#pragma unroll
-                for (int tt = 1; tt < MAXT; ++tt)
-                    if (tt == t) x = xin[k][tt];
+                const float x = MAXT == 1 ? xin[k][0] : xin_s[t][i];
                 const float y = fmaf(taps[k][3], x, fmaf(taps[k][2], hist[k][2],
                                                          fmaf(taps[k][1], hist[k][1], taps[k][0] * hist[k][0])));
                 u_s[i] = T::round(silu_f32(y));
@@ -194,10 +212,8 @@ void decode_step_kernel(DecodeParams p) {
             acc = wave_sum(acc);
             if (lane == 0) scal_s[wave] = acc;
         } else if (wave == 3 && lane == 0) {   // the lane that loaded the gates
-            float ga = gate_a[0], gb = gate_b[0];
-#pragma unroll
-            for (int tt = 1; tt < MAXT; ++tt)
-                if (tt == t) { ga = gate_a[tt]; gb = gate_b[tt]; }
+            const float ga = MAXT == 1 ? gate_a[0] : gab_s[t][0];
+            const float gb = MAXT == 1 ? gate_b[0] : gab_s[t][1];
             scal_s[3] = neg_A * softplus_f32(ga + dt_h);
             beta_s = sigmoid_f32(gb);
         }
@@ -298,8 +314,6 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     dim3 grid(p.head_v_dim / NCOL, p.num_v_heads, p.batch);
     if (p.num_tokens == 1 && !p.rec_snap && !p.conv_snap)
         hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 1, GATE, TH>), grid, dim3(TH), 0, stream, p);
-    else if (p.num_tokens <= 4)
-        hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, 4, GATE, TH>), grid, dim3(TH), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_step_kernel<IO, DK, NCOL, kMaxDecodeTokens, GATE, TH>), grid, dim3(TH), 0, stream,
                            p);
