@@ -5,8 +5,10 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -16,22 +18,36 @@ SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_gate.hip", "gdn_prefill.hip", "
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 
-def hipcc_cmd(out: str = LIB) -> list[str]:
-    return ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            # packed fp32 VALU instructions are kept out of every kernel
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}",
-            "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         # packed fp32 VALU instructions are kept out of every kernel
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
+NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if NOISE not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libgdn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    r = subprocess.run(hipcc_cmd(tmp), capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    """Compile every HIP source into libgdn.so (always recompiles): one hipcc
+    per source in parallel, then the link."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmpdir = tempfile.mkdtemp(prefix="gdn_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        jobs = [["hipcc"] + FLAGS + ["-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+            errs = list(ex.map(_run, jobs))
+        tmp = LIB + ".tmp"
+        errs.append(_run(["hipcc", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", tmp] + objs))
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+    err = "\n".join(e for e in errs if e.strip())
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
