@@ -73,7 +73,7 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads of the target, by index.
+# The five workloads, by index: the shapes of the pages' models at their lengths.
 WORKLOADS = {
     0: Workload("tiny-f32-recurrent", batch=1, seq_len=0, num_k_heads=2, num_v_heads=4,
                 head_k_dim=32, head_v_dim=32, io="f32", decode_steps=64, seed=1000),

@@ -265,7 +265,7 @@ def test_prefill_then_decode(G, path):
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("stress", ["slowdecay", "extreme"])
 def test_prefill_stress(G, path, stress):
-    """Not part of the target bars' workloads, held to the same bars: long
+    """Not among the five workloads, held to the same bars: long
     memory (decay close to 1) and gates in their tails."""
     w = small(seq_len=640, init_state=True, seed=28)
     w = I.slow_decay(w) if stress == "slowdecay" else I.extreme_gates(w)
