@@ -54,5 +54,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "c_abi", "gdn_c_demo.cpp")
+DEMO_BIN = os.path.join(ROOT, "tests", "c_abi", "gdn_c_demo")
+
+
+def build_c_demo(verbose: bool = False) -> str:
+    """The C-ABI caller of tests/c_abi (host code, linked against libgdn.so)."""
+    tmp = DEMO_BIN + ".tmp"
+    err = _run(["hipcc", "-O2", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", "-o", tmp, DEMO_SRC,
+                f"-L{PKG}", "-lgdn", "-Wl,-rpath,$ORIGIN/../../linear_attention_recurrence_causal_amd"])
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, DEMO_BIN)
+    return DEMO_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_demo(verbose=True))
