@@ -41,6 +41,16 @@
  *     oldest first.  (The cortex state keeps K columns; its oldest is never
  *     read by a width-K causal conv of the next token, so K-1 are stored.)
  *   - rec_state [B, H_v, d_k, d_v] fp32, d_v contiguous.
+ *
+ * Environment overrides (read at each call; for tests and tuning, the
+ * defaults are the measured best):
+ *   GDN_PREFILL_PATH=fused|split   prefill path when a workspace is given
+ *   GDN_PREFILL_STATE_WAVES=2|4     compute waves per two-pass state workgroup
+ *   GDN_PREFILL_WAVES=2|4|8         waves per fused prefill workgroup
+ *   GDN_DIAG_SOLVE=neumann          diagonal-block inverses by the Neumann
+ *                                   product (two-pass path)
+ *   GDN_DECODE_COLS=32|64|128       state columns per decode workgroup (the
+ *                                   gated step always takes all d_v)
  */
 #ifndef GDN_H
 #define GDN_H
