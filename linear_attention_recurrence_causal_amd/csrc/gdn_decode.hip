@@ -320,9 +320,11 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Columns of S per workgroup: 64 by default (3072 workgroups on the 32 x 48
-// head decode; measured fastest against 32 and 128); GDN_DECODE_COLS = 32 /
-// 64 / 128 selects another split.  The gated step takes all d_v columns.
+// Columns of S per workgroup: all d_v by default (a workgroup owns a head;
+// at d_v = 128, 512 threads with eight state rows each; on the 32 x 48 head
+// decode measured at least as fast as 64 columns for 1..8 tokens, and
+// faster with the Infinity Cache cold); GDN_DECODE_COLS = 32 / 64 / 128
+// selects another split.  The gated step always takes all d_v columns.
 template <typename IO, int DK>
 hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
     if (p.gate_y) {
@@ -333,7 +335,7 @@ hipError_t launch_dk(const DecodeParams& p, hipStream_t stream) {
             default: return hipErrorInvalidValue;
         }
     }
-    int cols = p.head_v_dim < 64 ? p.head_v_dim : 64;
+    int cols = p.head_v_dim;
     if (const char* env = getenv("GDN_DECODE_COLS")) {
         const int v = atoi(env);
         if ((v == 32 || v == 64 || v == 128) && v <= p.head_v_dim) cols = v;
