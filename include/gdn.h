@@ -119,7 +119,7 @@ gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_
 
 /* Workspace for the two-pass prefill (host only): the bytes with which a call
  * of seq_len tokens per sequence (any start_pos) runs each pass once,
- *   B * (chunks the call can span) * (H_k * 32768 + H_v * 17664).
+ *   B * (chunks the call can span) * (H_k * 32768 + H_v * 13568).
  * The chunked form splits into per-chunk work that does not depend on the
  * state and a short recurrence over chunks that does ("Performance note");
  * with a workspace the first part runs for every chunk in parallel and only
@@ -173,7 +173,7 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
 /* Workspace for gdn_prefill_varlen (host only): the bytes with which every
  * group of up to 64 sequences runs each pass once,
  *   max over groups of (sequences of the group) * (chunks its longest
- *   sequence spans) * (H_k * 32768 + H_v * 17664).
+ *   sequence spans) * (H_k * 32768 + H_v * 13568).
  * cu_seqlens, start_pos: host arrays as for gdn_prefill_varlen. */
 gdn_status gdn_prefill_varlen_workspace_bytes(const gdn_config* cfg, const int64_t* cu_seqlens,
                                               const int64_t* start_pos, uint64_t* bytes);
@@ -204,7 +204,7 @@ gdn_status gdn_prefill_varlen_workspace_bytes(const gdn_config* cfg, const int64
  *                sequence writes.
  *   workspace    required (this path is two-pass only): at least one chunk
  *                of records for the largest group of sequences,
- *                min(B, 64) * (H_k * 32768 + H_v * 17664) bytes, else
+ *                min(B, 64) * (H_k * 32768 + H_v * 13568) bytes, else
  *                GDN_ESPACE; gdn_prefill_varlen_workspace_bytes gives the
  *                size that runs every group in one segment.
  * Supported: as gdn_prefill_chunked's two-pass path (bf16 io, d = 128,

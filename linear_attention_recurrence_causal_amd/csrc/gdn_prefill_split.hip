@@ -38,19 +38,41 @@ namespace {
 
 using namespace chunked;
 
-// ---- workspace records.  Matrices are row-major, columns in pos() order,
+// P and AN hold only their lower triangle of 16x16 tiles: rows 0..31 keep
+// granules 0..3 (64-byte rows), rows 32..63 all eight (128-byte rows).
+// Granules are XOR-swizzled so that eight consecutive rows read by one phase
+// of an LDS read hit eight different bank groups.  The value records store
+// them in exactly this layout, so the state kernel copies them unchanged.
+constexpr int kPaMat = 32 * 64 + 32 * 128;          // 6144 bytes per matrix
+__device__ __forceinline__ int pa_off(int mat, int row, int g) {
+    return mat * kPaMat + (row < 32 ? row * 64 + 16 * (g ^ ((row >> 1) & 3))
+                                    : 2048 + (row - 32) * 128 + 16 * (g ^ (row & 7)));
+}
+// the inverse: byte l (a multiple of 16) of one matrix's layout holds row
+// `row`, granule g (8 pos()-ordered columns)
+__device__ __forceinline__ void pa_granule(int l, int& row, int& g) {
+    if (l < 2048) {
+        row = l >> 6;
+        g = ((l >> 4) & 3) ^ ((row >> 1) & 3);
+    } else {
+        row = 32 + ((l - 2048) >> 7);
+        g = ((l >> 4) & 7) ^ (row & 7);
+    }
+}
+
+// ---- workspace records.  Q and K are row-major, columns in pos() order,
 // unpadded.  Key record (sequence, key head, chunk): Q | K.  Value record
-// (sequence, value head, chunk): P | AN | five rows of 64 fp32
-// (beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k |
-// exp(gamma_C), 0, ...).
+// (sequence, value head, chunk): P | AN (lower tiles, the layout above) |
+// five rows of 64 fp32 (beta | beta Gamma n_k | Gamma n_q |
+// exp(gamma_C - gamma) n_k | exp(gamma_C), 0, ...).
 constexpr int kRecQ = 0;
 constexpr int kRecK = kC * kD * 2;
 constexpr int kKeyRec = 2 * kC * kD * 2;            // 32768
 constexpr int kRecP = 0;
-constexpr int kRecAN = kC * kC * 2;
-constexpr int kRecTok = 2 * kC * kC * 2;
+constexpr int kRecAN = kPaMat;
+constexpr int kRecTok = 2 * kPaMat;
 constexpr int kTokBytes = 5 * kC * 4;
-constexpr int kValRec = kRecTok + kTokBytes;        // 17664
+constexpr int kValRec = kRecTok + kTokBytes;        // 13568
 static_assert(kKeyRec % 256 == 0 && kValRec % 256 == 0, "records keep 256-byte alignment");
 
 constexpr int kMaxGroup = 8;                        // value heads per key head on this path
@@ -278,14 +300,23 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
             if (NEUMANN) diag_neumann(hv, wave, lane);
             else diag_solve<true>(hv, lane);
         } else {
-            for (int e = tid - 64 * kSolveWaves; e < kC * 8 + kTokBytes / 16; e += kPrepThreads - 64 * kSolveWaves) {
-                if (e < kC * 8) copy16(vrec + kRecP + (e >> 3) * 128 + 16 * (e & 7), sm.Ps + (e >> 3) * kKtLd + 8 * (e & 7));
-                else copy16(vrec + kRecTok + 16 * (e - kC * 8), &sm.tokS[0][0] + 4 * (e - kC * 8));
+            constexpr int kPaGran = kPaMat / 16;
+            for (int e = tid - 64 * kSolveWaves; e < kPaGran + kTokBytes / 16; e += kPrepThreads - 64 * kSolveWaves) {
+                if (e < kPaGran) {
+                    int row, g;
+                    pa_granule(16 * e, row, g);
+                    copy16(vrec + kRecP + 16 * e, sm.Ps + row * kKtLd + 8 * g);
+                } else {
+                    copy16(vrec + kRecTok + 16 * (e - kPaGran), &sm.tokS[0][0] + 4 * (e - kPaGran));
+                }
             }
         }
         __syncthreads();
-        for (int e = tid; e < kC * 8; e += kPrepThreads)
-            copy16(vrec + kRecAN + (e >> 3) * 128 + 16 * (e & 7), sm.AN + (e >> 3) * kKtLd + 8 * (e & 7));
+        for (int e = tid; e < kPaMat / 16; e += kPrepThreads) {
+            int row, g;
+            pa_granule(16 * e, row, g);
+            copy16(vrec + kRecAN + 16 * e, sm.AN + row * kKtLd + 8 * g);
+        }
         if (hh + 1 < r) __syncthreads();
     }
 }
@@ -315,15 +346,6 @@ void prep_kernel_varlen(VarlenParams vp) {
 // ============================================================ state kernel
 #define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
 
-// P and AN in LDS hold only their lower triangle of 16x16 tiles: rows 0..31
-// keep granules 0..3 (64-byte rows), rows 32..63 all eight (128-byte rows).
-// Granules are XOR-swizzled so that eight consecutive rows read by one phase
-// of an LDS read hit eight different bank groups.
-constexpr int kPaMat = 32 * 64 + 32 * 128;          // 6144 bytes per matrix
-__device__ __forceinline__ int pa_off(int mat, int row, int g) {
-    return mat * kPaMat + (row < 32 ? row * 64 + 16 * (g ^ ((row >> 1) & 3))
-                                    : 2048 + (row - 32) * 128 + 16 * (g ^ (row & 7)));
-}
 
 // LDS buffer of one chunk: Q | K | P | AN | rows | V^T (V^T of the slice's
 // columns, row stride kVtLd).  K^T is read from K by transposing LDS reads.
@@ -347,17 +369,8 @@ __device__ __forceinline__ void issue_piece(char* lds, const char* krec, const c
         src = krec + (pc < kPiecesK ? kRecQ : kRecK) + swz256(row, s);
         dst = (pc < kPiecesK ? kBufQ : kBufK) + o;
     } else if (pc < kPiecesTok) {
-        const int o = (pc - kPiecesPA) * 1024 + 16 * lane;
-        const int mat = o / kPaMat, l = o % kPaMat;
-        int row, g;
-        if (l < 2048) {
-            row = l >> 6;
-            g = ((l >> 4) & 3) ^ ((row >> 1) & 3);
-        } else {
-            row = 32 + ((l - 2048) >> 7);
-            g = ((l >> 4) & 7) ^ (row & 7);
-        }
-        src = vrec + mat * (kC * kC * 2) + row * 128 + 16 * g;
+        const int o = (pc - kPiecesPA) * 1024 + 16 * lane;   // P | AN, stored in their LDS layout
+        src = vrec + kRecP + o;
         dst = kBufPA + o;
     } else {
         const int l = (pc - kPiecesTok) * 1024 + 16 * lane;

@@ -88,15 +88,18 @@ def test_checkpoint_plan_errors(G):
 
 def test_workspace_bytes(G):
     """B x (chunks a call of L tokens can span, from any start) x per-chunk
-    records (H_k x (Q, K) + H_v x (P, AN, row scales))."""
+    records (H_k x (Q, K) + H_v x (P, AN, row scales)); P and AN keep the
+    first 32 columns of rows 0..31 and all of rows 32..63 (their lower 16x16
+    tiles, with two upper ones to keep rows 0..31 equal)."""
     for B, Hk, Hv in ((1, 16, 48), (8, 16, 32), (2, 2, 6)):
-        per = B * (Hk * 2 * 64 * 128 * 2 + Hv * (2 * 64 * 64 * 2 + 5 * 64 * 4))
+        lower = 32 * 64 + 32 * 128      # rows 0..31 keep 32 columns, rows 32..63 all 64
+        per = B * (Hk * 2 * 64 * 128 * 2 + Hv * (2 * lower + 5 * 64 * 4))
         c = cfg(G, batch=B, num_k_heads=Hk, num_v_heads=Hv)
         for L in (0, 1, 2, 63, 64, 65, 127, 128, 16384):
             # brute force over the start offset inside a chunk
             span = max((((s + L - 1) // 64) - s // 64 + 1) if L else 0 for s in range(64))
             assert G.prefill_workspace_bytes(c, L) == span * per, (B, Hk, Hv, L)
-    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 17664)
+    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 13568)
 
 
 FAKE = 1 << 34  # aligned, far-apart addresses that are never dereferenced: every call below fails validation
@@ -247,7 +250,7 @@ def test_varlen_workspace_bytes_and_lookup(G):
     """Host-only helpers of the varlen path: workspace sizes per group of 64
     sequences, and the prefix-cache lookup's slot, position and offsets."""
     c = cfg(G, batch=3)
-    per1 = 16 * 32768 + 48 * 17664
+    per1 = 16 * 32768 + 48 * 13568
     # lengths 100 (start 0: 2 chunks), 0, 4096 (start 5: 65 chunks)
     assert G.prefill_varlen_workspace_bytes(c, [0, 100, 100, 4196], [0, 64, 5]) == 3 * 65 * per1
     assert G.prefill_varlen_workspace_bytes(c, [0, 0, 0, 0], [0, 0, 0]) == 0
@@ -304,7 +307,7 @@ def test_varlen_rejects_bad_arguments(G):
     assert call(c, ws=P(FAKE * 10 + 16)) == G.GDN_EINVAL              # 256-byte workspace alignment
     assert call(c, qkv=P(FAKE + 2)) == G.GDN_EINVAL
     assert call(c, interval=100) == G.GDN_EINVAL
-    assert call(c, ws_bytes=2 * (16 * 32768 + 48 * 17664) - 1) == G.GDN_ESPACE
+    assert call(c, ws_bytes=2 * (16 * 32768 + 48 * 13568) - 1) == G.GDN_ESPACE
     assert call(c, interval=64) == G.GDN_EINVAL                       # checkpoints need a buffer
     assert call(c, interval=64, ck=P(FAKE * 11), ck_bytes=256) == G.GDN_ESPACE
     assert call(cfg(G, batch=2, io_dtype=G.GDN_F32)) == G.GDN_EUNSUPPORTED

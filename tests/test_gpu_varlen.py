@@ -107,7 +107,7 @@ def test_varlen_equals_single_calls(G, segmented):
         c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
         ws = torch.empty(G.prefill_varlen_workspace_bytes(c, [0, 1] + [1] * 7, [0] * 8) // 1,
                          dtype=torch.uint8, device="cuda")
-        assert ws.numel() == 8 * (2 * 32768 + 4 * 17664)
+        assert ws.numel() == 8 * (2 * 32768 + 4 * 13568)
     c, out, conv, S, _ = run_varlen(G, w, inp, qkv, a, b, LENS, STARTS, workspace=ws)
     check_against_singles(G, w, inp, LENS, STARTS, out, conv, S)
     assert finite(out, S)
