@@ -74,8 +74,9 @@ enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 /* Layer shape and numerics.  Supported today: conv_kernel 4, chunk 64;
- * prefill: d_k = d_v = 128, io GDN_BF16; decode: d_k, d_v in {32, 64, 128},
- * io GDN_F32 or GDN_BF16. */
+ * prefill: d_k = d_v = 128, io GDN_BF16, B * H_v <= 2^20; decode: d_k, d_v
+ * in {32, 64, 128}, io GDN_F32 or GDN_BF16, B and H_v <= 65535.  Larger
+ * shapes get GDN_EUNSUPPORTED (they would exceed a launch's grid). */
 typedef struct gdn_config {
     int32_t batch;        /* B >= 0                                          */
     int32_t num_k_heads;  /* H_k >= 1                                        */
@@ -291,7 +292,8 @@ gdn_status gdn_decode_gated(const gdn_config* cfg, int32_t num_tokens, const voi
  *               or z exactly (in place), no other overlap
  *   norm_w      [d_v] io, 16-byte aligned
  *   eps         >= 0, finite (the models use 1e-6)
- * Supported: d_v in {32, 64, 128}, io GDN_F32 or GDN_BF16.  Only
+ * Supported: d_v in {32, 64, 128}, io GDN_F32 or GDN_BF16, num_tokens *
+ * H_v <= 2^28 (else GDN_EUNSUPPORTED).  Only
  * cfg->num_v_heads, head_v_dim and io_dtype are used (the rest of cfg must
  * still be valid). */
 gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void* o, const void* z,

@@ -18,6 +18,14 @@ uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int io_size(int32_t io) { return io == GDN_BF16 ? 2 : 4; }
 
+// The prefill kernels launch about 4 B H_v workgroups of 512 threads, and a
+// launch's work-items along x must stay below 2^32: B H_v <= 2^20 keeps
+// every prefill grid below 2^23 workgroups.
+constexpr int64_t kMaxPrefillHeads = (int64_t)1 << 20;
+// The output gate launches 256-thread workgroups of 4096 / d_v rows, 8 *
+// rows work-items at d_v = 128: rows <= 2^28 keeps them below 2^31.
+constexpr int64_t kMaxGateRows = (int64_t)1 << 28;
+
 // Config checks shared by every entry point (shape sanity only; support for
 // a particular shape is checked per path).
 gdn_status check_config(const gdn_config* c) {
@@ -148,6 +156,7 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     if (!gdn::prefill_supported(cfg->head_k_dim, cfg->head_v_dim, cfg->io_dtype, cfg->conv_kernel,
                                 cfg->chunk))
         return GDN_EUNSUPPORTED;
+    if ((int64_t)cfg->batch * cfg->num_v_heads > kMaxPrefillHeads) return GDN_EUNSUPPORTED;
 
     const int64_t B = cfg->batch, L = seq_len, Hv = cfg->num_v_heads;
     const int64_t cd = conv_dim_of(cfg);
@@ -431,6 +440,7 @@ gdn_status gdn_prefill_varlen(const gdn_config* cfg, const int64_t* cu_seqlens, 
                                 cfg->chunk))
         return GDN_EUNSUPPORTED;
     if (cfg->num_v_heads / cfg->num_k_heads > 8) return GDN_EUNSUPPORTED;
+    if (B * Hv > kMaxPrefillHeads) return GDN_EUNSUPPORTED;
     if (B > 0 && workspace_bytes < gdn::prefill_varlen_group_bytes((int)B, cfg->num_k_heads, cfg->num_v_heads))
         return GDN_ESPACE;
 
@@ -533,9 +543,8 @@ gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void
     if (gdn_status s = check_config(cfg)) return s;
     if (num_tokens < 0 || !std::isfinite(eps) || eps < 0.f) return GDN_EINVAL;
     if (!gdn::gate_supported(cfg->head_v_dim, cfg->io_dtype)) return GDN_EUNSUPPORTED;
+    if (num_tokens > kMaxGateRows / cfg->num_v_heads) return GDN_EUNSUPPORTED;
     const int64_t rows = num_tokens * cfg->num_v_heads;
-    // the grid (at least 64 rows per workgroup) stays below 2^31 workgroups
-    if (num_tokens > ((int64_t)1 << 36) / cfg->num_v_heads) return GDN_EUNSUPPORTED;
     if (!norm_w || !aligned16(norm_w)) return GDN_EINVAL;
     if (rows > 0 && (!o || !z || !y)) return GDN_EINVAL;
     if (!aligned16(o) || !aligned16(z) || !aligned16(y)) return GDN_EINVAL;

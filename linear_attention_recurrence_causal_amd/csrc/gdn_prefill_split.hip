@@ -921,10 +921,12 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
     const uint64_t per = prefill_split_chunk_bytes(p.batch, p.num_k_heads, p.num_v_heads);
     const int64_t k_first = p.start_pos / kC;
     const int64_t k_end = p.seq_len > 0 ? (p.start_pos + p.seq_len - 1) / kC + 1 : k_first;
-    // segments of at most 2^30 / (B H_k) chunks keep the prep grid in range
+    // segments of at most 2^22 / (B H_k) chunks keep the prep grid's
+    // work-items below 2^31 (B H_k <= 2^20, so a segment holds a chunk)
     int64_t max_seg = (int64_t)(ws_bytes / per);
-    const int64_t grid_cap = ((int64_t)1 << 30) / ((int64_t)p.batch * p.num_k_heads);
+    const int64_t grid_cap = ((int64_t)1 << 22) / ((int64_t)p.batch * p.num_k_heads);
     if (max_seg > grid_cap) max_seg = grid_cap;
+    if (max_seg < 1) return hipErrorInvalidValue;
     SplitParams sp{};
     sp.p = p;
     sp.ws = static_cast<char*>(ws);
@@ -980,7 +982,7 @@ hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqle
             if (n > max_n) max_n = n;
         }
         int64_t seg = (int64_t)(ws_bytes / prefill_split_chunk_bytes(G, p.num_k_heads, p.num_v_heads));
-        const int64_t grid_cap = ((int64_t)1 << 30) / ((int64_t)G * p.num_k_heads);
+        const int64_t grid_cap = ((int64_t)1 << 22) / ((int64_t)G * p.num_k_heads);
         if (seg > max_n) seg = max_n;
         if (seg > grid_cap) seg = grid_cap;
         if (seg < 1) seg = 1;

@@ -133,6 +133,10 @@ def test_prefill_rejects_unsupported_and_aliasing(G):
     assert f(*prefill_args(G, cfg(G, head_k_dim=64, head_v_dim=64))) == G.GDN_EUNSUPPORTED
     assert f(*prefill_args(G, cfg(G, io_dtype=G.GDN_F32))) == G.GDN_EUNSUPPORTED
     assert f(*prefill_args(G, cfg(G, conv_kernel=3))) == G.GDN_EUNSUPPORTED
+    # B * H_v above 2^20 would take a grid past the launch limits
+    assert f(*prefill_args(G, cfg(G, batch=1 << 15, num_k_heads=16, num_v_heads=48))) == G.GDN_EUNSUPPORTED
+    # 2^20 itself passes this check and fails the next (the fake buffers overlap at that size)
+    assert f(*prefill_args(G, cfg(G, batch=1 << 14, num_k_heads=16, num_v_heads=64))) == G.GDN_EALIAS
     # conv_state_out on top of conv_state_in
     P = ctypes.c_void_p
     assert f(*prefill_args(G, cfg(G), cin=P(FAKE * 7))) == G.GDN_EALIAS
@@ -214,6 +218,8 @@ def test_output_gate_rejects_bad_arguments(G):
     assert call(c, y=P(FAKE * 4 + 8)) == G.GDN_EINVAL
     assert call(cfg(G, head_v_dim=96)) == G.GDN_EUNSUPPORTED
     assert call(cfg(G, io_dtype=7)) == G.GDN_EINVAL
+    # num_tokens * H_v above 2^28 rows
+    assert call(c, n=(1 << 28) // c.num_v_heads + 1) == G.GDN_EUNSUPPORTED
     # in place is exact equality only; a shifted y overlaps o, and y over the weights
     assert call(c, y=P(FAKE + 256)) == G.GDN_EALIAS
     assert call(c, y=P(FAKE * 2 + 4096)) == G.GDN_EALIAS
@@ -312,6 +318,8 @@ def test_varlen_rejects_bad_arguments(G):
     assert call(c, interval=64, ck=P(FAKE * 11), ck_bytes=256) == G.GDN_ESPACE
     assert call(cfg(G, batch=2, io_dtype=G.GDN_F32)) == G.GDN_EUNSUPPORTED
     assert call(cfg(G, batch=2, num_k_heads=4, num_v_heads=48)) == G.GDN_EUNSUPPORTED   # group of 12
+    big = 1 << 15                                                     # B * H_v above 2^20
+    assert call(cfg(G, batch=big), cu=[64 * i for i in range(big + 1)], st=[0] * big) == G.GDN_EUNSUPPORTED
     # outputs over the packed inputs, the workspace over an output
     assert call(c, out=P(FAKE + 4096)) == G.GDN_EALIAS
     assert call(c, cout=P(FAKE * 3)) == G.GDN_EALIAS
