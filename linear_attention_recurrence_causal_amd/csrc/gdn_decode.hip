@@ -42,9 +42,10 @@ constexpr int kDecodeThreads = 256;
 
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
 // whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
-// multi-token step, four waves per SIMD, its tokens' inputs parked in LDS).  The arithmetic per token is the same in both, so T
-// tokens in one call equal T one-token calls bit for bit.  GATE: also write
-// the gated output (NCOL must be d_v).
+// multi-token step, four waves per SIMD).  Every token's conv, norms and
+// gates are formed before the token loop, into LDS.  The arithmetic per
+// token is the same in both, so T tokens in one call equal T one-token calls
+// bit for bit.  GATE: also write the gated output (NCOL must be d_v).
 template <typename IO, int DK, int NCOL, int MAXT, bool GATE, int THREADS = kDecodeThreads>
 __global__ __launch_bounds__(THREADS, MAXT > 1 ? 4 : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
 void decode_step_kernel(DecodeParams p) {
@@ -57,15 +58,13 @@ void decode_step_kernel(DecodeParams p) {
     constexpr int NWAVES = THREADS / 64;
     constexpr int CPT = (NCH + THREADS - 1) / THREADS;   // channels per thread
 
-    __shared__ float u_s[NCH];                    // conv+SiLU outputs (io-rounded)
+    __shared__ float u_s[MAXT][NCH];              // conv+SiLU outputs (io-rounded) per token
     __shared__ float red_s[2][NWAVES][NCOL];      // cross-wave partial sums
     __shared__ __align__(16) float delta_s[NCOL];
-    __shared__ float scal_s[4];                   // n_q, n_k, k.q (unnormalised), g
-    __shared__ float beta_s;
+    __shared__ float scal_s[MAXT][4];             // per token: q.q, k.k, k.q (unnormalised), g
+    __shared__ float beta_s[MAXT];
     __shared__ float gsum_s[NWAVES];              // gate: per-wave sums of o^2
     __shared__ float gzw_s[GATE ? MAXT : 1][GATE ? NCOL : 1];   // gate: w silu(z) per token and column
-    __shared__ float xin_s[MAXT > 1 ? MAXT : 1][MAXT > 1 ? NCH : 1];   // multi-token: pre-conv inputs
-    __shared__ float gab_s[MAXT > 1 ? MAXT : 1][2];                    // multi-token: gate inputs a, b
 
     const int tid = threadIdx.x;
     const int z = blockIdx.x;                     // column slice
@@ -153,38 +152,22 @@ void decode_step_kernel(DecodeParams p) {
             if (t < ntok) gzw_s[t][tid] = gw * silu_f32(zin[t]);
     }
 
-    // the multi-token step parks its tokens' inputs in LDS, so that they do
-    // not stay in registers through the state arithmetic
-    if (MAXT > 1) {
+    // ---- 3. every token's front end, none of which depends on the state, so
+    // it runs while the state is in flight and leaves two barriers per token
+    // to the token loop.  Conv + SiLU of the slice's channels (io-rounded)
+    // into u_s[t]; the carried tail moves on token by token (to that token's
+    // conv snapshot, and after the last token to conv_out).
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int i = tid + k * THREADS;
-            if (i < NCH)
-#pragma unroll
-                for (int t = 0; t < MAXT; ++t)
-                    if (t < ntok) xin_s[t][i] = xin[k][t];
-        }
-        if (wave == 3 && lane == 0)
-#pragma unroll
-            for (int t = 0; t < MAXT; ++t)
-                if (t < ntok) {
-                    gab_s[t][0] = gate_a[t];
-                    gab_s[t][1] = gate_b[t];
-                }
-    }
-
-    for (int t = 0; t < ntok; ++t) {
-        // conv + SiLU of the slice's channels (io-rounded); the carried tail
-        // moves one token on (to this token's conv snapshot, and after the
-        // last token to conv_out)
+    for (int t = 0; t < MAXT; ++t) {
+        if (t >= ntok) break;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const int i = tid + k * THREADS;
             if (i < NCH) {
-                const float x = MAXT == 1 ? xin[k][0] : xin_s[t][i];
+                const float x = xin[k][t];
                 const float y = fmaf(taps[k][3], x, fmaf(taps[k][2], hist[k][2],
                                                          fmaf(taps[k][1], hist[k][1], taps[k][0] * hist[k][0])));
-                u_s[i] = T::round(silu_f32(y));
+                u_s[t][i] = T::round(silu_f32(y));
                 hist[k][0] = hist[k][1];
                 hist[k][1] = hist[k][2];
                 hist[k][2] = x;
@@ -200,29 +183,36 @@ void decode_step_kernel(DecodeParams p) {
                 }
             }
         }
-        __syncthreads();
-
-        // ---- 3. norms, k.q and the gates (one wave each, fixed order)
-        if (wave < 3) {
-            float acc = 0.f;
-            for (int i = lane; i < DK; i += 64) {
-                const float qv = u_s[i], kv = u_s[DK + i];
-                acc += wave == 0 ? qv * qv : (wave == 1 ? kv * kv : qv * kv);
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) scal_s[wave] = acc;
-        } else if (wave == 3 && lane == 0) {   // the lane that loaded the gates
-            const float ga = MAXT == 1 ? gate_a[0] : gab_s[t][0];
-            const float gb = MAXT == 1 ? gate_b[0] : gab_s[t][1];
-            scal_s[3] = neg_A * softplus_f32(ga + dt_h);
-            beta_s = sigmoid_f32(gb);
+    }
+    __syncthreads();
+    // q.q, k.k and k.q of every token (item 3t + kind, one wave each, fixed
+    // order), and the gates (the lane that loaded them)
+    for (int it = wave; it < 3 * ntok; it += NWAVES) {
+        const int t = it / 3, kind = it % 3;
+        float acc = 0.f;
+        for (int i = lane; i < DK; i += 64) {
+            const float qv = u_s[t][i], kv = u_s[t][DK + i];
+            acc = fmaf(kind == 1 ? kv : qv, kind == 0 ? qv : kv, acc);
         }
-        __syncthreads();
-        const float n_q = p.q_scale / sqrtf(scal_s[0] + p.l2_eps);
-        const float n_k = 1.0f / sqrtf(scal_s[1] + p.l2_eps);
-        const float kq = scal_s[2] * n_q * n_k;        // k_hat . q_hat
-        const float decay = expf(scal_s[3]);
-        const float beta = beta_s;
+        acc = wave_sum(acc);
+        if (lane == 0) scal_s[t][kind] = acc;
+    }
+    if (wave == 3 && lane == 0) {
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t)
+            if (t < ntok) {
+                scal_s[t][3] = neg_A * softplus_f32(gate_a[t] + dt_h);
+                beta_s[t] = sigmoid_f32(gate_b[t]);
+            }
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntok; ++t) {
+        const float n_q = p.q_scale / sqrtf(scal_s[t][0] + p.l2_eps);
+        const float n_k = 1.0f / sqrtf(scal_s[t][1] + p.l2_eps);
+        const float kq = scal_s[t][2] * n_q * n_k;     // k_hat . q_hat
+        const float decay = expf(scal_s[t][3]);
+        const float beta = beta_s[t];
 
         // ---- 4. S' = exp(g) S; partial S'^T k and S'^T q over this thread's rows
         float kv[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -230,8 +220,8 @@ void decode_step_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = rg + i * NRG;
-            const float kk = u_s[DK + row] * n_k;
-            const float qq = u_s[row] * n_q;
+            const float kk = u_s[t][DK + row] * n_k;
+            const float qq = u_s[t][row] * n_q;
             krow[i] = kk;
             S[i].x *= decay; S[i].y *= decay; S[i].z *= decay; S[i].w *= decay;
             kv[0] = fmaf(S[i].x, kk, kv[0]); kv[1] = fmaf(S[i].y, kk, kv[1]);
@@ -264,7 +254,7 @@ void decode_step_kernel(DecodeParams p) {
             float skv = 0.f, soq = 0.f;
 #pragma unroll
             for (int w = 0; w < NWAVES; ++w) { skv += red_s[0][w][tid]; soq += red_s[1][w][tid]; }
-            const float vv = u_s[2 * DK + tid];
+            const float vv = u_s[t][2 * DK + tid];
             const float d = beta * (vv - skv);
             delta_s[tid] = d;
             o = fmaf(d, kq, soq);
