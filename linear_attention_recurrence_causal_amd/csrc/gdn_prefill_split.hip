@@ -158,19 +158,33 @@ __device__ __forceinline__ void copy16(char* dst, const void* src) {
 constexpr int kPrepWaves = 8;
 constexpr int kPrepThreads = 64 * kPrepWaves;
 
-struct alignas(16) PrepSmem {
-    __bf16 Qs[kC * kKsLd];
-    __bf16 Ks[kC * kKsLd];
+// One value head's masked matrices, diagonal blocks and row scales.
+struct alignas(16) PrepHeadBuf {
     __bf16 Ps[kC * kKtLd];
     __bf16 AN[kC * kKtLd];
     float AdT[4 * 16 * kXLd];
+    float tokS[5][kC];
+};
+
+// Q and K are dead once their record is written and the Gram tiles are in
+// registers, so a second head buffer shares their space: one value head is
+// solved while the next one's masks are formed.
+struct alignas(16) PrepSmem {
+    union {
+        struct {
+            __bf16 Qs[kC * kKsLd];
+            __bf16 Ks[kC * kKsLd];
+        };
+        PrepHeadBuf hb1;
+    };
+    PrepHeadBuf hb0;
     alignas(16) float beta[kMaxGroup][kC];   // per value head of the group
     alignas(16) float gam[kMaxGroup][kC];
     alignas(16) float nq[kC];
     alignas(16) float nk[kC];
-    float tokS[5][kC];
     uint16_t Ws[4 * 2 * kD];   // conv taps (bf16 bits) [tap][channel]: q, then k
 };
+static_assert(sizeof(PrepHeadBuf) <= 2 * kC * kKsLd * 2, "the second head buffer fits in Q and K");
 
 // One value head's view of the prep LDS, in the member names the shared
 // mask, row-scale and solve helpers use.
@@ -219,12 +233,26 @@ __device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm,
     for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<bf16x4*>(dst0 + (tau0 + tt) * kKsLd) = ub[tt];
 }
 
+// Zero the upper tiles of a head buffer's P and AN (the masks never write
+// them) and the unused part of its fifth row of scales.
+__device__ __forceinline__ void zero_upper(PrepHeadBuf& hb, int tid) {
+    for (int e = tid; e < 6 * 256; e += kPrepThreads) {
+        const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
+        const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
+        const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
+        hb.Ps[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
+        hb.AN[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
+    }
+    if (tid < kC) hb.tokS[4][tid] = 0.f;
+}
+
 // Chunk j of the segment for sequence b (record-sequence rb) and key head kh
 template <bool NEUMANN>
 __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, int kh, int j) {
     const PrefillParams& p = sp.p;
     __shared__ PrepSmem sm;
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    // wave index in a scalar register: branches on it are uniform
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
     const int li = lane % 16, lq = lane / 16;
     const int Hk = p.num_k_heads, r = p.num_v_heads / Hk;
     const int64_t local0 = (sp.k0 + j) * kC - p.start_pos;
@@ -234,8 +262,7 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
     prep_front_load(p, b, kh, local0, interior, tid, raw);
 
     // ---- set-up: gates of every value head of the group (wave hh: head
-    // kh r + hh); conv taps -> LDS; zero the upper tiles of P and AN (the
-    // masks never write them) and the unused part of the fifth row
+    // kh r + hh); conv taps -> LDS; the first head buffer's zeros
     if (wave < r) {
         const int h = kh * r + wave;
         gates_scan(p, b, h, -expf(p.A_log[h]), p.dt_bias[h], local0, lane, sm.gam[wave], sm.beta[wave]);
@@ -244,14 +271,7 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
         const int ch = e % (2 * kD), tap = e / (2 * kD);
         sm.Ws[e] = static_cast<const uint16_t*>(p.conv_w)[qk_channel(ch, kh, Hk) * 4 + tap];
     }
-    for (int e = tid; e < 6 * 256; e += kPrepThreads) {
-        const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
-        const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
-        const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
-        sm.Ps[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
-        sm.AN[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
-    }
-    if (tid < kC) sm.tokS[4][tid] = 0.f;
+    zero_upper(sm.hb0, tid);
     __syncthreads();
 
     // ---- front end of q, k
@@ -270,54 +290,100 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
         const float n = row_inv_norm((isq ? sm.Qs : sm.Ks) + tau * kKsLd, isq ? p.q_scale : 1.0f, p.l2_eps);
         (isq ? sm.nq : sm.nk)[tau] = n;
     }
-    // wave w keeps the K K^T and Q K^T tiles of lower tile pairs w and w + 8
+    // The K K^T and Q K^T tiles of the ten lower tile pairs stay in the
+    // registers of the waves that mask them.  Substitution: waves 1..7 hold
+    // pairs wave - 1, waves 1..3 also pairs wave + 6, and wave 0, which
+    // solves, none.  Neumann product (solved by waves 0..3): wave w holds
+    // pair w, waves 0, 1 also pair w + 8.
+    const bool has0 = NEUMANN || wave >= 1;
+    const bool has1 = NEUMANN ? wave < 2 : (wave >= 1 && wave <= 3);
+    const int pa0 = NEUMANN ? wave : wave - 1, pa1 = NEUMANN ? wave + 8 : wave + 6;
     f32x4 gk[2], gq[2];
-    gk[0] = gram_tile(sm.Ks, sm.Qs, wave, li, lq);
-    gq[0] = gram_tile(sm.Ks, sm.Qs, 10 + wave, li, lq);
-    if (wave < 2) {
-        gk[1] = gram_tile(sm.Ks, sm.Qs, 8 + wave, li, lq);
-        gq[1] = gram_tile(sm.Ks, sm.Qs, 18 + wave, li, lq);
+    if (has0) {
+        gk[0] = gram_tile(sm.Ks, sm.Qs, pa0, li, lq);
+        gq[0] = gram_tile(sm.Ks, sm.Qs, 10 + pa0, li, lq);
+    }
+    if (has1) {
+        gk[1] = gram_tile(sm.Ks, sm.Qs, pa1, li, lq);
+        gq[1] = gram_tile(sm.Ks, sm.Qs, 10 + pa1, li, lq);
     }
     __syncthreads();
 
-    // ---- per value head of the group: masks, row scales, diagonal
-    // inverses -> value record
-    for (int hh = 0; hh < r; ++hh) {
-        char* vrec = val_rec(sp, rb, kh * r + hh, j);
-        PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, sm.Ps, sm.AN, sm.AdT, sm.tokS};
-        mask_pair(hv, wave, gk[0], gq[0], lane);
-        if (wave < 2) mask_pair(hv, 8 + wave, gk[1], gq[1], lane);
+    // masks and row scales of value head hh of the group into a head buffer
+    auto mask_head = [&](int hh, PrepHeadBuf& hb) {
+        PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, hb.Ps, hb.AN, hb.AdT, hb.tokS};
+        if (has0) mask_pair(hv, pa0, gk[0], gq[0], lane);
+        if (has1) mask_pair(hv, pa1, gk[1], gq[1], lane);
         if (wave == kPrepWaves - 1) {
             row_scales(hv, lane);
-            if (lane == 0) sm.tokS[4][0] = expf(sm.gam[hh][kC - 1]);
+            if (lane == 0) hb.tokS[4][0] = expf(sm.gam[hh][kC - 1]);
         }
-        __syncthreads();
-        // diagonal inverses on wave 0 (substitution) or waves 0..3 (one
-        // block each, Neumann product) while the other waves copy P and the
-        // row scales
-        constexpr int kSolveWaves = NEUMANN ? 4 : 1;
-        if (wave < kSolveWaves) {
-            if (NEUMANN) diag_neumann(hv, wave, lane);
-            else diag_solve<true>(hv, lane);
-        } else {
-            constexpr int kPaGran = kPaMat / 16;
-            for (int e = tid - 64 * kSolveWaves; e < kPaGran + kTokBytes / 16; e += kPrepThreads - 64 * kSolveWaves) {
-                if (e < kPaGran) {
-                    int row, g;
-                    pa_granule(16 * e, row, g);
-                    copy16(vrec + kRecP + 16 * e, sm.Ps + row * kKtLd + 8 * g);
-                } else {
-                    copy16(vrec + kRecTok + 16 * (e - kPaGran), &sm.tokS[0][0] + 4 * (e - kPaGran));
-                }
+    };
+    // P and the row scales of a head buffer -> value record (granules e0,
+    // e0 + stride, ...), and AN
+    constexpr int kPaGran = kPaMat / 16;
+    auto copy_p_tok = [&](char* vrec, const PrepHeadBuf& hb, int e0, int stride) {
+        for (int e = e0; e < kPaGran + kTokBytes / 16; e += stride) {
+            if (e < kPaGran) {
+                int row, g;
+                pa_granule(16 * e, row, g);
+                copy16(vrec + kRecP + 16 * e, hb.Ps + row * kKtLd + 8 * g);
+            } else {
+                copy16(vrec + kRecTok + 16 * (e - kPaGran), &hb.tokS[0][0] + 4 * (e - kPaGran));
             }
         }
-        __syncthreads();
-        for (int e = tid; e < kPaMat / 16; e += kPrepThreads) {
+    };
+    auto copy_an = [&](char* vrec, const PrepHeadBuf& hb, int e0, int stride) {
+        for (int e = e0; e < kPaGran; e += stride) {
             int row, g;
             pa_granule(16 * e, row, g);
-            copy16(vrec + kRecAN + 16 * e, sm.AN + row * kKtLd + 8 * g);
+            copy16(vrec + kRecAN + 16 * e, hb.AN + row * kKtLd + 8 * g);
         }
-        if (hh + 1 < r) __syncthreads();
+    };
+
+    if (NEUMANN) {
+        // per value head: masks, then the diagonal inverses on waves 0..3
+        // while waves 4..7 copy P and the row scales, then AN
+        for (int hh = 0; hh < r; ++hh) {
+            char* vrec = val_rec(sp, rb, kh * r + hh, j);
+            mask_head(hh, sm.hb0);
+            __syncthreads();
+            if (wave < 4) {
+                PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, sm.hb0.Ps, sm.hb0.AN, sm.hb0.AdT, sm.hb0.tokS};
+                diag_neumann(hv, wave, lane);
+            } else {
+                copy_p_tok(vrec, sm.hb0, tid - 256, kPrepThreads - 256);
+            }
+            __syncthreads();
+            copy_an(vrec, sm.hb0, tid, kPrepThreads);
+            if (hh + 1 < r) __syncthreads();
+        }
+    } else {
+        // software pipeline over the value heads, one barrier per head: wave
+        // 0 solves head hh's diagonal blocks and copies its AN, while waves
+        // 1..7 copy its P and row scales and form head hh + 1's masks in the
+        // other buffer
+        zero_upper(sm.hb1, tid);
+        mask_head(0, sm.hb0);
+        __syncthreads();
+        for (int hh = 0; hh < r; ++hh) {
+            PrepHeadBuf& cur = hh & 1 ? sm.hb1 : sm.hb0;
+            PrepHeadBuf& nxt = hh & 1 ? sm.hb0 : sm.hb1;
+            char* vrec = val_rec(sp, rb, kh * r + hh, j);
+            if (wave == 0) {
+                PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, cur.Ps, cur.AN, cur.AdT, cur.tokS};
+                diag_solve<true>(hv, lane);
+                // this wave's own LDS writes are read back in order; keep the
+                // compiler from moving the reads above them
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                copy_an(vrec, cur, lane, 64);
+            } else {
+                copy_p_tok(vrec, cur, tid - 64, kPrepThreads - 64);
+                if (hh + 1 < r) mask_head(hh + 1, nxt);
+            }
+            if (hh + 1 < r) __syncthreads();
+        }
     }
 }
 
