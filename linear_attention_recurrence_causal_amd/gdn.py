@@ -116,6 +116,17 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A tensor the call allocates for its outputs or workspace.  When the call
+    runs on a stream other than the current one, the tensor is recorded on that
+    stream, so that the caching allocator does not hand its memory to other work
+    while the call's kernels may still use it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
 def _check(t, name, shape, dtype, optional=False):
     if t is None:
         if optional:
@@ -180,11 +191,11 @@ def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_i
     _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
     dev = qkv.device
     if out is None:
-        out = torch.empty((B, L, Hv, dv), dtype=io, device=dev)
+        out = _empty((B, L, Hv, dv), io, dev, stream)
     if conv_state_out is None:
-        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_state_out = _empty((B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     if rec_state_out is None:
-        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_state_out = _empty((B, Hv, dk, dv), torch.float32, dev, stream)
     _check(out, "out", (B, L, Hv, dv), io)
     _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
     _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
@@ -197,7 +208,7 @@ def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_i
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
         ws = prefill_workspace_bytes(cfg, L)
-        wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        wsbuf = _empty(ws, torch.uint8, dev, stream) if ws else None
     elif workspace is None:
         ws, wsbuf = 0, None
     else:
@@ -232,11 +243,11 @@ def decode_step(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=No
     _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
     dev = qkv.device
     if out is None:
-        out = torch.empty((B, Hv, dv), dtype=io, device=dev)
+        out = _empty((B, Hv, dv), io, dev, stream)
     if conv_state_out is None:
-        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_state_out = _empty((B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     if rec_state_out is None:
-        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_state_out = _empty((B, Hv, dk, dv), torch.float32, dev, stream)
     _check(out, "out", (B, Hv, dv), io)
     _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
     _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
@@ -275,15 +286,15 @@ def decode_multi(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=N
     _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
     dev = qkv.device
     if out is None:
-        out = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+        out = _empty((B, T, Hv, dv), io, dev, stream)
     if conv_state_out is None:
-        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_state_out = _empty((B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     if rec_state_out is None:
-        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_state_out = _empty((B, Hv, dk, dv), torch.float32, dev, stream)
     if snapshots and rec_snapshots is None:
-        rec_snapshots = torch.empty((T, B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_snapshots = _empty((T, B, Hv, dk, dv), torch.float32, dev, stream)
     if snapshots and conv_snapshots is None:
-        conv_snapshots = torch.empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_snapshots = _empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     _check(out, "out", (B, T, Hv, dv), io)
     _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
     _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
@@ -315,7 +326,7 @@ def output_gate(cfg: Config, o, z, norm_w, eps: float = GATE_EPS, *, y=None, str
     _check(z, "z", shape, io)
     _check(norm_w, "norm_w", (dv,), io)
     if y is None:
-        y = torch.empty(shape, dtype=io, device=o.device)
+        y = _empty(shape, io, o.device, stream)
     _check(y, "y", shape, io)
     st = _lib.gdn_output_gate(ctypes.byref(cfg.c()), rows, _ptr(o), _ptr(z), _ptr(norm_w), eps, _ptr(y),
                               _stream(stream))
@@ -349,17 +360,17 @@ def decode_gated(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, z, norm_w, conv
     _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
     dev = qkv.device
     if y is None:
-        y = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+        y = _empty((B, T, Hv, dv), io, dev, stream)
     if out is None and want_out:
-        out = torch.empty((B, T, Hv, dv), dtype=io, device=dev)
+        out = _empty((B, T, Hv, dv), io, dev, stream)
     if conv_state_out is None:
-        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_state_out = _empty((B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     if rec_state_out is None:
-        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_state_out = _empty((B, Hv, dk, dv), torch.float32, dev, stream)
     if snapshots and rec_snapshots is None:
-        rec_snapshots = torch.empty((T, B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_snapshots = _empty((T, B, Hv, dk, dv), torch.float32, dev, stream)
     if snapshots and conv_snapshots is None:
-        conv_snapshots = torch.empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_snapshots = _empty((T, B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     _check(y, "y", (B, T, Hv, dv), io)
     _check(out, "out", (B, T, Hv, dv), io, True)
     _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
@@ -415,11 +426,11 @@ def prefill_varlen(cfg: Config, cu_seqlens, start_pos, qkv, a, b, conv_w, A_log,
     _check(rec_state_in, "rec_state_in", (B, Hv, dk, dv), torch.float32, True)
     dev = qkv.device
     if out is None:
-        out = torch.empty((T, Hv, dv), dtype=io, device=dev)
+        out = _empty((T, Hv, dv), io, dev, stream)
     if conv_state_out is None:
-        conv_state_out = torch.empty((B, cfg.conv_dim, cfg.conv_kernel - 1), dtype=io, device=dev)
+        conv_state_out = _empty((B, cfg.conv_dim, cfg.conv_kernel - 1), io, dev, stream)
     if rec_state_out is None:
-        rec_state_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        rec_state_out = _empty((B, Hv, dk, dv), torch.float32, dev, stream)
     _check(out, "out", (T, Hv, dv), io)
     _check(conv_state_out, "conv_state_out", (B, cfg.conv_dim, cfg.conv_kernel - 1), io)
     _check(rec_state_out, "rec_state_out", (B, Hv, dk, dv), torch.float32)
@@ -432,7 +443,7 @@ def prefill_varlen(cfg: Config, cu_seqlens, start_pos, qkv, a, b, conv_w, A_log,
         if workspace != "auto":
             raise ValueError("workspace must be 'auto' or a uint8 device tensor")
         ws = max(prefill_varlen_workspace_bytes(cfg, cu, sp), 256)
-        wsbuf = torch.empty(ws, dtype=torch.uint8, device=dev)
+        wsbuf = _empty(ws, torch.uint8, dev, stream)
     else:
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous device tensor")

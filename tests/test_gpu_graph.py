@@ -125,3 +125,27 @@ def test_graph_prefill_and_gate(G):
         torch.cuda.synchronize()
         for t, u in zip((out, conv, S, y), want):
             assert torch.equal(t, u), r
+
+
+def test_explicit_stream_argument(G):
+    """Calls made with stream= a side stream (outputs and the prefill
+    workspace allocated by the binding, recorded on that stream) equal the
+    same calls on the current stream bit for bit."""
+    w = I.Workload("side-stream", batch=2, seq_len=300, num_k_heads=2, num_v_heads=6, init_state=True,
+                   decode_steps=1, seed=72)
+    d = {k: (None if v is None else v.cuda()) for k, v in I.generate(w).items()}
+    c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    args = (d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"], d["conv_state"], d["rec_state"])
+    dec = (d["dec_qkv"][0], d["dec_a"][0], d["dec_b"][0], d["conv_w"], d["A_log"], d["dt_bias"],
+           d["conv_state"], d["rec_state"])
+    want_p = G.prefill_chunked(c, *args)
+    want_d = G.decode_step(c, *dec)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    got_p = G.prefill_chunked(c, *args, stream=s)
+    got_d = G.decode_step(c, *dec, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for x, y in zip(want_p + want_d, got_p + got_d):
+        assert torch.equal(x, y)
