@@ -170,6 +170,9 @@ def test_decode_rejects_bad_arguments(G):
     assert call(cfg(G), rout=P(FAKE * 8 + 4)) == G.GDN_EINVAL        # state needs 16 bytes
     assert call(cfg(G, head_k_dim=96)) == G.GDN_EUNSUPPORTED
     assert call(cfg(G, conv_kernel=2)) == G.GDN_EUNSUPPORTED
+    # the grid's y and z dimensions (heads, sequences) stay within 65535
+    assert call(cfg(G, batch=65536)) == G.GDN_EUNSUPPORTED
+    assert call(cfg(G, num_k_heads=1, num_v_heads=65536)) == G.GDN_EUNSUPPORTED
     assert call(cfg(G), cin=P(FAKE * 7)) == G.GDN_EALIAS
     # a partial overlap of the recurrent states is refused, exact equality is in place
     assert call(cfg(G), rin=P(FAKE * 8 + 256)) == G.GDN_EALIAS
