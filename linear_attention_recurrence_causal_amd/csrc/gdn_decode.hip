@@ -40,6 +40,15 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes) with raw byte offsets: one
+// 32-bit offset per lane addresses a whole state snapshot (the hardware drops
+// a store past the end instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t snap_rsrc(const float* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
 // whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
 // multi-token step, four waves per SIMD).  Every token's conv, norms and
@@ -47,7 +56,8 @@ constexpr int kDecodeThreads = 256;
 // token is the same in both, so T tokens in one call equal T one-token calls
 // bit for bit.  GATE: also write the gated output (NCOL must be d_v).
 template <typename IO, int DK, int NCOL, int MAXT, bool GATE, int THREADS = kDecodeThreads>
-__global__ __launch_bounds__(THREADS, MAXT > 1 ? 4 : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
+__global__ __launch_bounds__(THREADS, MAXT > 1 ? (THREADS == 512 && !GATE ? 6 : 4)
+                                               : (THREADS == 512 ? 6 : (NCOL == 64 && !GATE ? 7 : (NCOL == 128 ? 4 : 1))))
 void decode_step_kernel(DecodeParams p) {
     using T = io_traits<IO>;
     constexpr int NCQ = NCOL / 4;                 // column quads per slice
@@ -131,18 +141,25 @@ void decode_step_kernel(DecodeParams p) {
     }
 
     // ---- 2. the state slice (the bytes that matter), kept in registers for
-    // all the tokens
+    // all the tokens.  The one-token build requests it here, behind the
+    // front-end inputs, so that its front end runs while the state is in
+    // flight; the multi-token build requests it after its tokens' conv
+    // (below), so that the tokens' inputs and the state are not in registers
+    // together.
     const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * DK * dv + col0 + cq * 4;
     const int64_t state_elems = (int64_t)p.batch * p.num_v_heads * DK * dv;
     float4 S[RPT];
-    if (p.rec_in) {
+    auto load_state = [&] {
+        if (p.rec_in) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            S[i] = *reinterpret_cast<const float4*>(p.rec_in + s_base + (int64_t)(rg + i * NRG) * dv);
-    } else {
+            for (int i = 0; i < RPT; ++i)
+                S[i] = *reinterpret_cast<const float4*>(p.rec_in + s_base + (int64_t)(rg + i * NRG) * dv);
+        } else {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+            for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    if (MAXT == 1) load_state();
 
     // the gate factors w silu(z) go to LDS once, so that no gate input stays
     // in a register through the state arithmetic
@@ -184,6 +201,7 @@ void decode_step_kernel(DecodeParams p) {
             }
         }
     }
+    if (MAXT > 1) load_state();
     __syncthreads();
     // q.q, k.k and k.q of every token (item 3t + kind, one wave each, fixed
     // order), and the gates (the lane that loaded them)
@@ -216,13 +234,13 @@ void decode_step_kernel(DecodeParams p) {
 
         // ---- 4. S' = exp(g) S; partial S'^T k and S'^T q over this thread's rows
         float kv[4] = {0.f, 0.f, 0.f, 0.f}, oq[4] = {0.f, 0.f, 0.f, 0.f};
-        float krow[RPT];
+        float krow[MAXT == 1 ? RPT : 1];   // the multi-token build forms k again in step 6
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = rg + i * NRG;
             const float kk = u_s[t][DK + row] * n_k;
             const float qq = u_s[t][row] * n_q;
-            krow[i] = kk;
+            if (MAXT == 1) krow[i] = kk;
             S[i].x *= decay; S[i].y *= decay; S[i].z *= decay; S[i].w *= decay;
             kv[0] = fmaf(S[i].x, kk, kv[0]); kv[1] = fmaf(S[i].y, kk, kv[1]);
             kv[2] = fmaf(S[i].z, kk, kv[2]); kv[3] = fmaf(S[i].w, kk, kv[3]);
@@ -278,13 +296,19 @@ void decode_step_kernel(DecodeParams p) {
         const float4 dl = *reinterpret_cast<const float4*>(&delta_s[cq * 4]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            S[i].x = fmaf(krow[i], dl.x, S[i].x); S[i].y = fmaf(krow[i], dl.y, S[i].y);
-            S[i].z = fmaf(krow[i], dl.z, S[i].z); S[i].w = fmaf(krow[i], dl.w, S[i].w);
+            const float kk = MAXT == 1 ? krow[i] : u_s[t][DK + rg + i * NRG] * n_k;   // the same product
+            S[i].x = fmaf(kk, dl.x, S[i].x); S[i].y = fmaf(kk, dl.y, S[i].y);
+            S[i].z = fmaf(kk, dl.z, S[i].z); S[i].w = fmaf(kk, dl.w, S[i].w);
         }
         if (rec_snap) {
+            // snapshot t through a buffer resource: a uniform base and one
+            // 32-bit offset per lane, rather than a 64-bit address per row
+            const __amdgpu_buffer_rsrc_t rs = snap_rsrc(rec_snap + t * state_elems, state_elems * 4);
+            const int32_t off0 = (int32_t)((s_base + (int64_t)rg * dv) * 4);
 #pragma unroll
             for (int i = 0; i < RPT; ++i)
-                *reinterpret_cast<float4*>(rec_snap + t * state_elems + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4u32*>(&S[i]), rs,
+                                                       off0 + i * NRG * dv * 4, 0, 0);
         }
     }
 
