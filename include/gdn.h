@@ -24,9 +24,16 @@
  *     device) unless marked "host".  The library never allocates, frees or
  *     synchronises; it enqueues kernels on `stream` (a hipStream_t, NULL =
  *     the null stream) and returns.  It keeps no global mutable state.
- *   - Arguments are validated before anything is enqueued.  On an error
- *     nothing is enqueued and no output is touched.  No C++ exception crosses
- *     this boundary.
+ *   - Arguments are validated before anything is enqueued.  On a validation
+ *     error (GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIAS, GDN_ESPACE) nothing is
+ *     enqueued and no output is touched.  No C++ exception crosses this
+ *     boundary.
+ *   - GDN_EHIP means the HIP runtime refused a launch.  A call that launches
+ *     several kernels (a prefill run segment by segment through a small
+ *     workspace, a varlen prefill over several groups) stops at the first
+ *     refused launch and returns GDN_EHIP; the kernels launched before it
+ *     stay enqueued, so the outputs are then partly written and must be
+ *     treated as undefined.
  *   - Tensors are dense, row-major, with the shapes given below.  Every
  *     pointer needs the alignment of its element type; in addition qkv and
  *     out of gdn_prefill_chunked and both recurrent states of gdn_decode_step

@@ -42,11 +42,11 @@ constexpr int kDecodeThreads = 256;
 
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
-// Buffer resource over [base, base + bytes) with raw byte offsets: one
-// 32-bit offset per lane addresses a whole state snapshot (the hardware drops
-// a store past the end instead of faulting).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t snap_rsrc(const float* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource over one head's slice [base, base + bytes) of a state
+// snapshot, with raw byte offsets: one 32-bit offset per lane inside the
+// d_k x d_v slice (64 KiB at d = 128), whatever the snapshot's total size.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t snap_rsrc(const float* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
 }
 
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
@@ -146,7 +146,8 @@ void decode_step_kernel(DecodeParams p) {
     // flight; the multi-token build requests it after its tokens' conv
     // (below), so that the tokens' inputs and the state are not in registers
     // together.
-    const int64_t s_base = ((int64_t)b * p.num_v_heads + h) * DK * dv + col0 + cq * 4;
+    const int64_t head_base = ((int64_t)b * p.num_v_heads + h) * DK * dv;
+    const int64_t s_base = head_base + col0 + cq * 4;
     const int64_t state_elems = (int64_t)p.batch * p.num_v_heads * DK * dv;
     float4 S[RPT];
     auto load_state = [&] {
@@ -303,8 +304,8 @@ void decode_step_kernel(DecodeParams p) {
         if (rec_snap) {
             // snapshot t through a buffer resource: a uniform base and one
             // 32-bit offset per lane, rather than a 64-bit address per row
-            const __amdgpu_buffer_rsrc_t rs = snap_rsrc(rec_snap + t * state_elems, state_elems * 4);
-            const int32_t off0 = (int32_t)((s_base + (int64_t)rg * dv) * 4);
+            const __amdgpu_buffer_rsrc_t rs = snap_rsrc(rec_snap + t * state_elems + head_base, DK * dv * 4);
+            const int32_t off0 = (int32_t)((s_base - head_base + (int64_t)rg * dv) * 4);
 #pragma unroll
             for (int i = 0; i < RPT; ++i)
                 __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4u32*>(&S[i]), rs,

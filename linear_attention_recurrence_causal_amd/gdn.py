@@ -117,14 +117,18 @@ def _stream(stream):
 
 
 def _empty(shape, dtype, device, stream):
-    """A tensor the call allocates for its outputs or workspace.  When the call
-    runs on a stream other than the current one, the tensor is recorded on that
-    stream, so that the caching allocator does not hand its memory to other work
-    while the call's kernels may still use it."""
-    t = torch.empty(shape, dtype=dtype, device=device)
-    if stream is not None:
-        t.record_stream(stream)
-    return t
+    """A tensor the call allocates for its outputs or workspace.
+
+    Ordering contract: the call's kernels run on ``stream`` (the current
+    stream when None).  The tensor is allocated while that stream is current,
+    so the caching allocator hands out a block whose earlier users were all on
+    that stream, and the kernels that write it are ordered after them.  Reuse
+    of the block by other streams afterwards follows torch's usual rule for a
+    tensor that belongs to ``stream``."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _check(t, name, shape, dtype, optional=False):

@@ -107,6 +107,51 @@ def coincident_keys(w: Workload) -> Workload:
     return slow_decay(w).with_(key_common=10.0, b_shift=8.0, name=w.name + "-coincident")
 
 
+def orthonormal_keys(w: Workload, inp: dict, seed: int = 0) -> dict:
+    """Inputs of the store / retrieve / overwrite case (g = 0, beta = 1,
+    orthonormal keys): the q and k conv taps become the identity on the
+    current token (tap K-1 = 1, the others 0), each token's raw q and k rows
+    of a key head are 8 * a basis vector (seeded random index per token, so
+    keys repeat and overwrite earlier values, also inside a chunk), a is
+    pushed to -30 and b to +30 (softplus and sigmoid in their tails: decay 1,
+    beta 1 in fp32), and the initial state is zero.  After the conv, SiLU and
+    l2 norm the keys are unit basis vectors.  The v stream keeps its draws."""
+    gen = torch.Generator().manual_seed(seed + 31337)
+    out = dict(inp)
+    B, L, Hk, dk = w.batch, w.seq_len, w.num_k_heads, w.head_k_dim
+    kd = Hk * dk
+    qkv = inp["qkv"].clone()
+    qkv[:, :, : 2 * kd] = 0
+    for part in range(2):                      # q, then k
+        idx = torch.randint(0, dk, (B, L, Hk), generator=gen)
+        rows = torch.zeros(B, L, Hk, dk, dtype=qkv.dtype)
+        rows.scatter_(3, idx.unsqueeze(-1), 8.0)
+        qkv[:, :, part * kd:(part + 1) * kd] = rows.view(B, L, kd)
+    out["qkv"] = qkv
+    cw = inp["conv_w"].clone()
+    cw[: 2 * kd] = 0
+    cw[: 2 * kd, w.conv_kernel - 1] = 1
+    out["conv_w"] = cw
+    out["a"] = torch.full_like(inp["a"], -30.0)
+    out["b"] = torch.full_like(inp["b"], 30.0)
+    out["conv_state"] = None if inp["conv_state"] is None else torch.zeros_like(inp["conv_state"])
+    out["rec_state"] = None if inp["rec_state"] is None else torch.zeros_like(inp["rec_state"])
+    return out
+
+
+def zero_segments(inp: dict, segments) -> dict:
+    """The same inputs with every pre-conv channel of the given token ranges
+    [t0, t1) set to zero: the conv output, and with it q, k and v, is zero
+    from three tokens into a range until its end, so the l2 norm meets zero
+    vectors and the state only decays there."""
+    out = dict(inp)
+    qkv = inp["qkv"].clone()
+    for t0, t1 in segments:
+        qkv[:, t0:t1] = 0
+    out["qkv"] = qkv
+    return out
+
+
 def _randn(gen, shape, std, dtype):
     x = torch.randn(shape, generator=gen, dtype=torch.float32)
     if std != 1.0:

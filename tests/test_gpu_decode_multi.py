@@ -145,3 +145,36 @@ def test_multi_matches_oracle_per_token(G, w):
     for t in range(T):
         assert np.array_equal(I.to_numpy_io(csn[t]), ck[t]), t
     assert finite(out, So, rs)
+
+
+def test_multi_snapshots_beyond_4gib(G):
+    """One state snapshot of more than 4 GiB (B * H_v = 65,568 heads of
+    128 x 128): every head's snapshot slice is addressed from its own base,
+    so the heads at the end of the snapshot land where they belong.  Two
+    tokens in one call equal two one-token calls bit for bit, snapshots
+    included (checked on every head)."""
+    B, Hk, Hv, d, T = 1366, 16, 48, 128, 2
+    assert B * Hv * d * d * 4 > 4 * 2 ** 30
+    c = G.Config(batch=B, num_k_heads=Hk, num_v_heads=Hv, head_k_dim=d, head_v_dim=d, io_dtype=G.GDN_BF16)
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    bf = torch.bfloat16
+    qkv = torch.randn(B, T, c.conv_dim, device="cuda", generator=gen).to(bf)
+    a = torch.randn(B, T, Hv, device="cuda", generator=gen).to(bf)
+    b = torch.randn(B, T, Hv, device="cuda", generator=gen).to(bf)
+    conv_w = (0.5 * torch.randn(c.conv_dim, 4, device="cuda", generator=gen)).to(bf)
+    A_log = torch.log(1 + 15 * torch.rand(Hv, device="cuda", generator=gen))
+    dt_bias = 0.1 * torch.randn(Hv, device="cuda", generator=gen)
+    cs = torch.randn(B, c.conv_dim, 3, device="cuda", generator=gen).to(bf)
+    S0 = 0.05 * torch.randn(B, Hv, d, d, device="cuda", generator=gen)
+    print(f"[multi >4GiB] B={B} H_v={Hv}: snapshot {B * Hv * d * d * 4 / 2 ** 30:.3f} GiB per token",
+          flush=True)
+    out, cso, So, rs, csn = G.decode_multi(c, qkv, a, b, conv_w, A_log, dt_bias, cs, S0, snapshots=True)
+    o1, cs1, S1 = G.decode_step(c, qkv[:, 0].contiguous(), a[:, 0].contiguous(), b[:, 0].contiguous(),
+                                conv_w, A_log, dt_bias, cs, S0)
+    assert torch.equal(rs[0], S1) and torch.equal(csn[0], cs1)
+    del S0
+    o2, cs2, S2 = G.decode_step(c, qkv[:, 1].contiguous(), a[:, 1].contiguous(), b[:, 1].contiguous(),
+                                conv_w, A_log, dt_bias, cs1, S1)
+    assert torch.equal(rs[1], S2) and torch.equal(So, S2) and torch.equal(csn[1], cs2)
+    assert torch.equal(out[:, 0], o1) and torch.equal(out[:, 1], o2)
+    torch.cuda.synchronize()
