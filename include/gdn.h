@@ -80,6 +80,22 @@ enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/* Operand precision of the chunked prefill's MFMA products (the decode step
+ * is fp32 throughout and ignores it).
+ *   GDN_PRECISION_DEFAULT: raw bf16 q/k/v are exact MFMA operands, norms,
+ *     beta and decays are fp32 row scales, the product that builds the state
+ *     takes Delta as bf16 hi + lo; the other state-path operands (S0 in K S0
+ *     and Q S0, the triangular solve's coupling and diagonal blocks, P and
+ *     Delta in P Delta) are single bf16.
+ *   GDN_PRECISION_HILO: every one of those operands as bf16 hi + lo (about
+ *     16 significant bits; three MFMAs per product), for inputs where the
+ *     triangular solve cancels heavily (keys that nearly coincide, beta near
+ *     1, slow decay).  About 1.7x the state-path MFMA work, and 12.75 KiB
+ *     more workspace per value head and chunk.
+ * The solve is the stable direct one of the Qwen3.6-27B PR ("Known
+ * limitations and follow-ups") in both. */
+typedef enum { GDN_PRECISION_DEFAULT = 0, GDN_PRECISION_HILO = 1 } gdn_precision;
+
 /* Layer shape and numerics.  Supported today: conv_kernel 4, chunk 64;
  * prefill: d_k = d_v = 128, io GDN_BF16, B * H_v <= 2^20; decode: d_k, d_v
  * in {32, 64, 128}, io GDN_F32 or GDN_BF16, B and H_v <= 65535.  Larger
@@ -95,6 +111,7 @@ typedef struct gdn_config {
     int32_t io_dtype;     /* gdn_dtype                                       */
     float q_scale;        /* factor on the unit-norm query; 1 = the pages' rule */
     float l2_eps;         /* epsilon in x * (sum x^2 + eps)^(-1/2), >= 0      */
+    int32_t precision;    /* gdn_precision of the prefill (0 = default)        */
 } gdn_config;
 
 /* One emitted checkpoint slot.  Slot j holds the state after absolute

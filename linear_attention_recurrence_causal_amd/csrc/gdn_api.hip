@@ -36,6 +36,7 @@ gdn_status check_config(const gdn_config* c) {
         return GDN_EINVAL;
     if (c->io_dtype != GDN_F32 && c->io_dtype != GDN_BF16) return GDN_EINVAL;
     if (!std::isfinite(c->q_scale) || !std::isfinite(c->l2_eps) || c->l2_eps < 0.f) return GDN_EINVAL;
+    if (c->precision != GDN_PRECISION_DEFAULT && c->precision != GDN_PRECISION_HILO) return GDN_EINVAL;
     return GDN_OK;
 }
 
@@ -125,7 +126,7 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
     // seq_len tokens starting anywhere inside a chunk span at most
     // floor((seq_len + chunk - 2) / chunk) + 1 chunks
     const int64_t chunks = seq_len == 0 ? 0 : (seq_len + cfg->chunk - 2) / cfg->chunk + 1;
-    *bytes = (uint64_t)chunks * gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads);
+    *bytes = (uint64_t)chunks * gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads, cfg->precision == GDN_PRECISION_HILO);
     return GDN_OK;
 }
 
@@ -187,7 +188,7 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
 
     // The two-pass path needs at least one chunk of records in the
     // workspace; GDN_PREFILL_PATH=split|fused overrides the choice.
-    const uint64_t chunk_ws = gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads);
+    const uint64_t chunk_ws = gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads, cfg->precision == GDN_PRECISION_HILO);
     const bool ws_ok = workspace && chunk_ws > 0 && workspace_bytes >= chunk_ws &&
                        cfg->num_v_heads / cfg->num_k_heads <= 8;
     const char* path_env = getenv("GDN_PREFILL_PATH");
@@ -233,6 +234,7 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     // Neumann product instead of substitution
     const char* solve_env = getenv("GDN_DIAG_SOLVE");
     p.diag_neumann = solve_env && solve_env[0] == 'n';
+    p.precise = cfg->precision == GDN_PRECISION_HILO;
     const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream))
                                   : gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
@@ -397,7 +399,7 @@ static gdn_status varlen_shape(const gdn_config* cfg, const int64_t* cu_seqlens,
             const int64_t chunks = len > 0 ? (st + len - 1) / cfg->chunk + 1 - st / cfg->chunk : 0;
             if (chunks > max_n) max_n = chunks;
         }
-        const uint64_t g = (uint64_t)max_n * gdn::prefill_split_chunk_bytes(n, cfg->num_k_heads, cfg->num_v_heads);
+        const uint64_t g = (uint64_t)max_n * gdn::prefill_split_chunk_bytes(n, cfg->num_k_heads, cfg->num_v_heads, cfg->precision == GDN_PRECISION_HILO);
         if (g > need) need = g;
     }
     *ws_all = need;
@@ -441,7 +443,7 @@ gdn_status gdn_prefill_varlen(const gdn_config* cfg, const int64_t* cu_seqlens, 
         return GDN_EUNSUPPORTED;
     if (cfg->num_v_heads / cfg->num_k_heads > 8) return GDN_EUNSUPPORTED;
     if (B * Hv > kMaxPrefillHeads) return GDN_EUNSUPPORTED;
-    if (B > 0 && workspace_bytes < gdn::prefill_varlen_group_bytes((int)B, cfg->num_k_heads, cfg->num_v_heads))
+    if (B > 0 && workspace_bytes < gdn::prefill_varlen_group_bytes((int)B, cfg->num_k_heads, cfg->num_v_heads, cfg->precision == GDN_PRECISION_HILO))
         return GDN_ESPACE;
 
     const int64_t cd = conv_dim_of(cfg);
@@ -510,6 +512,7 @@ gdn_status gdn_prefill_varlen(const gdn_config* cfg, const int64_t* cu_seqlens, 
     p.l2_eps = cfg->l2_eps;
     const char* solve_env = getenv("GDN_DIAG_SOLVE");
     p.diag_neumann = solve_env && solve_env[0] == 'n';
+    p.precise = cfg->precision == GDN_PRECISION_HILO;
     if (B == 0) return GDN_OK;
     const hipError_t e = gdn::launch_prefill_varlen(p, cu_seqlens, start_pos, workspace, workspace_bytes,
                                                     static_cast<hipStream_t>(stream));

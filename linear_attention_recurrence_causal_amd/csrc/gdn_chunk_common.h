@@ -66,6 +66,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {
 
 __device__ __forceinline__ f32x8 to_f32x8(bf16x8 v) { return __builtin_convertvector(v, f32x8); }
 
+// bf16 hi + lo of fp32 values: hi = RNE(x), lo = RNE(x - hi); hi + lo carries
+// about 16 significant bits (the operands of the precise mode)
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = __bf16(x);
+    lo = __bf16(x - float(hi));
+}
+
+__device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    const f32x4 back = __builtin_convertvector(hi, f32x4);
+    lo = __builtin_convertvector(x - back, bf16x4);
+}
+
+__device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+    hi = to_bf16x8(a, b);
+    const f32x8 back = to_f32x8(hi);
+    const f32x4 la = {a[0] - back[0], a[1] - back[1], a[2] - back[2], a[3] - back[3]};
+    const f32x4 lb = {b[0] - back[4], b[1] - back[5], b[2] - back[6], b[3] - back[7]};
+    lo = to_bf16x8(la, lb);
+}
+
 // Column order inside Q, K (d_k columns) and K^T, P, AN (token columns).  An
 // index x = 32a + 16h + 4q + e is stored at 32a + 8q + 4h + e, so the eight
 // reduction slots that lane group q of v_mfma_f32_16x16x32_bf16 needs for
@@ -241,8 +262,9 @@ __device__ __forceinline__ f32x4 gram_tile(const __bf16* Ks, const __bf16* Qs, i
 //   A[r,i] = beta_r n_k[r] n_k[i] exp(gamma_r - gamma_i) (K K^T)[r,i], i < r
 //     -> -A (bf16) off the diagonal blocks, fp32 transposed on them
 //   P[r,i] = n_q[r] n_k[i] exp(gamma_r - gamma_i) (Q K^T)[r,i], i <= r (bf16)
-// SM provides gam, beta, nq, nk [64] and Ps, AN [64 x kKtLd], AdT.
-template <class SM>
+// SM provides gam, beta, nq, nk [64] and Ps, AN [64 x kKtLd], AdT; with
+// PRECISE also Ps_lo, AN_lo, which take the bf16 lo parts of P and -A.
+template <bool PRECISE = false, class SM>
 __device__ __forceinline__ void mask_pair(SM& sm, int pi, f32x4 g, f32x4 qk, int l) {
     const int li = l % 16, lq = l / 16;
     int m, pp;
@@ -259,9 +281,15 @@ __device__ __forceinline__ void mask_pair(SM& sm, int pi, f32x4 g, f32x4 qk, int
         const int rr = r0 + e;
         const float dec = ii <= rr ? __expf(gr[e] - gi) * nki : 0.f;
         const float av = ii < rr ? br[e] * kr[e] * dec * g[e] : 0.f;
-        sm.Ps[rr * kKtLd + pii] = __bf16(qr[e] * dec * qk[e]);
-        if (m == pp) sm.AdT[(m * 16 + li) * kXLd + 4 * lq + e] = av;
-        else sm.AN[rr * kKtLd + pii] = __bf16(-av);
+        if constexpr (PRECISE) {
+            split_bf16(qr[e] * dec * qk[e], sm.Ps[rr * kKtLd + pii], sm.Ps_lo[rr * kKtLd + pii]);
+            if (m == pp) sm.AdT[(m * 16 + li) * kXLd + 4 * lq + e] = av;
+            else split_bf16(-av, sm.AN[rr * kKtLd + pii], sm.AN_lo[rr * kKtLd + pii]);
+        } else {
+            sm.Ps[rr * kKtLd + pii] = __bf16(qr[e] * dec * qk[e]);
+            if (m == pp) sm.AdT[(m * 16 + li) * kXLd + 4 * lq + e] = av;
+            else sm.AN[rr * kKtLd + pii] = __bf16(-av);
+        }
     }
 }
 
@@ -287,7 +315,7 @@ __device__ __forceinline__ void row_scales(SM& sm, int r) {
 // applied.  BOUNDED ties the address of column i + 1 to x[i] through an empty
 // asm, so the compiler cannot hoist all 120 loads to the top (which costs
 // ~200 registers); without it the loads are scheduled freely.
-template <bool BOUNDED, class SM>
+template <bool BOUNDED, bool PRECISE = false, class SM>
 __device__ __forceinline__ void diag_solve(SM& sm, int lane) {
     const int m = lane / 16, c = lane % 16;
     const float* At = sm.AdT + m * 16 * kXLd;
@@ -311,8 +339,11 @@ __device__ __forceinline__ void diag_solve(SM& sm, int lane) {
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        sm.AN[(16 * m + rr) * kKtLd + pos(16 * m + c)] = __bf16(rr == c ? 0.f : x[rr]);
+    for (int rr = 0; rr < 16; ++rr) {
+        const int o = (16 * m + rr) * kKtLd + pos(16 * m + c);
+        if constexpr (PRECISE) split_bf16(rr == c ? 0.f : x[rr], sm.AN[o], sm.AN_lo[o]);
+        else sm.AN[o] = __bf16(rr == c ? 0.f : x[rr]);
+    }
 }
 
 // fp32 16x16 product on v_mfma_f32_16x16x4_f32 in the accumulator layout:
@@ -335,7 +366,7 @@ __device__ __forceinline__ f32x4 mm16_f32(f32x4 leftT, f32x4 right, f32x4 acc) {
 // factor.  Exact in exact arithmetic; in fp32 the powers X^k can be far
 // larger than the inverse (keys that nearly coincide, beta near 1, slow
 // decay), and their rounding then survives the cancellation.
-template <class SM>
+template <bool PRECISE = false, class SM>
 __device__ __forceinline__ void diag_neumann(SM& sm, int m, int lane) {
     const int n = lane % 16, q = lane / 16;
     const float* At = sm.AdT + m * 16 * kXLd;   // At[i * kXLd + r] = A_mm[r][i]
@@ -355,8 +386,11 @@ __device__ __forceinline__ void diag_neumann(SM& sm, int m, int lane) {
     R = mm16_f32(X2T, R, R);
     R = mm16_f32(XT, R, R);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        sm.AN[(16 * m + 4 * q + e) * kKtLd + pos(16 * m + n)] = __bf16(4 * q + e > n ? R[e] : 0.f);
+    for (int e = 0; e < 4; ++e) {
+        const int o = (16 * m + 4 * q + e) * kKtLd + pos(16 * m + n);
+        if constexpr (PRECISE) split_bf16(4 * q + e > n ? R[e] : 0.f, sm.AN[o], sm.AN_lo[o]);
+        else sm.AN[o] = __bf16(4 * q + e > n ? R[e] : 0.f);
+    }
 }
 
 // Blocked forward substitution for Delta of one wave's 16 columns:
@@ -391,6 +425,45 @@ __device__ __forceinline__ void delta_substitution(const f32x4 R[4], const bf16x
 __device__ __forceinline__ void delta_substitution(const f32x4 R[4], const bf16x4 d[4], bf16x4 a10, bf16x8 a2x,
                                                    bf16x8 a3x, bf16x4 a32, f32x4 Dl[4], bf16x4 Db[4]) {
     delta_substitution(R, d, a10, a2x, a3x, a32, Dl, Db, [](int) {});
+}
+
+// The same substitution with every coupling and diagonal product on bf16 hi
+// + lo operands (X_hi Y_hi + X_lo Y_hi + X_hi Y_lo, the lo x lo term below
+// fp32 rounding dropped): the precise mode.  The fragments come as {hi, lo}
+// pairs; Db, Dbl are the hi and lo parts of Delta for the later products.
+struct SubstFrags {
+    bf16x4 d[2][4];
+    bf16x4 a10[2];
+    bf16x8 a2x[2], a3x[2];
+    bf16x4 a32[2];
+};
+
+template <class Hook>
+__device__ __forceinline__ void delta_substitution_hl(const f32x4 R[4], const SubstFrags& f, f32x4 Dl[4],
+                                                      bf16x4 Db[4], bf16x4 Dbl[4], Hook&& hook) {
+    const bf16x4 z4 = {__bf16(0.f), __bf16(0.f), __bf16(0.f), __bf16(0.f)};
+    auto mm3 = [&](bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 acc) {
+        acc = mfma16(ah, bh, acc);
+        acc = mfma16(al, bh, acc);
+        return mfma16(ah, bl, acc);
+    };
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 y = R[m];
+        if (m == 1)
+            y = mm3(cat4(f.a10[0], z4), cat4(f.a10[1], z4), cat4(Db[0], z4), cat4(Dbl[0], z4), y);
+        if (m == 2) y = mm3(f.a2x[0], f.a2x[1], cat4(Db[0], Db[1]), cat4(Dbl[0], Dbl[1]), y);
+        if (m == 3) {
+            y = mm3(f.a3x[0], f.a3x[1], cat4(Db[0], Db[1]), cat4(Dbl[0], Dbl[1]), y);
+            y = mm3(cat4(f.a32[0], z4), cat4(f.a32[1], z4), cat4(Db[2], z4), cat4(Dbl[2], z4), y);
+        }
+        hook(2 * m);
+        bf16x4 yh, yl;
+        split_bf16x4(y, yh, yl);
+        Dl[m] = mm3(cat4(f.d[0][m], z4), cat4(f.d[1][m], z4), cat4(yh, z4), cat4(yl, z4), y);
+        hook(2 * m + 1);
+        split_bf16x4(Dl[m], Db[m], Dbl[m]);
+    }
 }
 
 // Delta' = exp(gamma_C - gamma) n_k Delta as bf16 hi + lo B operands of the

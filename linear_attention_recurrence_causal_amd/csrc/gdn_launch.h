@@ -52,6 +52,7 @@ struct PrefillParams {
     int32_t batch, num_k_heads, num_v_heads;
     float q_scale, l2_eps;
     int32_t diag_neumann;   // two-pass path: diagonal-block inverses by the Neumann product
+    int32_t precise;        // bf16 hi + lo operands on every state-path product (GDN_PRECISION_HILO)
 };
 
 // Output gate: rows = tokens x H_v rows of d_v elements.
@@ -77,7 +78,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 // Two-pass path: workspace bytes per chunk of every sequence, whether the
 // head grouping is supported, and the launcher (segments of
 // ws_bytes / prefill_split_chunk_bytes chunks; at least one must fit).
-uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads);
+uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads, bool precise);
 bool prefill_split_supported(const PrefillParams& p);
 hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream);
 
@@ -87,7 +88,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
 // the workspace must hold one chunk of records for a group
 // (prefill_varlen_group_bytes) and is used in segments beyond that.
 int prefill_varlen_group();
-uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads);
+uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads, bool precise);
 hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqlens, const int64_t* start_pos,
                                  void* ws, uint64_t ws_bytes, hipStream_t stream);
 

@@ -32,7 +32,7 @@ using namespace chunked;
 
 constexpr int kVtLd = kC + 12;      // bf16 row stride of V^T
 
-template <int NW>
+template <int NW, bool PRECISE = false>
 struct alignas(16) Smem {
     static constexpr int N = 16 * NW;
     static constexpr int VLd = N + 8;
@@ -52,6 +52,9 @@ struct alignas(16) Smem {
     alignas(16) float nq[kC];
     alignas(16) float nk[kC];
     float tokS[4][kC];            // per row: beta | beta Gamma n_k | Gamma n_q | exp(gamma_C - gamma) n_k
+    // precise mode: the bf16 lo parts of P and AN (same layout)
+    __bf16 Ps_lo[PRECISE ? kC * kKtLd : 8];
+    __bf16 AN_lo[PRECISE ? kC * kKtLd : 8];
     static_assert(kC * VLd <= kC * kKsLd, "output staging fits a Q buffer");
     static_assert(NW != 8 || (10 * 64 * 16 <= kC * kKsLd * 2 && 10 * 64 * 16 <= N * kVtLd * 2),
                   "raw Gram tiles fit the dead K and V^T buffers");
@@ -75,10 +78,10 @@ constexpr int kTilesPerWave = 4;   // 20 Gram tiles over waves 3..7
 
 // Front end of one work item (4 channels x 8 chunk rows) into buffer `buf`:
 // q, k channels -> Q, K rows, v channels -> V^T rows.
-template <bool INTERIOR, int NW>
-__device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+template <bool INTERIOR, int NW, class SM>
+__device__ __forceinline__ void front_item(const PrefillParams& p, SM& sm, const Ctx& cx, int buf,
                                            int64_t local0, int item) {
-    constexpr int NCH = Smem<NW>::NCH;
+    constexpr int NCH = SM::NCH;
     constexpr int CG4 = NCH / 4;
     const int cg = item % CG4, seg = item / CG4;
     const int ch0 = cg * 4;
@@ -108,11 +111,11 @@ __device__ __forceinline__ void front_item(const PrefillParams& p, Smem<NW>& sm,
 }
 
 // ---- A1: front end of a chunk into Q, K, V^T buffer `buf`
-template <int NW>
-__device__ __forceinline__ void phase_front(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+template <int NW, class SM>
+__device__ __forceinline__ void phase_front(const PrefillParams& p, SM& sm, const Ctx& cx, int buf,
                                             int64_t local0, int tid) {
     constexpr int NT = 64 * NW;
-    constexpr int CG4 = Smem<NW>::NCH / 4;
+    constexpr int CG4 = SM::NCH / 4;
     // interior chunks (all 64 rows and the 3-row halo inside the call) take a
     // path with no clamping and no masking
     if (local0 >= 3 && local0 + kC <= cx.L) {
@@ -124,8 +127,8 @@ __device__ __forceinline__ void phase_front(const PrefillParams& p, Smem<NW>& sm
 
 // ---- A2: K^T, gates + inclusive scan of g, L2 norms; with 8 waves also the
 // raw Gram tiles, into the dead K / V^T buffer `gbuf` (fp32, accumulator layout)
-template <int NW>
-__device__ __forceinline__ void phase_rows(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+template <int NW, class SM>
+__device__ __forceinline__ void phase_rows(const PrefillParams& p, SM& sm, const Ctx& cx, int buf,
                                            int gbuf, int64_t local0, int tid) {
     constexpr int NT = 64 * NW;
     const int wave = tid / 64, lane = tid % 64, li = lane % 16, lq = lane / 16;
@@ -173,8 +176,8 @@ __device__ __forceinline__ void phase_rows(const PrefillParams& p, Smem<NW>& sm,
 }
 
 // ---- A3: decay masks on the Gram tiles; per-row scales
-template <int NW>
-__device__ __forceinline__ void phase_masks(Smem<NW>& sm, int buf, int gbuf, int tid) {
+template <int NW, bool PRECISE, class SM>
+__device__ __forceinline__ void phase_masks(SM& sm, int buf, int gbuf, int tid) {
     constexpr int NT = 64 * NW;
     const int wave = tid / 64, lane = tid % 64, li = lane % 16, lq = lane / 16;
     if constexpr (NW == 8) {
@@ -182,12 +185,12 @@ __device__ __forceinline__ void phase_masks(Smem<NW>& sm, int buf, int gbuf, int
         // lower tile pair, 640 jobs over 512 threads, branch-free within a wave
         const f32x4* G = reinterpret_cast<const f32x4*>(sm.Ks[gbuf]);
         const f32x4* GQ = reinterpret_cast<const f32x4*>(sm.Vt[gbuf]);
-        for (int j = tid; j < 10 * 64; j += NT) mask_pair(sm, j >> 6, G[j], GQ[j], j & 63);
+        for (int j = tid; j < 10 * 64; j += NT) mask_pair<PRECISE>(sm, j >> 6, G[j], GQ[j], j & 63);
         if (wave == NW - 1) row_scales(sm, lane);
     } else {
         if (wave == 0) row_scales(sm, lane);
         for (int pi = wave - 1; pi >= 0 && pi < 10; pi += NW - 1)
-            mask_pair(sm, pi, gram_tile(sm.Ks[buf], sm.Qs[buf], pi, li, lq),
+            mask_pair<PRECISE>(sm, pi, gram_tile(sm.Ks[buf], sm.Qs[buf], pi, li, lq),
                       gram_tile(sm.Ks[buf], sm.Qs[buf], 10 + pi, li, lq), lane);
     }
 }
@@ -197,8 +200,8 @@ __device__ __forceinline__ void phase_masks(Smem<NW>& sm, int buf, int gbuf, int
 // Every block of LDS operands is loaded in one batch (fenced with a
 // scheduling barrier) before the products that use it.  Returns Q S0 and
 // Delta (bf16, as the B operands of P Delta) for B2.
-template <int NW>
-__device__ __forceinline__ void phase_state(Smem<NW>& sm, int buf, f32x4 S[8], f32x4 QS[4], bf16x8 BD[2],
+template <class SM>
+__device__ __forceinline__ void phase_state(SM& sm, int buf, f32x4 S[8], f32x4 QS[4], bf16x8 BD[2], bf16x8*,
                                             int wave, int li, int lq) {
     const int cw = 16 * wave + li;   // column inside the slice
     const __bf16* Ks = sm.Ks[buf];
@@ -295,12 +298,111 @@ __device__ __forceinline__ void phase_state(Smem<NW>& sm, int buf, f32x4 S[8], f
     }
 }
 
+// ---- B1 of the precise mode: the same products with S0, Q S0 and K S0,
+// the substitution (delta_substitution_hl) and Delta on bf16 hi + lo
+// operands (three MFMAs per product, the lo x lo term dropped).  Returns
+// Delta's hi and lo parts for B2.
+template <class SM>
+__device__ __forceinline__ void phase_state_hl(SM& sm, int buf, f32x4 S[8], f32x4 QS[4], bf16x8 BD[2],
+                                               bf16x8 BDl[2], int wave, int li, int lq) {
+    const int cw = 16 * wave + li;
+    const __bf16* Ks = sm.Ks[buf];
+    const __bf16* Qs = sm.Qs[buf];
+    bf16x8 Bh[4], Bl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) split_bf16x8(S[2 * ks], S[2 * ks + 1], Bh[ks], Bl[ks]);
+    f32x4 KS[4];
+#pragma unroll
+    for (int mh = 0; mh < 4; mh += 2) {
+        bf16x8 ak[2][4], aq[2][4];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = (16 * (mh + mm) + li) * kKsLd + 32 * ks + 8 * lq;
+                ak[mm][ks] = lds_load8(&Ks[off]);
+                aq[mm][ks] = lds_load8(&Qs[off]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            f32x4 k = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                k = mfma16(ak[mm][ks], Bh[ks], k);
+                q = mfma16(aq[mm][ks], Bh[ks], q);
+                k = mfma16(ak[mm][ks], Bl[ks], k);
+                q = mfma16(aq[mm][ks], Bl[ks], q);
+            }
+            KS[mh + mm] = k;
+            QS[mh + mm] = q;
+        }
+    }
+    f32x4 R[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r0 = 16 * m + 4 * lq;
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(&sm.tokS[0][r0]);
+        const f32x4 sr = *reinterpret_cast<const f32x4*>(&sm.tokS[1][r0]);
+        const bf16x4 vv = lds_load4(&sm.Vt[buf][cw * kVtLd + r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[m][e] = sb[e] * float(vv[e]) - sr[e] * KS[m][e];
+    }
+    SubstFrags f;
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+        const __bf16* an = (hl ? sm.AN_lo : sm.AN) + li * kKtLd + 8 * lq;
+        f.d[hl][0] = lds_load4(an);
+        f.d[hl][1] = lds_load4(an + 16 * kKtLd + 4);
+        f.d[hl][2] = lds_load4(an + 32 * kKtLd + 32);
+        f.d[hl][3] = lds_load4(an + 48 * kKtLd + 36);
+        f.a10[hl] = lds_load4(an + 16 * kKtLd);
+        f.a2x[hl] = lds_load8(an + 32 * kKtLd);
+        f.a3x[hl] = lds_load8(an + 48 * kKtLd);
+        f.a32[hl] = lds_load4(an + 48 * kKtLd + 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 Dl[4];
+    bf16x4 Db[4], Dbl[4];
+    delta_substitution_hl(R, f, Dl, Db, Dbl, [](int) {});
+    BD[0] = cat4(Db[0], Db[1]);
+    BD[1] = cat4(Db[2], Db[3]);
+    BDl[0] = cat4(Dbl[0], Dbl[1]);
+    BDl[1] = cat4(Dbl[2], Dbl[3]);
+    f32x4 su[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) su[m] = *reinterpret_cast<const f32x4*>(&sm.tokS[3][16 * m + 4 * lq]);
+    const float eC = expf(sm.gam[kC - 1]);
+    bf16x8 BH[2], BL[2];
+    split_hi_lo(su, Dl, BH, BL);
+#pragma unroll
+    for (int th = 0; th < 8; th += 4) {
+        bf16x8 akt[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                akt[t][ks] = lds_load8(&sm.Kt[(16 * (th + t) + li) * kKtLd + 32 * ks + 8 * lq]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = S[th + t] * eC;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                acc = mfma16(akt[t][ks], BH[ks], acc);
+                acc = mfma16(akt[t][ks], BL[ks], acc);
+            }
+            S[th + t] = acc;
+        }
+    }
+}
+
 // ---- B2: O = Gamma n_q (Q S0) + P Delta, staged (bf16) into the chunk's Q
 // buffer, which no wave reads any more
-template <int NW>
-__device__ __forceinline__ void phase_out(Smem<NW>& sm, int buf, const f32x4 QS[4], const bf16x8 BD[2],
+template <bool PRECISE, class SM>
+__device__ __forceinline__ void phase_out(SM& sm, int buf, const f32x4 QS[4], const bf16x8 BD[2], const bf16x8 BDl[2],
                                           int wave, int li, int lq) {
-    constexpr int VLd = Smem<NW>::VLd;
+    constexpr int VLd = SM::VLd;
     const int cw = 16 * wave + li;
     __bf16* Os = sm.Qs[buf];
     f32x4 so[4];
@@ -318,7 +420,15 @@ __device__ __forceinline__ void phase_out(Smem<NW>& sm, int buf, const f32x4 QS[
         f32x4 acc = so[m] * QS[m];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            if (ks == 0 || m >= 2) acc = mfma16(pa[i++], BD[ks], acc);
+            if (ks == 0 || m >= 2) {
+                acc = mfma16(pa[i], BD[ks], acc);
+                if constexpr (PRECISE) {
+                    const bf16x8 pl = lds_load8(&sm.Ps_lo[(16 * m + li) * kKtLd + 32 * ks + 8 * lq]);
+                    acc = mfma16(pl, BD[ks], acc);
+                    acc = mfma16(pa[i], BDl[ks], acc);
+                }
+                ++i;
+            }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Os[(16 * m + 4 * lq + e) * VLd + cw] = __bf16(acc[e]);
     }
@@ -326,14 +436,14 @@ __device__ __forceinline__ void phase_out(Smem<NW>& sm, int buf, const f32x4 QS[
 
 // ---- C: O rows -> HBM (16-byte stores); checkpoint slot when the chunk end
 // is a multiple of the checkpoint interval
-template <int NW>
-__device__ __forceinline__ void phase_store(const PrefillParams& p, Smem<NW>& sm, const Ctx& cx, int buf,
+template <int NW, class SM>
+__device__ __forceinline__ void phase_store(const PrefillParams& p, SM& sm, const Ctx& cx, int buf,
                                             const f32x4 S[8], int64_t kc, int64_t s_base, bool owns_qk_tail,
                                             int tid) {
     constexpr int NT = 64 * NW;
     constexpr int N = 16 * NW;
-    constexpr int VLd = Smem<NW>::VLd;
-    constexpr int NCH = Smem<NW>::NCH;
+    constexpr int VLd = SM::VLd;
+    constexpr int NCH = SM::NCH;
     const int lane = tid % 64, lq = lane / 16;
     const int64_t local0 = kc * kC - cx.sp;
     const __bf16* Os = sm.Qs[buf];
@@ -361,12 +471,13 @@ __device__ __forceinline__ void phase_store(const PrefillParams& p, Smem<NW>& sm
     }
 }
 
-template <int NW>
+template <int NW, bool PRECISE>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     constexpr int NT = 64 * NW;
     constexpr int N = 16 * NW;
     constexpr int S_SPLIT = kD / N;
-    using SM = Smem<NW>;
+    using SM = Smem<NW, PRECISE>;
+    static_assert(sizeof(SM) <= 160 * 1024, "LDS of one workgroup");
     constexpr int NCH = SM::NCH;
     static_assert(NCH % 4 == 0, "channel groups of 4");
     __shared__ SM sm;
@@ -401,6 +512,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
         const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
         sm.Ps[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
+        if constexpr (PRECISE) sm.Ps_lo[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
     }
     for (int e = tid; e < NCH * 4; e += NT) {
         // taps stored [tap][channel] so that four channels of one tap are one
@@ -426,13 +538,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
     // ---- prologue: the S-independent work of the first chunk
     if (k_first < k_end) {
         const int64_t local0 = k_first * kC - cx.sp;
-        phase_front(p, sm, cx, 0, local0, tid);
+        phase_front<NW>(p, sm, cx, 0, local0, tid);
         __syncthreads();
-        phase_rows(p, sm, cx, 0, 1, local0, tid);
+        phase_rows<NW>(p, sm, cx, 0, 1, local0, tid);
         __syncthreads();
-        phase_masks(sm, 0, 1, tid);
+        phase_masks<NW, PRECISE>(sm, 0, 1, tid);
         __syncthreads();
-        if (wave == 0) diag_solve<false>(sm, lane);
+        if (wave == 0) diag_solve<false, PRECISE>(sm, lane);
         __syncthreads();
     }
 
@@ -445,23 +557,27 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
         const bool next = kc + 1 < k_end;
         const int64_t nlocal0 = (kc + 1) * kC - cx.sp;
         f32x4 QS[4];
-        bf16x8 BD[2];
+        bf16x8 BD[2], BDl[2];
+        auto state = [&] {
+            if constexpr (PRECISE) phase_state_hl(sm, buf, S, QS, BD, BDl, wave, li, lq);
+            else phase_state(sm, buf, S, QS, BD, BDl, wave, li, lq);
+        };
         if (wave < NW / 2 || !next) {
-            phase_state(sm, buf, S, QS, BD, wave, li, lq);
-            if (next) phase_front(p, sm, cx, nbuf, nlocal0, tid);
+            state();
+            if (next) phase_front<NW>(p, sm, cx, nbuf, nlocal0, tid);
         } else {
-            phase_front(p, sm, cx, nbuf, nlocal0, tid);
-            phase_state(sm, buf, S, QS, BD, wave, li, lq);
+            phase_front<NW>(p, sm, cx, nbuf, nlocal0, tid);
+            state();
         }
         __syncthreads();
-        phase_out(sm, buf, QS, BD, wave, li, lq);
-        if (next) phase_rows(p, sm, cx, nbuf, buf, nlocal0, tid);
+        phase_out<PRECISE>(sm, buf, QS, BD, BDl, wave, li, lq);
+        if (next) phase_rows<NW>(p, sm, cx, nbuf, buf, nlocal0, tid);
         __syncthreads();
-        phase_store(p, sm, cx, buf, S, kc, s_base, owns_qk_tail, tid);
-        if (next) phase_masks(sm, nbuf, buf, tid);
+        phase_store<NW>(p, sm, cx, buf, S, kc, s_base, owns_qk_tail, tid);
+        if (next) phase_masks<NW, PRECISE>(sm, nbuf, buf, tid);
         __syncthreads();
         if (next) {
-            if (wave == 0) diag_solve<false>(sm, lane);
+            if (wave == 0) diag_solve<false, PRECISE>(sm, lane);
             __syncthreads();
         }
     }
@@ -477,13 +593,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams p) {
                        static_cast<uint16_t*>(p.conv_out));
 }
 
-template <int NW>
+template <int NW, bool PRECISE = false>
 hipError_t launch_nw(const PrefillParams& p, hipStream_t stream) {
     const int s_split = kD / (16 * NW);
     const int r = p.num_v_heads / p.num_k_heads;
     const int ng = p.batch * p.num_k_heads;
     const int blocks = ((ng + 7) / 8) * 8 * r * s_split;
-    hipLaunchKernelGGL((prefill_kernel<NW>), dim3(blocks), dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<NW, PRECISE>), dim3(blocks), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -508,6 +624,9 @@ int prefill_waves() {
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
+    // the precise mode's lo parts of P and AN do not fit beside the 8-wave
+    // layout: 4 waves (64 state columns) per workgroup
+    if (p.precise) return launch_nw<4, true>(p, stream);
     switch (prefill_waves()) {
         case 8: return launch_nw<8>(p, stream);
         case 4: return launch_nw<4>(p, stream);

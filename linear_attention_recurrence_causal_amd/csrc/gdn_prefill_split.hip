@@ -73,13 +73,21 @@ constexpr int kRecAN = kPaMat;
 constexpr int kRecTok = 2 * kPaMat;
 constexpr int kTokBytes = 5 * kC * 4;
 constexpr int kValRec = kRecTok + kTokBytes;        // 13568
-static_assert(kKeyRec % 256 == 0 && kValRec % 256 == 0, "records keep 256-byte alignment");
+// precise mode (bf16 hi + lo operands): the rows of scales take a 2 KiB slot
+// and the lo parts of P and AN follow, so that the whole value record has the
+// layout of its LDS image
+constexpr int kRecPlo = kRecTok + 2048;
+constexpr int kValRecHL = kRecPlo + 2 * kPaMat;     // 26624
+static_assert(kKeyRec % 256 == 0 && kValRec % 256 == 0 && kValRecHL % 256 == 0,
+              "records keep 256-byte alignment");
+constexpr int val_rec_bytes(bool precise) { return precise ? kValRecHL : kValRec; }
 
 constexpr int kMaxGroup = 8;                        // value heads per key head on this path
 
 struct SplitParams {
     PrefillParams p;
     char* ws;
+    int32_t vrec_bytes;  // bytes of a value record (val_rec_bytes(p.precise))
     int64_t k0;          // absolute index of the segment's first chunk
     int32_t nseg;        // chunks in the segment
     int32_t first_seg;   // state comes from rec_in (else from rec_out)
@@ -96,7 +104,7 @@ __device__ __forceinline__ char* key_rec(const SplitParams& s, int rb, int kh, i
 
 __device__ __forceinline__ char* val_rec(const SplitParams& s, int rb, int h, int j) {
     return s.ws + (int64_t)s.rec_batch * s.p.num_k_heads * s.rec_stride * kKeyRec +
-           (((int64_t)rb * s.p.num_v_heads + h) * s.rec_stride + j) * kValRec;
+           (((int64_t)rb * s.p.num_v_heads + h) * s.rec_stride + j) * s.vrec_bytes;
 }
 
 // ---- sequences of different lengths and start positions in one call
@@ -158,33 +166,40 @@ __device__ __forceinline__ void copy16(char* dst, const void* src) {
 constexpr int kPrepWaves = 8;
 constexpr int kPrepThreads = 64 * kPrepWaves;
 
-// One value head's masked matrices, diagonal blocks and row scales.
+// One value head's masked matrices, diagonal blocks and row scales (and in
+// the precise mode the lo parts of P and AN).
+template <bool PRECISE>
 struct alignas(16) PrepHeadBuf {
+    static constexpr int LO = PRECISE ? kC * kKtLd : 8;
     __bf16 Ps[kC * kKtLd];
     __bf16 AN[kC * kKtLd];
     float AdT[4 * 16 * kXLd];
     float tokS[5][kC];
+    __bf16 Ps_lo[LO];
+    __bf16 AN_lo[LO];
 };
 
 // Q and K are dead once their record is written and the Gram tiles are in
 // registers, so a second head buffer shares their space: one value head is
 // solved while the next one's masks are formed.
+template <bool PRECISE>
 struct alignas(16) PrepSmem {
     union {
         struct {
             __bf16 Qs[kC * kKsLd];
             __bf16 Ks[kC * kKsLd];
         };
-        PrepHeadBuf hb1;
+        PrepHeadBuf<PRECISE> hb1;
     };
-    PrepHeadBuf hb0;
+    PrepHeadBuf<PRECISE> hb0;
     alignas(16) float beta[kMaxGroup][kC];   // per value head of the group
     alignas(16) float gam[kMaxGroup][kC];
     alignas(16) float nq[kC];
     alignas(16) float nk[kC];
     uint16_t Ws[4 * 2 * kD];   // conv taps (bf16 bits) [tap][channel]: q, then k
 };
-static_assert(sizeof(PrepHeadBuf) <= 2 * kC * kKsLd * 2, "the second head buffer fits in Q and K");
+static_assert(sizeof(PrepHeadBuf<false>) <= 2 * kC * kKsLd * 2, "the second head buffer fits in Q and K");
+static_assert(sizeof(PrepSmem<false>) <= 160 * 1024 / 2, "two prep workgroups per CU");
 
 // One value head's view of the prep LDS, in the member names the shared
 // mask, row-scale and solve helpers use.
@@ -197,6 +212,8 @@ struct PrepHeadView {
     __bf16* AN;
     float* AdT;
     float (*tokS)[kC];
+    __bf16* Ps_lo;
+    __bf16* AN_lo;
 };
 
 // Global channel of prep channel index ch: q then k of key head kh
@@ -218,8 +235,8 @@ __device__ __forceinline__ void prep_front_load(const PrefillParams& p, int b, i
     else conv_load<false>(p, b, gc, local0, tau0, raw);
 }
 
-template <bool INTERIOR>
-__device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm, int b, int kh, int64_t local0,
+template <bool INTERIOR, class SMEM>
+__device__ __forceinline__ void prep_front(const PrefillParams& p, SMEM& sm, int b, int kh, int64_t local0,
                                            int tid, const uint2 raw[11]) {
     const int ch0 = (tid % 64) * 4, tau0 = (tid / 64) * 8;
     const int64_t gc = qk_channel(ch0, kh, p.num_k_heads);
@@ -235,22 +252,29 @@ __device__ __forceinline__ void prep_front(const PrefillParams& p, PrepSmem& sm,
 
 // Zero the upper tiles of a head buffer's P and AN (the masks never write
 // them) and the unused part of its fifth row of scales.
-__device__ __forceinline__ void zero_upper(PrepHeadBuf& hb, int tid) {
+template <bool PRECISE>
+__device__ __forceinline__ void zero_upper(PrepHeadBuf<PRECISE>& hb, int tid) {
     for (int e = tid; e < 6 * 256; e += kPrepThreads) {
         const int t6 = e / 256, rr = (e / 16) % 16, cc = e % 16;
         const int m = t6 < 3 ? 0 : (t6 < 5 ? 1 : 2);
         const int pp = t6 < 3 ? t6 + 1 : (t6 < 5 ? t6 - 1 : 3);
-        hb.Ps[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
-        hb.AN[(16 * m + rr) * kKtLd + pos(16 * pp + cc)] = __bf16(0.f);
+        const int o = (16 * m + rr) * kKtLd + pos(16 * pp + cc);
+        hb.Ps[o] = __bf16(0.f);
+        hb.AN[o] = __bf16(0.f);
+        if constexpr (PRECISE) {
+            hb.Ps_lo[o] = __bf16(0.f);
+            hb.AN_lo[o] = __bf16(0.f);
+        }
     }
     if (tid < kC) hb.tokS[4][tid] = 0.f;
 }
 
 // Chunk j of the segment for sequence b (record-sequence rb) and key head kh
-template <bool NEUMANN>
+template <bool NEUMANN, bool PRECISE>
 __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, int kh, int j) {
     const PrefillParams& p = sp.p;
-    __shared__ PrepSmem sm;
+    using HB = PrepHeadBuf<PRECISE>;
+    __shared__ PrepSmem<PRECISE> sm;
     // wave index in a scalar register: branches on it are uniform
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
     const int li = lane % 16, lq = lane / 16;
@@ -309,35 +333,40 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
     }
     __syncthreads();
 
+    auto view = [&](int hh, HB& hb) {
+        return PrepHeadView{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, hb.Ps, hb.AN, hb.AdT, hb.tokS, hb.Ps_lo, hb.AN_lo};
+    };
     // masks and row scales of value head hh of the group into a head buffer
-    auto mask_head = [&](int hh, PrepHeadBuf& hb) {
-        PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, hb.Ps, hb.AN, hb.AdT, hb.tokS};
-        if (has0) mask_pair(hv, pa0, gk[0], gq[0], lane);
-        if (has1) mask_pair(hv, pa1, gk[1], gq[1], lane);
+    auto mask_head = [&](int hh, HB& hb) {
+        PrepHeadView hv = view(hh, hb);
+        if (has0) mask_pair<PRECISE>(hv, pa0, gk[0], gq[0], lane);
+        if (has1) mask_pair<PRECISE>(hv, pa1, gk[1], gq[1], lane);
         if (wave == kPrepWaves - 1) {
             row_scales(hv, lane);
             if (lane == 0) hb.tokS[4][0] = expf(sm.gam[hh][kC - 1]);
         }
     };
     // P and the row scales of a head buffer -> value record (granules e0,
-    // e0 + stride, ...), and AN
+    // e0 + stride, ...), and AN; in the precise mode their lo parts too
     constexpr int kPaGran = kPaMat / 16;
-    auto copy_p_tok = [&](char* vrec, const PrepHeadBuf& hb, int e0, int stride) {
+    auto copy_p_tok = [&](char* vrec, const HB& hb, int e0, int stride) {
         for (int e = e0; e < kPaGran + kTokBytes / 16; e += stride) {
             if (e < kPaGran) {
                 int row, g;
                 pa_granule(16 * e, row, g);
                 copy16(vrec + kRecP + 16 * e, hb.Ps + row * kKtLd + 8 * g);
+                if constexpr (PRECISE) copy16(vrec + kRecPlo + 16 * e, hb.Ps_lo + row * kKtLd + 8 * g);
             } else {
                 copy16(vrec + kRecTok + 16 * (e - kPaGran), &hb.tokS[0][0] + 4 * (e - kPaGran));
             }
         }
     };
-    auto copy_an = [&](char* vrec, const PrepHeadBuf& hb, int e0, int stride) {
+    auto copy_an = [&](char* vrec, const HB& hb, int e0, int stride) {
         for (int e = e0; e < kPaGran; e += stride) {
             int row, g;
             pa_granule(16 * e, row, g);
             copy16(vrec + kRecAN + 16 * e, hb.AN + row * kKtLd + 8 * g);
+            if constexpr (PRECISE) copy16(vrec + kRecPlo + kPaMat + 16 * e, hb.AN_lo + row * kKtLd + 8 * g);
         }
     };
 
@@ -349,8 +378,8 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
             mask_head(hh, sm.hb0);
             __syncthreads();
             if (wave < 4) {
-                PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, sm.hb0.Ps, sm.hb0.AN, sm.hb0.AdT, sm.hb0.tokS};
-                diag_neumann(hv, wave, lane);
+                PrepHeadView hv = view(hh, sm.hb0);
+                diag_neumann<PRECISE>(hv, wave, lane);
             } else {
                 copy_p_tok(vrec, sm.hb0, tid - 256, kPrepThreads - 256);
             }
@@ -367,12 +396,12 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
         mask_head(0, sm.hb0);
         __syncthreads();
         for (int hh = 0; hh < r; ++hh) {
-            PrepHeadBuf& cur = hh & 1 ? sm.hb1 : sm.hb0;
-            PrepHeadBuf& nxt = hh & 1 ? sm.hb0 : sm.hb1;
+            HB& cur = hh & 1 ? sm.hb1 : sm.hb0;
+            HB& nxt = hh & 1 ? sm.hb0 : sm.hb1;
             char* vrec = val_rec(sp, rb, kh * r + hh, j);
             if (wave == 0) {
-                PrepHeadView hv{sm.gam[hh], sm.beta[hh], sm.nq, sm.nk, cur.Ps, cur.AN, cur.AdT, cur.tokS};
-                diag_solve<true>(hv, lane);
+                PrepHeadView hv = view(hh, cur);
+                diag_solve<true, PRECISE>(hv, lane);
                 // this wave's own LDS writes are read back in order; keep the
                 // compiler from moving the reads above them
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -387,18 +416,18 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
     }
 }
 
-template <bool NEUMANN>
+template <bool NEUMANN, bool PRECISE>
 __global__ __launch_bounds__(kPrepThreads)
 void prep_kernel(SplitParams sp) {
     const int j = blockIdx.x % sp.rec_stride;
     const int grp = blockIdx.x / sp.rec_stride;
     const int b = grp / sp.p.num_k_heads, kh = grp % sp.p.num_k_heads;
-    prep_body<NEUMANN>(sp, b, b, kh, j);
+    prep_body<NEUMANN, PRECISE>(sp, b, b, kh, j);
 }
 
 // Varlen: blockIdx = (entry i, key head, chunk j of the segment); entries
 // whose sequence has fewer chunks left leave at once
-template <bool NEUMANN>
+template <bool NEUMANN, bool PRECISE>
 __global__ __launch_bounds__(kPrepThreads)
 void prep_kernel_varlen(VarlenParams vp) {
     const int j = blockIdx.x % vp.sp.rec_stride;
@@ -406,25 +435,37 @@ void prep_kernel_varlen(VarlenParams vp) {
     const int i = grp / vp.sp.p.num_k_heads, kh = grp % vp.sp.p.num_k_heads;
     const SplitParams sp = seq_view(vp, i, vp.b0 + i);
     if (j >= sp.nseg) return;
-    prep_body<NEUMANN>(sp, vp.b0 + i, i, kh, j);
+    prep_body<NEUMANN, PRECISE>(sp, vp.b0 + i, i, kh, j);
 }
 
 // ============================================================ state kernel
-#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
+// LDS pointer from a generic pointer into LDS by its low 32 bits (the LDS
+// offset): no address-space cast, whose null check costs a compare and a
+// select per copy
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(uint32_t)(uintptr_t)(x))
 
 
-// LDS buffer of one chunk: Q | K | P | AN | rows | V^T (V^T of the slice's
-// columns, row stride kVtLd).  K^T is read from K by transposing LDS reads.
+// LDS buffer of one chunk: Q | K | P | AN | rows [| P_lo | AN_lo] | V^T (V^T
+// of the slice's columns, row stride kVtLd; the lo parts of P and AN in the
+// precise mode only).  K^T is read from K by transposing LDS reads.
 constexpr int kVtLd = kC + 4;                       // bf16 row stride of V^T (conflict-free column reads)
 constexpr int kBufQ = 0, kBufK = kC * kD * 2, kBufPA = 2 * kC * kD * 2,
-              kBufTok = kBufPA + 2 * kPaMat, kBufVt = kBufTok + kTokBytes;
-static_assert(kBufPA % 1024 == 0 && kBufTok % 1024 == 0 && kBufVt % 16 == 0, "piece and row alignment");
+              kBufTok = kBufPA + 2 * kPaMat, kBufPAlo = kBufTok + 2048;
+constexpr int buf_vt(bool precise) { return precise ? kBufPAlo + 2 * kPaMat : kBufTok + kTokBytes; }
+static_assert(kBufPA % 1024 == 0 && kBufTok % 1024 == 0 && kBufPAlo % 1024 == 0 && kBufTok + kTokBytes <= kBufPAlo,
+              "piece and row alignment");
+static_assert(kBufTok - kBufPA == kRecTok && kBufPAlo - kBufPA == kRecPlo && kRecP == 0,
+              "a value record is the LDS image from kBufPA on");
 
 // Record copies of one chunk: 1 KiB pieces, one wave-wide
 // global_load_lds_dwordx4 each.  Pieces 0..15: Q, 16..31: K (256-byte rows),
-// 32..43: P | AN triangles, 44..45: the rows of scales (1280 bytes).
-constexpr int kPiecesK = 16, kPiecesPA = 32, kPiecesTok = 44, kPieces = 46;
+// 32..43: P | AN triangles, 44..45: the rows of scales (1280 bytes, padded
+// to 2 KiB in the precise mode); in the precise mode 46..57: the lo parts of
+// P | AN.
+constexpr int kPiecesK = 16, kPiecesPA = 32, kPiecesTok = 44, kPiecesLo = 46;
+constexpr int num_pieces(bool precise) { return precise ? kPiecesLo + 12 : kPiecesLo; }
 
+template <bool PRECISE>
 __device__ __forceinline__ void issue_piece(char* lds, const char* krec, const char* vrec, int pc, int lane) {
     const char* src;
     int dst;
@@ -434,15 +475,12 @@ __device__ __forceinline__ void issue_piece(char* lds, const char* krec, const c
         const int row = o >> 8, s = (o >> 4) & 15;
         src = krec + (pc < kPiecesK ? kRecQ : kRecK) + swz256(row, s);
         dst = (pc < kPiecesK ? kBufQ : kBufK) + o;
-    } else if (pc < kPiecesTok) {
-        const int o = (pc - kPiecesPA) * 1024 + 16 * lane;   // P | AN, stored in their LDS layout
-        src = vrec + kRecP + o;
-        dst = kBufPA + o;
     } else {
-        const int l = (pc - kPiecesTok) * 1024 + 16 * lane;
-        act = l < kTokBytes;
-        src = vrec + kRecTok + l;
-        dst = kBufTok + l;
+        // the value record is the image of LDS from kBufPA on
+        const int o = (pc - kPiecesPA) * 1024 + 16 * lane;
+        act = PRECISE || o < kRecTok + kTokBytes;
+        src = vrec + o;
+        dst = kBufPA + o;
     }
     if (act) __builtin_amdgcn_global_load_lds(src, LDS_PTR(lds + (dst & ~1023)), 16, 0, 0);
 }
@@ -577,6 +615,132 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
         for (int t = 0; t < 8; ++t) S[t] = mfma16(akt[t][st / 2], (st % 2 ? BL : BH)[st / 2], S[t]);
 }
 
+// The precise mode's chunk (bf16 hi + lo on every state-path operand): K S0
+// and (Q S0)^T with S0 as hi + lo, the substitution with the coupling and
+// diagonal products on hi + lo (delta_substitution_hl), O's P Delta on hi +
+// lo, and the state update as in chunk_products.  About 1.7x the MFMAs of
+// the default; the operands are loaded in smaller batches (fewer registers,
+// more exposed LDS latency).
+template <class StorePrev>
+__device__ __forceinline__ void chunk_products_hl(const char* buf, f32x4 S[8], const bf16x4 vv[4], bf16x4 Ob[4],
+                                                  int li, int lq, StorePrev&& store_prev) {
+    bf16x8 Bh[4], Bl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) split_bf16x8(S[2 * ks], S[2 * ks + 1], Bh[ks], Bl[ks]);
+    // K S0 in two halves of row tiles
+    f32x4 KS[4];
+#pragma unroll
+    for (int mh = 0; mh < 4; mh += 2) {
+        bf16x8 ak[2][4];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) ak[mm][ks] = ld8(buf, kBufK + swz256(16 * (mh + mm) + li, 4 * ks + lq));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc = mfma16(ak[mm][ks], Bh[ks], acc);
+                acc = mfma16(ak[mm][ks], Bl[ks], acc);
+            }
+            KS[mh + mm] = acc;
+        }
+    }
+    // R and the substitution's operands (hi from AN, lo from AN_lo)
+    f32x4 R[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r0 = 16 * m + 4 * lq;
+        const f32x4 sb = ldf4(buf, kBufTok + 4 * (0 * kC + r0));
+        const f32x4 sr = ldf4(buf, kBufTok + 4 * (1 * kC + r0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[m][e] = sb[e] * float(vv[m][e]) - sr[e] * KS[m][e];
+    }
+    SubstFrags f;
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+        const char* an = buf + (hl ? kBufPAlo : kBufPA);
+        f.d[hl][0] = ld4(an, pa_off(1, li, lq));
+        f.d[hl][1] = ld4(an, pa_off(1, 16 + li, lq) + 8);
+        f.d[hl][2] = ld4(an, pa_off(1, 32 + li, 4 + lq));
+        f.d[hl][3] = ld4(an, pa_off(1, 48 + li, 4 + lq) + 8);
+        f.a10[hl] = ld4(an, pa_off(1, 16 + li, lq));
+        f.a2x[hl] = ld8(an, pa_off(1, 32 + li, lq));
+        f.a3x[hl] = ld8(an, pa_off(1, 48 + li, lq));
+        f.a32[hl] = ld4(an, pa_off(1, 48 + li, 4 + lq));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 Dl[4];
+    bf16x4 Db[4], Dbl[4];
+    delta_substitution_hl(R, f, Dl, Db, Dbl, [&](int st) {
+        if (st == 2) store_prev();
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    // (Q S0)^T in two halves, then O^T = (Q S0)^T diag(Gamma n_q) + (P Delta)^T
+    f32x4 QT[4];
+#pragma unroll
+    for (int mh = 0; mh < 4; mh += 2) {
+        bf16x8 aq[2][4];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) aq[mm][ks] = ld8(buf, kBufQ + swz256(16 * (mh + mm) + li, 4 * ks + lq));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc = mfma16(Bh[k], aq[mm][k], acc);
+                acc = mfma16(Bl[k], aq[mm][k], acc);
+            }
+            QT[mh + mm] = acc;
+        }
+    }
+    const bf16x8 BDh[2] = {cat4(Db[0], Db[1]), cat4(Db[2], Db[3])};
+    const bf16x8 BDl[2] = {cat4(Dbl[0], Dbl[1]), cat4(Dbl[2], Dbl[3])};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float so = *reinterpret_cast<const float*>(buf + kBufTok + 4 * (2 * kC + 16 * m + li));
+        f32x4 acc = QT[m] * so;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            if (ks == 0 || m >= 2) {
+                const bf16x8 ph = ld8(buf + kBufPA, pa_off(0, 16 * m + li, 4 * ks + lq));
+                const bf16x8 pl = ld8(buf + kBufPAlo, pa_off(0, 16 * m + li, 4 * ks + lq));
+                acc = mfma16(BDh[ks], ph, acc);
+                acc = mfma16(BDh[ks], pl, acc);
+                acc = mfma16(BDl[ks], ph, acc);
+            }
+        Ob[m] = __builtin_convertvector(acc, bf16x4);
+    }
+    // the state update, as in chunk_products
+    f32x4 su[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) su[m] = ldf4(buf, kBufTok + 4 * (3 * kC + 16 * m + 4 * lq));
+    const float eC = *reinterpret_cast<const float*>(buf + kBufTok + 4 * 4 * kC);
+    bf16x8 BH[2], BL[2];
+    split_hi_lo(su, Dl, BH, BL);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] *= eC;
+#pragma unroll
+    for (int th = 0; th < 8; th += 4) {
+        bf16x8 akt[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) akt[t][ks] = kt_frag(buf, th + t, ks, li, lq);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                S[th + t] = mfma16(akt[t][st / 2], (st % 2 ? BL : BH)[st / 2], S[th + t]);
+    }
+}
+
 struct StateCtx {
     int b, rb, kh, h, zcol0;   // rb: the sequence's index among the launch's records
     bool owns_qk_tail;
@@ -600,12 +764,14 @@ __device__ __forceinline__ int64_t state_channel(const PrefillParams& p, const S
 // one 4-channel x 4-row item per lane, from a raw slab of exactly those rows
 // (+ 3 rows of conv history) that the same wave copied one chunk earlier
 // into its own slab region.
-template <int NW>
+template <int NW, bool PRECISE = false>
 struct StateShape {
     static constexpr int NM = 8 - NW;
     static constexpr int N = 16 * NW;                        // state columns per workgroup
     static constexpr int SPLIT = kD / N;
-    static constexpr int BUF = kBufVt + N * kVtLd * 2;
+    static constexpr int VT = buf_vt(PRECISE);               // V^T offset in a buffer
+    static constexpr int BUF = VT + N * kVtLd * 2;
+    static constexpr int PIECES = num_pieces(PRECISE);
     static constexpr int NV = NW == 4 ? 4 : 2;               // V waves = parts of the chunk's rows
     static constexpr int SLAB_ROW = N * 2;                   // raw v slab: [rows][N channels] bf16
     static constexpr int PART_ROWS = kC / NV;
@@ -616,11 +782,14 @@ struct StateShape {
     static constexpr bool is_v(int m) { return NW == 4 || m >= 4; }
     static constexpr int v_part(int m) { return NW == 4 ? m : m - 4; }
     // record pieces: NW = 2: 10, 10, 10, 8 for m 0..3 and 4, 4 for the V
-    // waves; NW = 4: 12, 12, 11, 11
+    // waves; NW = 4: 12, 12, 11, 11 (precise: 13, 13, 13, 11, 4, 4 and 15,
+    // 15, 14, 14)
     static constexpr int rec_lo(int m) {
+        if constexpr (PRECISE)
+            return NW == 4 ? (m < 2 ? 15 * m : 30 + 14 * (m - 2)) : (m < 3 ? 13 * m : m == 3 ? 39 : 50 + 4 * (m - 4));
         return NW == 4 ? (m < 2 ? 12 * m : 24 + 11 * (m - 2)) : (m < 3 ? 10 * m : m == 3 ? 30 : 38 + 4 * (m - 4));
     }
-    static constexpr int rec_hi(int m) { return m + 1 == NM ? kPieces : rec_lo(m + 1); }
+    static constexpr int rec_hi(int m) { return m + 1 == NM ? PIECES : rec_lo(m + 1); }
 };
 
 // Copy piece pc of the raw v slab of row part `part` of a chunk (slab row i
@@ -642,10 +811,10 @@ __device__ __forceinline__ void issue_slab(const PrefillParams& p, const StateCt
 // Front end of row part `part` of the slice's v channels for one chunk from
 // its raw slab -> V^T in the chunk's buffer.  Items of 4 channels x 4 rows,
 // one per lane: N / 4 channel groups x PART_ROWS / 4 row groups = 64 items.
-template <int NW, bool INTERIOR>
+template <int NW, bool INTERIOR, bool PRECISE>
 __device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& cx, const float* Wv, const char* slab,
                                         char* buf, int64_t local0, int part, int lane) {
-    using SS = StateShape<NW>;
+    using SS = StateShape<NW, PRECISE>;
     constexpr int CG = SS::N / 4;
     static_assert(CG * (SS::PART_ROWS / 4) == 64, "one item per lane");
     const int c0 = (lane % CG) * 4, rt = (lane / CG) * 4;
@@ -663,12 +832,20 @@ __device__ __forceinline__ void v_front(const PrefillParams& p, const StateCtx& 
     conv_compute<INTERIOR, 4>(p, cx.b, gc, local0, tau0, w, raw, ub);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<bf16x4*>(buf + kBufVt + ((c0 + i) * kVtLd + tau0) * 2) = bf16x4{ub[0][i], ub[1][i], ub[2][i], ub[3][i]};
+        *reinterpret_cast<bf16x4*>(buf + SS::VT + ((c0 + i) * kVtLd + tau0) * 2) = bf16x4{ub[0][i], ub[1][i], ub[2][i], ub[3][i]};
 }
 
 // O of chunk kc -> out (bf16): lane (i, q) of compute wave w writes columns
 // 16w + 4q .. 16w + 4q + 3 of token 16m + i, one 8-byte store per tile.
 // `obase` points at this lane's columns of call-local token i.
+// x unchanged but hidden from the optimiser: the addresses formed from it
+// are computed where they are used, not kept live across the chunk loop
+// (which would spill them)
+__device__ __forceinline__ int64_t opaque(int64_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ void store_o(const PrefillParams& p, uint16_t* obase, const bf16x4 O[4], int64_t kc, int li) {
     const int64_t row_stride = (int64_t)p.num_v_heads * kD;
     const int64_t t0 = kc * kC - p.start_pos;
@@ -700,7 +877,7 @@ __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCt
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rec[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+            for (int e = 0; e < 4; ++e) rec[opaque(cx.s_base) + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
         uint16_t* ctail = reinterpret_cast<uint16_t*>(slot);
         for (int ch = tid; ch < NCH; ch += NT)
             if (ch >= 2 * kD || cx.owns_qk_tail) write_tail(p, cx.b, pe - p.start_pos, state_channel(p, cx, ch), ctail);
@@ -731,10 +908,10 @@ __device__ __forceinline__ void lds_barrier() {
 // a V wave then the v front end from slab_cur (this wave's raw slab of chunk
 // jn, copied in the previous step) and the copy of chunk jn + 1's slab into
 // slab_next, which may stay in flight across the barrier that follows.
-template <int NW, int M>
+template <int NW, int M, bool PRECISE>
 __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf,
                                          const char* slab_cur, char* slab_next, int jn, int lane) {
-    using SS = StateShape<NW>;
+    using SS = StateShape<NW, PRECISE>;
     constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M);
     if (jn >= sp.nseg) {
         wait_vm<0, true>();
@@ -743,13 +920,15 @@ __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& 
     const char* krec = key_rec(sp, cx.rb, cx.kh, jn);
     const char* vrec = val_rec(sp, cx.rb, cx.h, jn);
 #pragma unroll
-    for (int pc = LO; pc < HI; ++pc) issue_piece(buf, krec, vrec, pc, lane);
+    for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(buf, krec, vrec, pc, lane);
     if constexpr (SS::is_v(M)) {
         constexpr int part = SS::v_part(M);
         wait_vm<HI - LO>();   // the slab copies issued before these pieces have landed
         const int64_t local0 = (sp.k0 + jn) * kC - sp.p.start_pos;
-        if (local0 >= 3 && local0 + kC <= sp.p.seq_len) v_front<NW, true>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
-        else v_front<NW, false>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
+        if (local0 >= 3 && local0 + kC <= sp.p.seq_len)
+            v_front<NW, true, PRECISE>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
+        else
+            v_front<NW, false, PRECISE>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
         if (jn + 1 < sp.nseg) {
 #pragma unroll
             for (int pc = 0; pc < SS::SLAB_PIECES; ++pc) issue_slab<NW>(sp.p, cx, slab_next, local0 + kC, part, pc, lane);
@@ -767,10 +946,10 @@ __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& 
 // each LDS buffer and slab region is a distinct object: the compiler then
 // orders reads of one only after its own copies.  Chunk c's buffer is
 // buf[c % 2] and its raw slab slab[c % 2].
-template <int NW, int M>
+template <int NW, int M, bool PRECISE>
 __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
                                          char* buf1, char* slab0, char* slab1, int lane) {
-    using SS = StateShape<NW>;
+    using SS = StateShape<NW, PRECISE>;
     if constexpr (SS::is_v(M)) {
         if (sp.nseg > 0)
 #pragma unroll
@@ -779,13 +958,13 @@ __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& 
     }
     wait_vm<0>();
     __syncthreads();
-    mem_step<NW, M>(sp, cx, Wv, buf0, slab0, slab1, 0, lane);
+    mem_step<NW, M, PRECISE>(sp, cx, Wv, buf0, slab0, slab1, 0, lane);
     __syncthreads();
     for (int j = 0; j < sp.nseg; j += 2) {
-        mem_step<NW, M>(sp, cx, Wv, buf1, slab1, slab0, j + 1, lane);
+        mem_step<NW, M, PRECISE>(sp, cx, Wv, buf1, slab1, slab0, j + 1, lane);
         lds_barrier();
         if (j + 1 < sp.nseg) {
-            mem_step<NW, M>(sp, cx, Wv, buf0, slab0, slab1, j + 2, lane);
+            mem_step<NW, M, PRECISE>(sp, cx, Wv, buf0, slab0, slab1, j + 2, lane);
             lds_barrier();
         }
     }
@@ -806,12 +985,14 @@ __device__ __forceinline__ const SplitParams& base_of(const VarlenParams& v) { r
 // its state and conv tail written by the segment that held its last chunk,
 // except in the first segment, where a sequence of no tokens copies its
 // states).
-template <int NW, class KP>
+template <int NW, bool PRECISE, class KP>
 __global__ __launch_bounds__(512) void state_kernel(KP kp) {
     constexpr bool VARLEN = std::is_same<KP, VarlenParams>::value;
-    using SS = StateShape<NW>;
+    using SS = StateShape<NW, PRECISE>;
     constexpr int N = SS::N, NCH = 2 * kD + N;
     const PrefillParams& p0 = base_of(kp).p;
+    // separate arrays: the compiler keeps their accesses apart (one block
+    // with computed offsets measured 10% slower)
     __shared__ __attribute__((aligned(16))) char buf0[SS::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[SS::BUF];
     __shared__ __attribute__((aligned(16))) char slab0[SS::NV * SS::SLAB];   // raw v slabs of the V waves,
@@ -890,11 +1071,13 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
             bf16x4 vv[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
-                vv[mb] = *reinterpret_cast<const bf16x4*>(cur + kBufVt + (cw * kVtLd + 16 * mb + 4 * lq) * 2);
+                vv[mb] = *reinterpret_cast<const bf16x4*>(cur + SS::VT + (cw * kVtLd + 16 * mb + 4 * lq) * 2);
             bf16x4 On[4];
-            chunk_products(cur, S, vv, On, li, lq, [&] {
+            auto store_prev = [&] {
                 if (j > 0) store_o(p, obase, Ob, sp.k0 + j - 1, li);
-            });
+            };
+            if constexpr (PRECISE) chunk_products_hl(cur, S, vv, On, li, lq, store_prev);
+            else chunk_products(cur, S, vv, On, li, lq, store_prev);
 #pragma unroll
             for (int m = 0; m < 4; ++m) Ob[m] = On[m];
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): every LDS read of this buffer has returned
@@ -905,10 +1088,11 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
             }
         }
         if (sp.nseg > 0) store_o(p, obase, Ob, sp.k0 + sp.nseg - 1, li);
+        const int64_t sb = opaque(cx.s_base);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p.rec_out[cx.s_base + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+            for (int e = 0; e < 4; ++e) p.rec_out[sb + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
     } else {
         // each V wave's slab region: part v_part(m) of the slab arrays
         const int m = wave - NW;
@@ -916,14 +1100,14 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         char* s0 = slab0 + vo;
         char* s1 = slab1 + vo;
         switch (m) {
-            case 0: mem_role<NW, 0>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 1: mem_role<NW, 1>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 2: mem_role<NW, 2>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 3: mem_role<NW, 3>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 0: mem_role<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 1: mem_role<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 2: mem_role<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            case 3: mem_role<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
             default:
                 if constexpr (NW == 2) {
-                    if (m == 4) mem_role<NW, 4>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
-                    else mem_role<NW, 5>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
+                    if (m == 4) mem_role<NW, 4, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
+                    else mem_role<NW, 5, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
                 }
                 break;
         }
@@ -935,12 +1119,12 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
     }
 }
 
-template <int NW>
+template <int NW, bool PRECISE>
 hipError_t launch_state(const SplitParams& sp, hipStream_t stream) {
     const int r = sp.p.num_v_heads / sp.p.num_k_heads;
     const int ng = sp.p.batch * sp.p.num_k_heads;
     const int blocks = ((ng + 7) / 8) * 8 * r * StateShape<NW>::SPLIT;
-    hipLaunchKernelGGL((state_kernel<NW, SplitParams>), dim3(blocks), dim3(512), 0, stream, sp);
+    hipLaunchKernelGGL((state_kernel<NW, PRECISE, SplitParams>), dim3(blocks), dim3(512), 0, stream, sp);
     return hipGetLastError();
 }
 
@@ -959,15 +1143,41 @@ int state_waves(const PrefillParams& p) {
 }
 
 hipError_t launch_state_any(const SplitParams& sp, hipStream_t stream) {
-    return state_waves(sp.p) == 4 ? launch_state<4>(sp, stream) : launch_state<2>(sp, stream);
+    const bool w4 = state_waves(sp.p) == 4;
+    if (sp.p.precise) return w4 ? launch_state<4, true>(sp, stream) : launch_state<2, true>(sp, stream);
+    return w4 ? launch_state<4, false>(sp, stream) : launch_state<2, false>(sp, stream);
 }
 
-template <int NW>
+template <int NW, bool PRECISE>
 hipError_t launch_state_varlen(const VarlenParams& vp, hipStream_t stream) {
     const int r = vp.sp.p.num_v_heads / vp.sp.p.num_k_heads;
     const int ng = vp.nb * vp.sp.p.num_k_heads;
     const int blocks = ((ng + 7) / 8) * 8 * r * StateShape<NW>::SPLIT;
-    hipLaunchKernelGGL((state_kernel<NW, VarlenParams>), dim3(blocks), dim3(512), 0, stream, vp);
+    hipLaunchKernelGGL((state_kernel<NW, PRECISE, VarlenParams>), dim3(blocks), dim3(512), 0, stream, vp);
+    return hipGetLastError();
+}
+
+// prep launch for (Neumann diagonal solve, precise mode)
+template <class KP>
+hipError_t launch_prep_any(const PrefillParams& p, const KP& kp, dim3 grid, hipStream_t stream) {
+    constexpr bool V = std::is_same<KP, VarlenParams>::value;
+    if (p.precise) {
+        if (p.diag_neumann) {
+            if constexpr (V) hipLaunchKernelGGL((prep_kernel_varlen<true, true>), grid, dim3(kPrepThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((prep_kernel<true, true>), grid, dim3(kPrepThreads), 0, stream, kp);
+        } else {
+            if constexpr (V) hipLaunchKernelGGL((prep_kernel_varlen<false, true>), grid, dim3(kPrepThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((prep_kernel<false, true>), grid, dim3(kPrepThreads), 0, stream, kp);
+        }
+    } else {
+        if (p.diag_neumann) {
+            if constexpr (V) hipLaunchKernelGGL((prep_kernel_varlen<true, false>), grid, dim3(kPrepThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((prep_kernel<true, false>), grid, dim3(kPrepThreads), 0, stream, kp);
+        } else {
+            if constexpr (V) hipLaunchKernelGGL((prep_kernel_varlen<false, false>), grid, dim3(kPrepThreads), 0, stream, kp);
+            else hipLaunchKernelGGL((prep_kernel<false, false>), grid, dim3(kPrepThreads), 0, stream, kp);
+        }
+    }
     return hipGetLastError();
 }
 
@@ -978,13 +1188,13 @@ bool prefill_split_supported(const PrefillParams& p) {
     return r >= 1 && r <= kMaxGroup;
 }
 
-uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads) {
-    return (uint64_t)batch * ((uint64_t)num_k_heads * kKeyRec + (uint64_t)num_v_heads * kValRec);
+uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads, bool precise) {
+    return (uint64_t)batch * ((uint64_t)num_k_heads * kKeyRec + (uint64_t)num_v_heads * val_rec_bytes(precise));
 }
 
 hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    const uint64_t per = prefill_split_chunk_bytes(p.batch, p.num_k_heads, p.num_v_heads);
+    const uint64_t per = prefill_split_chunk_bytes(p.batch, p.num_k_heads, p.num_v_heads, p.precise);
     const int64_t k_first = p.start_pos / kC;
     const int64_t k_end = p.seq_len > 0 ? (p.start_pos + p.seq_len - 1) / kC + 1 : k_first;
     // segments of at most 2^22 / (B H_k) chunks keep the prep grid's
@@ -996,6 +1206,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
     SplitParams sp{};
     sp.p = p;
     sp.ws = static_cast<char*>(ws);
+    sp.vrec_bytes = val_rec_bytes(p.precise);
     sp.first_seg = 1;
     if (k_end == k_first) {
         sp.k0 = k_first;
@@ -1011,9 +1222,7 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         sp.rec_stride = (int32_t)n;
         sp.last_seg = k0 + n == k_end;
         const dim3 grid((unsigned)(p.batch * p.num_k_heads * n));
-        if (p.diag_neumann) hipLaunchKernelGGL(prep_kernel<true>, grid, dim3(kPrepThreads), 0, stream, sp);
-        else hipLaunchKernelGGL(prep_kernel<false>, grid, dim3(kPrepThreads), 0, stream, sp);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_prep_any(p, sp, grid, stream);
         if (e != hipSuccess) return e;
         e = launch_state_any(sp, stream);
         if (e != hipSuccess) return e;
@@ -1022,8 +1231,9 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
     return hipSuccess;
 }
 
-uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads) {
-    return prefill_split_chunk_bytes(num_seqs < kVarlenGroup ? num_seqs : kVarlenGroup, num_k_heads, num_v_heads);
+uint64_t prefill_varlen_group_bytes(int num_seqs, int num_k_heads, int num_v_heads, bool precise) {
+    return prefill_split_chunk_bytes(num_seqs < kVarlenGroup ? num_seqs : kVarlenGroup, num_k_heads, num_v_heads,
+                                     precise);
 }
 
 int prefill_varlen_group() { return kVarlenGroup; }
@@ -1037,6 +1247,7 @@ hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqle
         VarlenParams vp{};
         vp.sp.p = p;
         vp.sp.ws = static_cast<char*>(ws);
+        vp.sp.vrec_bytes = val_rec_bytes(p.precise);
         vp.sp.rec_batch = G;
         vp.b0 = g0;
         vp.nb = G;
@@ -1047,7 +1258,7 @@ hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqle
             const int64_t n = len > 0 ? (st + len - 1) / kC + 1 - st / kC : 0;
             if (n > max_n) max_n = n;
         }
-        int64_t seg = (int64_t)(ws_bytes / prefill_split_chunk_bytes(G, p.num_k_heads, p.num_v_heads));
+        int64_t seg = (int64_t)(ws_bytes / prefill_split_chunk_bytes(G, p.num_k_heads, p.num_v_heads, p.precise));
         const int64_t grid_cap = ((int64_t)1 << 22) / ((int64_t)G * p.num_k_heads);
         if (seg > max_n) seg = max_n;
         if (seg > grid_cap) seg = grid_cap;
@@ -1060,12 +1271,13 @@ hipError_t launch_prefill_varlen(const PrefillParams& p, const int64_t* cu_seqle
             vp.j0 = j0;
             if (max_n > 0) {
                 const dim3 grid((unsigned)(G * p.num_k_heads * seg));
-                if (p.diag_neumann) hipLaunchKernelGGL(prep_kernel_varlen<true>, grid, dim3(kPrepThreads), 0, stream, vp);
-                else hipLaunchKernelGGL(prep_kernel_varlen<false>, grid, dim3(kPrepThreads), 0, stream, vp);
-                const hipError_t e = hipGetLastError();
+                const hipError_t e = launch_prep_any(p, vp, grid, stream);
                 if (e != hipSuccess) return e;
             }
-            const hipError_t e = nw == 4 ? launch_state_varlen<4>(vp, stream) : launch_state_varlen<2>(vp, stream);
+            const hipError_t e = p.precise ? (nw == 4 ? launch_state_varlen<4, true>(vp, stream)
+                                                      : launch_state_varlen<2, true>(vp, stream))
+                                           : (nw == 4 ? launch_state_varlen<4, false>(vp, stream)
+                                                      : launch_state_varlen<2, false>(vp, stream));
             if (e != hipSuccess) return e;
         }
     }

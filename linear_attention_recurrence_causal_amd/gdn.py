@@ -20,6 +20,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EALIAS, GDN_ESPACE, GDN_EHIP = range(6)
 GDN_F32, GDN_BF16 = 0, 1
+GDN_PRECISION_DEFAULT, GDN_PRECISION_HILO = 0, 1
 
 
 class GdnError(RuntimeError):
@@ -34,7 +35,7 @@ class _Config(ctypes.Structure):
                 ("num_v_heads", ctypes.c_int32), ("head_k_dim", ctypes.c_int32),
                 ("head_v_dim", ctypes.c_int32), ("conv_kernel", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+                ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float), ("precision", ctypes.c_int32)]
 
 
 class CkptEntry(ctypes.Structure):
@@ -92,6 +93,7 @@ class Config:
     io_dtype: int = GDN_BF16
     q_scale: float = 1.0
     l2_eps: float = 1e-6
+    precision: int = GDN_PRECISION_DEFAULT
 
     @property
     def conv_dim(self) -> int:
@@ -104,7 +106,7 @@ class Config:
     def c(self) -> _Config:
         return _Config(self.batch, self.num_k_heads, self.num_v_heads, self.head_k_dim,
                        self.head_v_dim, self.conv_kernel, self.chunk, self.io_dtype,
-                       self.q_scale, self.l2_eps)
+                       self.q_scale, self.l2_eps, self.precision)
 
 
 def _ptr(t):

@@ -102,6 +102,20 @@ def test_workspace_bytes(G):
     assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 13568)
 
 
+def test_workspace_bytes_precise(G):
+    """The precise mode's value record adds the bf16 lo parts of P and AN
+    (two more 6144-byte triangles) and pads the row scales to 2 KiB: 26624
+    bytes per value head and chunk; key records are unchanged."""
+    c = cfg(G, precision=G.GDN_PRECISION_HILO)
+    assert G.prefill_workspace_bytes(c, 16384) == 257 * (16 * 32768 + 48 * (2 * 6144 + 2048 + 2 * 6144))
+    for L in (1, 64, 65, 1000):
+        assert G.prefill_workspace_bytes(c, L) > G.prefill_workspace_bytes(cfg(G), L)
+    for p in (-1, 2, 7):
+        nb = ctypes.c_uint64(0)
+        bad = cfg(G, precision=p)
+        assert G.lib.gdn_prefill_workspace_bytes(ctypes.byref(bad.c()), 64, ctypes.byref(nb)) == G.GDN_EINVAL
+
+
 FAKE = 1 << 34  # aligned, far-apart addresses that are never dereferenced: every call below fails validation
 
 
@@ -154,6 +168,7 @@ def test_prefill_rejects_unsupported_and_aliasing(G):
     # bad config
     assert f(*prefill_args(G, cfg(G, num_v_heads=20))) == G.GDN_EINVAL
     assert f(*prefill_args(G, cfg(G, l2_eps=-1.0))) == G.GDN_EINVAL
+    assert f(*prefill_args(G, cfg(G, precision=2))) == G.GDN_EINVAL
 
 
 def test_decode_rejects_bad_arguments(G):

@@ -40,8 +40,8 @@ def cu_of(lens):
     return [0] + list(np.cumsum(lens))
 
 
-def run_varlen(G, w, inp, qkv, a, b, lens, starts, ckpt_interval=0, workspace="auto"):
-    c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+def run_varlen(G, w, inp, qkv, a, b, lens, starts, ckpt_interval=0, workspace="auto", precision=0):
+    c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads, precision=precision)
     ck = None
     if ckpt_interval:
         need = max(G.state_checkpoint(c, s, n, ckpt_interval)[1] for s, n in zip(starts, lens))
@@ -55,9 +55,9 @@ def run_varlen(G, w, inp, qkv, a, b, lens, starts, ckpt_interval=0, workspace="a
     return c, out, conv, S, ck
 
 
-def run_single(G, w, inp, i, n, start, ckpt_interval=0):
+def run_single(G, w, inp, i, n, start, ckpt_interval=0, precision=0):
     """Sequence i alone through gdn_prefill_chunked (two-pass path)."""
-    c = G.Config(batch=1, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    c = G.Config(batch=1, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads, precision=precision)
     sl = lambda t: None if t is None else t[i:i + 1].contiguous().cuda()
     ck = None
     if ckpt_interval:
@@ -73,10 +73,10 @@ def run_single(G, w, inp, i, n, start, ckpt_interval=0):
     return out[0], conv[0], S[0], ck
 
 
-def check_against_singles(G, w, inp, lens, starts, out, conv, S, ck=None, ckpt_interval=0, cfg=None):
+def check_against_singles(G, w, inp, lens, starts, out, conv, S, ck=None, ckpt_interval=0, cfg=None, precision=0):
     cu = cu_of(lens)
     for i, (n, st) in enumerate(zip(lens, starts)):
-        o1, c1, S1, ck1 = run_single(G, w, inp, i, n, st, ckpt_interval)
+        o1, c1, S1, ck1 = run_single(G, w, inp, i, n, st, ckpt_interval, precision)
         assert torch.equal(out[cu[i]:cu[i + 1]], o1), f"out of sequence {i}"
         assert torch.equal(conv[i], c1), f"conv tail of sequence {i}"
         assert torch.equal(S[i], S1), f"state of sequence {i}"
@@ -110,6 +110,25 @@ def test_varlen_equals_single_calls(G, segmented):
         assert ws.numel() == 8 * (2 * 32768 + 4 * 13568)
     c, out, conv, S, _ = run_varlen(G, w, inp, qkv, a, b, LENS, STARTS, workspace=ws)
     check_against_singles(G, w, inp, LENS, STARTS, out, conv, S)
+    assert finite(out, S)
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+def test_varlen_precise_equals_single_calls(G, segmented):
+    """The precise mode (larger value records) through the varlen entry:
+    bitwise equal to precise single calls, in one segment or in segments of
+    one chunk per sequence."""
+    w, inp, qkv, a, b = packed_case(LENS, STARTS, seed=64)
+    ws = "auto"
+    if segmented:
+        c = G.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads,
+                     precision=G.GDN_PRECISION_HILO)
+        ws = torch.empty(G.prefill_varlen_workspace_bytes(c, [0, 1] + [1] * 7, [0] * 8),
+                         dtype=torch.uint8, device="cuda")
+        assert ws.numel() == 8 * (2 * 32768 + 4 * 26624)
+    c, out, conv, S, _ = run_varlen(G, w, inp, qkv, a, b, LENS, STARTS, workspace=ws,
+                                    precision=G.GDN_PRECISION_HILO)
+    check_against_singles(G, w, inp, LENS, STARTS, out, conv, S, precision=G.GDN_PRECISION_HILO)
     assert finite(out, S)
 
 
