@@ -442,7 +442,7 @@ void prep_kernel_varlen(VarlenParams vp) {
 // LDS pointer from a generic pointer into LDS by its low 32 bits (the LDS
 // offset): no address-space cast, whose null check costs a compare and a
 // select per copy
-#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(uint32_t)(uintptr_t)(x))
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(uintptr_t)(uint32_t)(uintptr_t)(x))
 
 
 // LDS buffer of one chunk: Q | K | P | AN | rows [| P_lo | AN_lo] | V^T (V^T
