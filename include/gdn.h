@@ -195,6 +195,36 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
                                void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* gdn_prefill_chunked without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc)
+ * but want the two-pass path rather than the fused kernel.  Arguments,
+ * results and errors are those of gdn_prefill_chunked; the chunk records live
+ * in a static device array of GDN_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library's code object holds on every device it is loaded on, until the
+ * process ends.  A call whose records exceed it runs in segments, as with a
+ * small workspace.
+ *   - GDN_ESPACE if one chunk's records do not fit the array: B * (H_k *
+ *     32768 + H_v * 13568) bytes (26624 per value head in the precise mode)
+ *     above 64 MiB, e.g. B above 57 with 16 key and 48 value heads.
+ *   - The array's address is looked up (hipGetSymbolAddress) on the first
+ *     call on a device, with that device current; GDN_EHIP if that fails.
+ *   - Every call on one device shares its array: calls that overlap in time
+ *     on one device (two streams, two threads) race and give wrong results.
+ *     Consecutive calls on one stream are safe.  Nothing in the array has to
+ *     start at zero: each segment's first pass writes every record its
+ *     second pass reads.
+ *   - A head group H_v / H_k above 8 or GDN_PREFILL_PATH=fused runs the
+ *     fused kernel, which needs no scratch. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((uint64_t)64 << 20)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                                       const void* qkv, const void* a, const void* b, const void* conv_w,
+                                       const float* A_log, const float* dt_bias,
+                                       const void* conv_state_in, void* conv_state_out,
+                                       const float* rec_state_in, float* rec_state_out, void* out,
+                                       void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                                       void* stream);
+
 /* Workspace for gdn_prefill_varlen (host only): the bytes with which every
  * group of up to 64 sequences runs each pass once,
  *   max over groups of (sequences of the group) * (chunks its longest
@@ -326,7 +356,12 @@ gdn_status gdn_output_gate(const gdn_config* cfg, int64_t num_tokens, const void
 /* Static description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 
-/* Library version, major*10000 + minor*100 + patch. */
+/* Library version, major*10000 + minor*100 + patch.  gdn_config is passed
+ * by pointer, so a caller compiled against a header of another minor
+ * version must not call the library: compare gdn_version() with
+ * GDN_VERSION first.  0.2.0 added gdn_config.precision and
+ * gdn_prefill_chunked_noalloc. */
+#define GDN_VERSION 200
 int32_t gdn_version(void);
 
 #ifdef __cplusplus

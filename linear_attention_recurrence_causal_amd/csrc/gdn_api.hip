@@ -1,11 +1,14 @@
 // gdn_api.hip -- the C ABI of libgdn: validation, checkpoint plan, dispatch.
 //
 // Every entry point validates all arguments before it enqueues anything, so
-// an error leaves every output untouched.  No allocation, no synchronisation,
-// no global mutable state.
+// an error leaves every output untouched.  No allocation and no
+// synchronisation.  The only global state is the device address of the
+// static scratch array of gdn_prefill_chunked_noalloc, looked up once per
+// device.
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "gdn_launch.h"
 #include "../../include/gdn.h"
@@ -82,6 +85,44 @@ Plan checkpoint_plan(const gdn_config* c, int64_t start_pos, int64_t seq_len, in
 
 }  // namespace
 
+// Scratch of gdn_prefill_chunked_noalloc: the two-pass path's chunk records,
+// in a device array that the code object brings (each device the library is
+// loaded on holds its own copy until the process ends).  In host code the
+// name `scratch` is only a stand-in; its device address comes from
+// hipGetSymbolAddress, per device.
+static constexpr uint64_t kNoAllocScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of the scratch array on the device of `stream` (the current
+// device for the null stream), looked up on the first call on that device
+// with the device current.
+gdn_status scratch_of(void* stream, void** ptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GDN_EHIP;
+    hipDevice_t dev = cur;
+    if (stream && hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess) return GDN_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return GDN_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GDN_EHIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return GDN_EHIP;
+        if (e != hipSuccess || !p) return GDN_EHIP;
+        scratch_addr[dev] = p;
+    }
+    *ptr = scratch_addr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* gdn_status_string(gdn_status s) {
@@ -96,7 +137,7 @@ const char* gdn_status_string(gdn_status s) {
     }
 }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return GDN_VERSION; }
 
 gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_t seq_len,
                                 int64_t interval, gdn_ckpt_entry* entries, int64_t capacity,
@@ -238,6 +279,24 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream))
                                   : gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                                       const void* qkv, const void* a, const void* b, const void* conv_w,
+                                       const float* A_log, const float* dt_bias, const void* conv_state_in,
+                                       void* conv_state_out, const float* rec_state_in, float* rec_state_out,
+                                       void* out, void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                                       void* stream) {
+    if (gdn_status s = check_config(cfg)) return s;
+    // one chunk's records must fit the array; longer calls run in segments
+    if (gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads,
+                                       cfg->precision == GDN_PRECISION_HILO) > kNoAllocScratchBytes)
+        return GDN_ESPACE;
+    void* ws = nullptr;
+    if (gdn_status s = scratch_of(stream, &ws)) return s;
+    return gdn_prefill_chunked(cfg, seq_len, start_pos, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in,
+                               conv_state_out, rec_state_in, rec_state_out, out, ckpt_buf, ckpt_buf_bytes,
+                               ckpt_interval, ws, kNoAllocScratchBytes, stream);
 }
 
 // Output gate arguments of a decode call (y == NULL: no gate).

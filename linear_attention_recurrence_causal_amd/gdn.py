@@ -50,6 +50,9 @@ _CFG = ctypes.POINTER(_Config)
 _lib.gdn_status_string.argtypes = [ctypes.c_int32]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_version.restype = ctypes.c_int32
+GDN_VERSION = 200   # the header this binding's structures mirror
+if _lib.gdn_version() != GDN_VERSION:
+    raise ImportError(f"{_LIB_PATH} is version {_lib.gdn_version()}, this binding expects {GDN_VERSION}: rebuild")
 _lib.gdn_state_checkpoint.argtypes = [_CFG, _I64, _I64, _I64, ctypes.POINTER(CkptEntry), _I64,
                                       ctypes.POINTER(_I64), ctypes.POINTER(_U64)]
 _lib.gdn_state_checkpoint.restype = ctypes.c_int32
@@ -58,6 +61,10 @@ _lib.gdn_prefill_workspace_bytes.restype = ctypes.c_int32
 _lib.gdn_prefill_chunked.argtypes = [_CFG, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _U64, _I64, _P, _U64, _P]
 _lib.gdn_prefill_chunked.restype = ctypes.c_int32
+_lib.gdn_prefill_chunked_noalloc.argtypes = [_CFG, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _U64, _I64, _P]
+_lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int32
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _lib.gdn_decode_step.argtypes = [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.gdn_decode_multi.argtypes = [_CFG, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P]
@@ -171,19 +178,11 @@ def prefill_workspace_bytes(cfg: Config, seq_len: int) -> int:
     return n.value
 
 
-def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
-                    rec_state_in=None, *, start_pos: int = 0, ckpt_interval: int = 0,
-                    ckpt_buf=None, out=None, conv_state_out=None, rec_state_out=None,
-                    workspace="auto", stream=None):
-    """Chunked prefill; returns (out, conv_state_out, rec_state_out).
-
-    Outputs not passed in are allocated with torch.  ``ckpt_buf`` is a uint8
-    device tensor of at least ``state_checkpoint(...)[1]`` bytes.
-    ``workspace``: "auto" allocates ``prefill_workspace_bytes`` (two-pass
-    path, whole call in one segment); a contiguous uint8 device tensor is used
-    as given (any size; below one chunk's worth the fused path runs); None
-    runs the fused single-pass kernel.
-    """
+def _prefill_buffers(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, rec_state_in,
+                     ckpt_buf, out, conv_state_out, rec_state_out, stream):
+    """Shape checks of a prefill call and the outputs (allocated with torch
+    when not given); returns (L, out, conv_state_out, rec_state_out,
+    ckpt_bytes)."""
     B, Hv, dk, dv = cfg.batch, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim
     L = qkv.shape[1]
     io = cfg.torch_io
@@ -210,11 +209,30 @@ def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_i
         if not ckpt_buf.is_cuda or not ckpt_buf.is_contiguous():
             raise ValueError("ckpt_buf must be a contiguous device tensor")
         ck_bytes = ckpt_buf.numel() * ckpt_buf.element_size()
+    return L, out, conv_state_out, rec_state_out, ck_bytes
+
+
+def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
+                    rec_state_in=None, *, start_pos: int = 0, ckpt_interval: int = 0,
+                    ckpt_buf=None, out=None, conv_state_out=None, rec_state_out=None,
+                    workspace="auto", stream=None):
+    """Chunked prefill; returns (out, conv_state_out, rec_state_out).
+
+    Outputs not passed in are allocated with torch.  ``ckpt_buf`` is a uint8
+    device tensor of at least ``state_checkpoint(...)[1]`` bytes.
+    ``workspace``: "auto" allocates ``prefill_workspace_bytes`` (two-pass
+    path, whole call in one segment); a contiguous uint8 device tensor is used
+    as given (any size; below one chunk's worth the fused path runs); None
+    runs the fused single-pass kernel.
+    """
+    L, out, conv_state_out, rec_state_out, ck_bytes = _prefill_buffers(
+        cfg, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, rec_state_in, ckpt_buf, out,
+        conv_state_out, rec_state_out, stream)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
         ws = prefill_workspace_bytes(cfg, L)
-        wsbuf = _empty(ws, torch.uint8, dev, stream) if ws else None
+        wsbuf = _empty(ws, torch.uint8, qkv.device, stream) if ws else None
     elif workspace is None:
         ws, wsbuf = 0, None
     else:
@@ -228,6 +246,27 @@ def prefill_chunked(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_i
         ckpt_interval, _ptr(wsbuf), ws, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_prefill_chunked")
+    return out, conv_state_out, rec_state_out
+
+
+def prefill_chunked_noalloc(cfg: Config, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in=None,
+                            rec_state_in=None, *, start_pos: int = 0, ckpt_interval: int = 0,
+                            ckpt_buf=None, out=None, conv_state_out=None, rec_state_out=None,
+                            stream=None):
+    """gdn_prefill_chunked_noalloc: the two-pass prefill on the library's
+    static scratch array (no workspace, nothing allocated by the call; the
+    outputs are allocated here only when not passed in).  Returns (out,
+    conv_state_out, rec_state_out)."""
+    L, out, conv_state_out, rec_state_out, ck_bytes = _prefill_buffers(
+        cfg, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, rec_state_in, ckpt_buf, out,
+        conv_state_out, rec_state_out, stream)
+    st = _lib.gdn_prefill_chunked_noalloc(
+        ctypes.byref(cfg.c()), L, start_pos, _ptr(qkv), _ptr(a), _ptr(b), _ptr(conv_w),
+        _ptr(A_log), _ptr(dt_bias), _ptr(conv_state_in), _ptr(conv_state_out),
+        _ptr(rec_state_in), _ptr(rec_state_out), _ptr(out), _ptr(ckpt_buf), ck_bytes,
+        ckpt_interval, _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_chunked_noalloc")
     return out, conv_state_out, rec_state_out
 
 

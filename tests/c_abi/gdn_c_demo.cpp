@@ -77,6 +77,10 @@ std::vector<uint16_t> bf16_vec(size_t n, float scale, float shift = 0.f) {
 }  // namespace
 
 int main() {
+    if (gdn_version() != GDN_VERSION) {
+        std::fprintf(stderr, "libgdn %d, header %d\n", gdn_version(), GDN_VERSION);
+        return 2;
+    }
     CHECK_HIP(hipSetDevice(0));
     gdn_config cfg{};
     cfg.batch = 2;
@@ -136,6 +140,14 @@ int main() {
         if (!std::isfinite(from_bf16(v))) return 5;
     for (float v : s1)
         if (!std::isfinite(v)) return 5;
+    // the two-pass path on the library's static scratch (no workspace)
+    CHECK_GDN(gdn_prefill_chunked_noalloc(&cfg, L, 0, qkv, a, b, conv_w, A_log, dt_bias, nullptr, conv1, nullptr,
+                                          rec1, out1, nullptr, 0, 0, nullptr));
+    CHECK_HIP(hipDeviceSynchronize());
+    if (download(out1, out_n) != o2 || download(rec1, rec_n) != s2 || download(conv1, conv_n) != c2) {
+        std::fprintf(stderr, "static-scratch prefill differs\n");
+        return 4;
+    }
 
     // T decode steps from the prefill's states, one call each, then one
     // T-token call; the decode inputs are [T][B][...] for the single steps

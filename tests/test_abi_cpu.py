@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(G):
     assert {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_checkpoint"} <= set(names)
     for n in names:
         assert hasattr(G.lib, n), n
-    assert G.lib.gdn_version() >= 100
+    assert G.lib.gdn_version() == 200   # GDN_VERSION of include/gdn.h
     for s in range(6):
         assert G.lib.gdn_status_string(s)
     assert G.lib.gdn_status_string(99) == b"unknown status"
