@@ -13,9 +13,14 @@ times the fp64 CPU oracle on a bounded sample of the prefill workload.
 The multi-token decode step (4 tokens per sequence per call) is timed on the
 decode workload too, and so is the output gate (RMSNormGated with z): on its
 own over the prefill output shape, and fused into the decode step.  The
-varlen prefill is timed on a serving-like mix of eight sequences.
+varlen prefill is timed on a serving-like mix of eight sequences.  Two more
+workloads get keys of their own: the Qwen3-Coder-Next-shaped prefill (B=8 x
+4096 tokens, 16/32 heads, nonzero initial states) followed by 64 decode steps
+from the states it produced, and the 262,144-token Qwen3.6-27B-shaped prefill
+that writes 64 checkpoint slots (one per 4096 tokens).  The precise mode
+(bf16 hi + lo operands) is timed on the 16k prefill beside the default.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTIONS]
 """
 from __future__ import annotations
 
@@ -130,10 +135,22 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     t = time_events(lambda: step(ws), args.steps, args.warmup)
     t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
+    # the precise mode (bf16 hi + lo on every state-path product), both paths
+    cfg_p = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads,
+                       precision=gdn.GDN_PRECISION_HILO)
+    ws_p = torch.empty(gdn.prefill_workspace_bytes(cfg_p, w.seq_len), dtype=torch.uint8, device="cuda")
+
+    def step_p(workspace):
+        gdn.prefill_chunked(cfg_p, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"],
+                            None, None, out=out, conv_state_out=conv, rec_state_out=S, workspace=workspace)
+
+    t_p = time_events(lambda: step_p(ws_p), max(2, args.steps // 2), 5)
+    t_pf = time_events(lambda: step_p(None), 2, 1)
+    del ws_p
     tokens = w.batch * w.seq_len
     flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
     byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads)
-    return w, t, t_fused, tokens, flops, byts, inp, ws.numel()
+    return w, t, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws.numel()
 
 
 def bench_decode(args):
@@ -176,8 +193,24 @@ def bench_decode(args):
         evs.append((e0, e1))
     torch.cuda.synchronize()
     flushed = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
-    del flush, total
-    return w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads), flushed[len(flushed) // 2]
+    # the ceiling for those bytes from HBM: a plain copy of one state's size
+    # (read 100.7 MB, write 100.7 MB), timed the same way after the same read
+    src = torch.ones_like(S)
+    dst = torch.empty_like(S)
+    evs = []
+    for k in range(32):
+        torch.sum(flush, dim=0, out=total)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        dst.copy_(src)
+        e1.record(s)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    copies = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+    copy_bytes = 2 * S.numel() * 4
+    del flush, total, src, dst
+    return (w, t, decode_bytes(w.batch, w.num_k_heads, w.num_v_heads), flushed[len(flushed) // 2],
+            (copy_bytes, copies[len(copies) // 2]))
 
 
 def bench_decode_multi(args, T=4):
@@ -322,6 +355,94 @@ def bench_varlen(args):
             "single_calls_us": t1 * 1e6, "speedup_vs_single_calls": t1 / t}
 
 
+def prefill_roofline(kernel, flops, t, byts, profile):
+    return {"kernel": kernel, "bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_FLOPS / 1e12,
+            "unit": "TFLOP/s", "frac": flops / t / BF16_PEAK_FLOPS,
+            "traffic": profiled_traffic(profile, PREFILL_SOURCES),
+            "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
+            "hbm_floor_frac": byts / t / HBM_PEAK_BYTES}
+
+
+def bench_coder(args):
+    """Qwen3-Coder-Next-shaped layer: a B=8 x 4096-token chunked prefill (16
+    key / 32 value heads, nonzero initial conv and recurrent states, two-pass
+    path with a workspace), then 64 one-token decode steps continuing from
+    the states that prefill produced."""
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[3]
+    d = {k: (None if v is None else v.cuda()) for k, v in I.generate(w).items()}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    out = torch.empty(w.batch, w.seq_len, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    conv = torch.empty_like(d["conv_state"])
+    S = torch.empty_like(d["rec_state"])
+    ws = torch.empty(gdn.prefill_workspace_bytes(cfg, w.seq_len), dtype=torch.uint8, device="cuda")
+    t = time_events(lambda: gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"],
+                                                d["dt_bias"], d["conv_state"], d["rec_state"], out=out,
+                                                conv_state_out=conv, rec_state_out=S, workspace=ws),
+                    args.steps, args.warmup)
+    del ws
+    Sd = S.clone()
+    cs = [conv.clone(), torch.empty_like(conv)]
+    dout = torch.empty(w.batch, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    n = w.decode_steps
+    state = {"i": 0}
+
+    def dstep():
+        i = state["i"]
+        k = i % n
+        gdn.decode_step(cfg, d["dec_qkv"][k], d["dec_a"][k], d["dec_b"][k], d["conv_w"], d["A_log"],
+                        d["dt_bias"], cs[i % 2], Sd, out=dout, conv_state_out=cs[(i + 1) % 2], rec_state_out=Sd)
+        state["i"] = i + 1
+
+    td = time_events(dstep, n, 4 * n)
+    tokens = w.batch * w.seq_len
+    flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
+    byts = varlen_bytes(tokens, w.batch, w.num_k_heads, w.num_v_heads)
+    bd = decode_bytes(w.batch, w.num_k_heads, w.num_v_heads)
+    return {"workload": "Qwen3-Coder-Next-shaped GDN layer: B=8 x 4096-token chunked prefill (16/32 heads, "
+                        "nonzero initial states), then 64 decode steps from the produced states",
+            "prefill": {"ms_per_call": t * 1e3, "tokens_per_s": tokens / t,
+                        "roofline": prefill_roofline("two-pass prefill: prep_kernel + state_kernel<4> (one call)",
+                                                     flops, t, byts, "prefill_two_pass_coder_next_b8_4k.md")},
+            "decode": {"us_per_step": td * 1e6, "tokens_per_s": w.batch / td, "bytes_per_step": bd,
+                       "roofline": {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": bd / td / 1e9,
+                                    "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
+                                    "frac": bd / td / HBM_PEAK_BYTES,
+                                    "traffic": profiled_traffic("decode_step_kernel_coder_next_b8.md",
+                                                                DECODE_SOURCES)}}}
+
+
+def bench_long(args):
+    """The 262,144-token Qwen3.6-27B-shaped prefill (B=1, 16/48 heads) in one
+    call with a workspace, writing a conv + recurrent checkpoint slot every
+    4096 tokens (64 slots)."""
+    import torch
+    from linear_attention_recurrence_causal_amd import gdn, inputs as I
+    w = I.WORKLOADS[4]
+    d = {k: (None if v is None else v.cuda()) for k, v in I.generate(w).items()}
+    cfg = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads)
+    ents, nb = gdn.state_checkpoint(cfg, 0, w.seq_len, w.ckpt_interval)
+    ck = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty(w.batch, w.seq_len, w.num_v_heads, 128, dtype=torch.bfloat16, device="cuda")
+    conv = torch.empty(w.batch, w.conv_dim, 3, dtype=torch.bfloat16, device="cuda")
+    S = torch.empty(w.batch, w.num_v_heads, 128, 128, device="cuda")
+    ws = torch.empty(gdn.prefill_workspace_bytes(cfg, w.seq_len), dtype=torch.uint8, device="cuda")
+    t = time_events(lambda: gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"],
+                                                d["dt_bias"], None, None, ckpt_interval=w.ckpt_interval,
+                                                ckpt_buf=ck, out=out, conv_state_out=conv, rec_state_out=S,
+                                                workspace=ws),
+                    max(2, args.steps // 4), 2)
+    tokens = w.batch * w.seq_len
+    flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
+    byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads) + len(ents) * (nb // len(ents))
+    return {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill of 262,144 tokens (B=1, 16/48 heads) "
+                        "with a checkpoint slot every 4096 tokens (64 slots)",
+            "ms_per_call": t * 1e3, "tokens_per_s": tokens / t, "checkpoint_slots": len(ents),
+            "roofline": prefill_roofline("two-pass prefill: prep_kernel + state_kernel<2> (one call)", flops, t,
+                                         byts, "prefill_two_pass_qwen36-27b_prefill_256k.md")}
+
+
 def cpu_baseline(inp, tokens):
     from linear_attention_recurrence_causal_amd import inputs as I
     from oracle import oracle as O
@@ -347,6 +468,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="comma-separated sections to run (prefill, decode, gate, varlen, coder, long, cpu); "
+                         "default all.  Without prefill the line has no headline value (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 elementwise copy (read 1 GiB, write 1 GiB) "
                          "three times, the reference for scaling HBM byte counters")
@@ -364,44 +488,54 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
-    print("bench: prefill", file=sys.stderr, flush=True)
-    w, t, t_fused, tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
-    achieved = flops / t
-    rec = {
-        "metric": METRIC,
-        "value": tokens / t,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": t * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill", "batch": w.batch,
-                   "seq_len": w.seq_len, "num_k_heads": w.num_k_heads,
-                   "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk": 64,
-                   "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "two-pass prefill: prep_kernel + state_kernel<2> (one call)",
-                     "bound": "mfma", "achieved": achieved / 1e12,
-                     "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_FLOPS,
-                     "traffic": profiled_traffic("prefill_two_pass_qwen36-27b_prefill_16k.md",
-                                                 PREFILL_SOURCES),
-                     "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
-                     "hbm_floor_frac": byts / t / HBM_PEAK_BYTES,
-                     "workspace_bytes": ws_bytes},
-        "fused_path": {"kernel": "prefill_kernel<8>", "ms_per_call": t_fused * 1e3,
-                       "tokens_per_s": tokens / t_fused,
-                       "frac": flops / t_fused / BF16_PEAK_FLOPS,
-                       "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
-                                                   FUSED_SOURCES)},
-    }
-    if not args.no_decode:
+    sections = {"prefill", "decode", "gate", "varlen", "coder", "long", "cpu"}
+    if args.only:
+        want = {x.strip() for x in args.only.split(",") if x.strip()}
+        bad = want - sections
+        if bad:
+            ap.error(f"unknown sections {sorted(bad)}")
+        sections = want
+    if args.no_decode:
+        sections -= {"decode", "gate"}
+    if args.no_cpu_baseline:
+        sections.discard("cpu")
+    rec = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    inp = None
+    if "prefill" in sections:
+        print("bench: prefill", file=sys.stderr, flush=True)
+        w, t, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
+        achieved = flops / t
+        rec.update({
+            "value": tokens / t,
+            "ms_per_step": t * 1e3,
+            "config": {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill", "batch": w.batch,
+                       "seq_len": w.seq_len, "num_k_heads": w.num_k_heads,
+                       "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk": 64,
+                       "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
+            "roofline": {"kernel": "two-pass prefill: prep_kernel + state_kernel<2> (one call)",
+                         "bound": "mfma", "achieved": achieved / 1e12,
+                         "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": achieved / BF16_PEAK_FLOPS,
+                         "traffic": profiled_traffic("prefill_two_pass_qwen36-27b_prefill_16k.md",
+                                                     PREFILL_SOURCES),
+                         "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
+                         "hbm_floor_frac": byts / t / HBM_PEAK_BYTES,
+                         "workspace_bytes": ws_bytes},
+            "fused_path": {"kernel": "prefill_kernel<8>", "ms_per_call": t_fused * 1e3,
+                           "tokens_per_s": tokens / t_fused,
+                           "frac": flops / t_fused / BF16_PEAK_FLOPS,
+                           "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
+                                                       FUSED_SOURCES)},
+            "precise_mode": {"what": "gdn_config.precision = GDN_PRECISION_HILO (bf16 hi + lo on every "
+                                     "state-path product) on the same prefill",
+                             "two_pass_ms_per_call": t_p * 1e3, "two_pass_vs_default": t_p / t,
+                             "fused_ms_per_call": t_pf * 1e3, "fused_vs_default": t_pf / t_fused},
+        })
+    if "decode" in sections:
         print("bench: decode", file=sys.stderr, flush=True)
-        wd, td, bd, tf = bench_decode(args)
+        wd, td, bd, tf, (cb, tc) = bench_decode(args)
         rec["decode"] = {
             "workload": "Qwen3.6-27B-shaped GDN layer decode step, B=32, 256 consecutive steps",
             "us_per_step": td * 1e6, "tokens_per_s": wd.batch / td, "bytes_per_step": bd,
@@ -413,19 +547,36 @@ def main():
             "mall_flushed": {"what": "median of 32 single steps, each after a 512 MiB read that "
                                      "evicts the 256 MB Infinity Cache",
                              "us_per_step": tf * 1e6, "achieved": bd / tf / 1e9, "unit": "GB/s",
-                             "frac": bd / tf / HBM_PEAK_BYTES},
+                             "frac": bd / tf / HBM_PEAK_BYTES,
+                             "cold_copy_ceiling": {"what": "median of 32 plain copies of one state's bytes "
+                                                           "(read 100.7 MB, write 100.7 MB), each after "
+                                                           "the same 512 MiB read",
+                                                   "bytes": cb, "us": tc * 1e6, "achieved": cb / tc / 1e9,
+                                                   "frac": cb / tc / HBM_PEAK_BYTES,
+                                                   "step_vs_copy_rate": (bd / tf) / (cb / tc)}},
         }
         wm, T, tm = bench_decode_multi(args)
         rec["decode_multi"] = {
             "workload": f"the same decode workload, {T} tokens per sequence per call (verify step)",
             "us_per_call": tm * 1e6, "tokens_per_s": wm.batch * T / tm,
             "speedup_vs_single_steps": T * td / tm}
+    if "gate" in sections:
         print("bench: output gate", file=sys.stderr, flush=True)
         rec["output_gate"] = bench_output_gate(args)
-    print("bench: varlen prefill", file=sys.stderr, flush=True)
-    rec["prefill_varlen"] = bench_varlen(args)
-    if not args.no_cpu_baseline:
+    if "varlen" in sections:
+        print("bench: varlen prefill", file=sys.stderr, flush=True)
+        rec["prefill_varlen"] = bench_varlen(args)
+    if "coder" in sections:
+        print("bench: coder-next prefill + decode", file=sys.stderr, flush=True)
+        rec["coder_next_prefill_decode"] = bench_coder(args)
+    if "long" in sections:
+        print("bench: 256k prefill with checkpoints", file=sys.stderr, flush=True)
+        rec["long_context_256k"] = bench_long(args)
+    if "cpu" in sections:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        if inp is None:
+            from linear_attention_recurrence_causal_amd import inputs as I
+            inp = I.generate(I.WORKLOADS[2])
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
     if args.calibrate_copy:
         n = 1 << 28
