@@ -432,6 +432,52 @@ def test_prefill_precise_recipes(G, waves, path, nw, kind):
     compare(f"precise {kind} {path} nw={nw}", w, out, conv, S, oracle_prefill(w, inp))
 
 
+def test_prefill_precise_paths_agree(G):
+    """The precise mode on both paths (the fused kernel's 4-wave instance
+    and the two-pass kernels), from nonzero states at an unaligned start:
+    the same operations in the same order, so the same bits; printed, and
+    held to a bar well inside the oracle's."""
+    w = small(batch=2, seq_len=450, num_k_heads=2, num_v_heads=6, init_state=True, seed=35)
+    d = to_dev(I.generate(w))
+    hl = G.GDN_PRECISION_HILO
+    f = gpu_prefill(G, w, d, seq=slice(19, 450), start_pos=83, path="fused", precision=hl)
+    s = gpu_prefill(G, w, d, seq=slice(19, 450), start_pos=83, path="split", precision=hl)
+    e_out = rel(s[0].double().cpu().numpy(), f[0].double().cpu().numpy())
+    e_state = rel(s[2].double().cpu().numpy(), f[2].double().cpu().numpy())
+    print(f"[precise paths] out rel {e_out:.3e}, state rel {e_state:.3e}, bitwise "
+          f"{torch.equal(f[0], s[0]) and torch.equal(f[2], s[2])}", flush=True)
+    assert torch.equal(f[1], s[1])
+    assert e_out <= 1e-3 and e_state <= 1e-4
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_precise_checkpoints_and_bitwise_resume(G, path):
+    """The precise mode writes the oracle's state into every checkpoint slot
+    (every 128 tokens), and resuming from a slot repeats the uninterrupted
+    call bit for bit."""
+    w = small(seq_len=520, init_state=True, seed=36)
+    inp = I.generate(w)
+    d = to_dev(inp)
+    hl = G.GDN_PRECISION_HILO
+    c = cfg_of(G, w, hl)
+    ents, nbytes = G.state_checkpoint(c, 0, 520, 128)
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out, conv, S = gpu_prefill(G, w, d, ckpt_interval=128, ckpt_buf=buf, path=path, precision=hl)
+    ref = oracle_prefill(w, inp, want_ckpt=True, ckpt_interval=128)
+    compare(f"precise ckpt run {path}", w, out, conv, S, ref)
+    n = w.batch * w.num_v_heads * 128 * 128 * 4
+    for j, e in enumerate(ents):
+        rs = buf[e.rec_offset:e.rec_offset + n].view(torch.float32).view(w.batch, w.num_v_heads, 128, 128)
+        assert state_rel_per_head(rs.double().cpu().numpy(), ref["ckpt_S"][j]) <= TOL_BF16_STATE, j
+    e = ents[2]   # resume at position 384
+    cv = buf[e.conv_offset:e.conv_offset + w.batch * w.conv_dim * 3 * 2].view(torch.bfloat16)
+    rs = buf[e.rec_offset:e.rec_offset + n].view(torch.float32)
+    o2, c2, S2 = gpu_prefill(G, w, d, seq=slice(384, 520), start_pos=384,
+                             conv_in=cv.view(w.batch, w.conv_dim, 3).clone(),
+                             rec_in=rs.view(w.batch, w.num_v_heads, 128, 128).clone(), path=path, precision=hl)
+    assert torch.equal(o2, out[:, 384:]) and torch.equal(S2, S) and torch.equal(c2, conv)
+
+
 @pytest.mark.parametrize("chunks", [1, 3])
 def test_prefill_precise_segmented_workspace(G, chunks):
     """Precise mode with a workspace of 1 or 3 chunks' records (the larger
