@@ -435,8 +435,7 @@ def test_prefill_precise_recipes(G, waves, path, nw, kind):
 def test_prefill_precise_paths_agree(G):
     """The precise mode on both paths (the fused kernel's 4-wave instance
     and the two-pass kernels), from nonzero states at an unaligned start:
-    the same operations in the same order, so the same bits; printed, and
-    held to a bar well inside the oracle's."""
+    the same operations in the same order, so the same bits."""
     w = small(batch=2, seq_len=450, num_k_heads=2, num_v_heads=6, init_state=True, seed=35)
     d = to_dev(I.generate(w))
     hl = G.GDN_PRECISION_HILO
@@ -447,7 +446,7 @@ def test_prefill_precise_paths_agree(G):
     print(f"[precise paths] out rel {e_out:.3e}, state rel {e_state:.3e}, bitwise "
           f"{torch.equal(f[0], s[0]) and torch.equal(f[2], s[2])}", flush=True)
     assert torch.equal(f[1], s[1])
-    assert e_out <= 1e-3 and e_state <= 1e-4
+    assert torch.equal(f[0], s[0]) and torch.equal(f[2], s[2])
 
 
 @pytest.mark.parametrize("path", PATHS)
