@@ -462,7 +462,7 @@ static_assert(kBufTok - kBufPA == kRecTok && kBufPAlo - kBufPA == kRecPlo && kRe
 // 32..43: P | AN triangles, 44..45: the rows of scales (1280 bytes, padded
 // to 2 KiB in the precise mode); in the precise mode 46..57: the lo parts of
 // P | AN.
-constexpr int kPiecesK = 16, kPiecesPA = 32, kPiecesTok = 44, kPiecesLo = 46;
+constexpr int kPiecesK = 16, kPiecesPA = 32, kPiecesLo = 46;
 constexpr int num_pieces(bool precise) { return precise ? kPiecesLo + 12 : kPiecesLo; }
 
 template <bool PRECISE>
@@ -759,11 +759,12 @@ __device__ __forceinline__ int64_t state_channel(const PrefillParams& p, const S
 // (16 state columns each) and 8 - NW memory waves (m = wave - NW; wave w
 // runs on SIMD w % 4).  Memory wave m copies the record pieces
 // [rec_lo(m), rec_hi(m)) of each chunk.  The V waves (NW = 4: every memory
-// wave; NW = 2: m = 4, 5, on the SIMDs without a compute wave) also run the
-// front end of the slice's v channels, part v_part(m) of the chunk's rows,
-// one 4-channel x 4-row item per lane, from a raw slab of exactly those rows
-// (+ 3 rows of conv history) that the same wave copied one chunk earlier
-// into its own slab region.
+// wave, which also copies record pieces; NW = 2: m = 4, 5, on the SIMDs
+// without a compute wave, which copy none) run the front end of the slice's
+// v channels, part v_part(m) of the chunk's rows, one 4-channel x 4-row item
+// per lane, from a raw slab of exactly those rows (+ 3 rows of conv history)
+// that the same wave copied into its own slab region one chunk (NW = 4) or
+// two chunks (NW = 2) earlier.
 template <int NW, bool PRECISE = false>
 struct StateShape {
     static constexpr int NM = 8 - NW;
@@ -777,17 +778,23 @@ struct StateShape {
     static constexpr int PART_ROWS = kC / NV;
     static constexpr int SLAB_ROWS = PART_ROWS + 3;
     static constexpr int SLAB_PIECES = (SLAB_ROWS * SLAB_ROW + 1023) / 1024;
-    static constexpr int SLAB = SLAB_PIECES * 1024;          // one part's slab region
-    static_assert(SLAB_PIECES == 3, "three slab pieces per V wave");
+    // one part's slab region: the bytes copied (the last piece's lanes past
+    // them are inactive and write nothing)
+    static constexpr int SLAB = SLAB_ROWS * SLAB_ROW;
+    static_assert(SLAB_PIECES == 3 && SLAB % 16 == 0, "three slab pieces per V wave");
+    // chunk buffers: three (records requested two chunks ahead) where they
+    // fit in LDS, else two
+    static constexpr int NB = NW == 2 && !PRECISE ? 3 : 2;
+    static_assert(NB * BUF + 2 * NV * SLAB + 16 * N <= 160 * 1024, "state kernel LDS");
     static constexpr bool is_v(int m) { return NW == 4 || m >= 4; }
     static constexpr int v_part(int m) { return NW == 4 ? m : m - 4; }
-    // record pieces: NW = 2: 10, 10, 10, 8 for m 0..3 and 4, 4 for the V
-    // waves; NW = 4: 12, 12, 11, 11 (precise: 13, 13, 13, 11, 4, 4 and 15,
-    // 15, 14, 14)
+    // record pieces: NW = 2: 12, 12, 11, 11 for the copy waves m 0..3 and
+    // none for the V waves; NW = 4: 12, 12, 11, 11 (precise: 15, 15, 14, 14
+    // in both shapes)
     static constexpr int rec_lo(int m) {
-        if constexpr (PRECISE)
-            return NW == 4 ? (m < 2 ? 15 * m : 30 + 14 * (m - 2)) : (m < 3 ? 13 * m : m == 3 ? 39 : 50 + 4 * (m - 4));
-        return NW == 4 ? (m < 2 ? 12 * m : 24 + 11 * (m - 2)) : (m < 3 ? 10 * m : m == 3 ? 30 : 38 + 4 * (m - 4));
+        if (m >= 4) return PIECES;
+        if constexpr (PRECISE) return m < 2 ? 15 * m : 30 + 14 * (m - 2);
+        return m < 2 ? 12 * m : 24 + 11 * (m - 2);
     }
     static constexpr int rec_hi(int m) { return m + 1 == NM ? PIECES : rec_lo(m + 1); }
 };
@@ -946,6 +953,103 @@ __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& 
 // each LDS buffer and slab region is a distinct object: the compiler then
 // orders reads of one only after its own copies.  Chunk c's buffer is
 // buf[c % 2] and its raw slab slab[c % 2].
+// NW = 2: memory wave M's step c, run while the compute waves work on chunk
+// c - 1 (c = 0: before the first chunk).  It completes chunk c's buffer
+// vbuf.  A copy wave requests its pieces of chunk c + NB - 2 into rbuf and
+// waits for those of chunk c.  A V wave waits for chunk c's slab (in `slab`,
+// requested two steps earlier), runs the front end into vbuf, then requests
+// chunk c + 2's slab into the same region, which stays in flight across the
+// barrier that follows.
+template <int NW, int M, bool PRECISE>
+__device__ __forceinline__ void mem_step2(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* rbuf,
+                                          char* vbuf, char* slab, int c, int lane) {
+    using SS = StateShape<NW, PRECISE>;
+    constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M), AHEAD = SS::NB - 2;
+    if constexpr (!SS::is_v(M)) {
+        const int cr = c + AHEAD;
+        if (cr < sp.nseg) {
+            const char* krec = key_rec(sp, cx.rb, cx.kh, cr);
+            const char* vrec = val_rec(sp, cx.rb, cx.h, cr);
+#pragma unroll
+            for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(rbuf, krec, vrec, pc, lane);
+            if constexpr (AHEAD > 0) {
+                wait_vm<HI - LO, true>();   // chunk c's pieces, requested one step earlier, have landed
+                return;
+            }
+        }
+        wait_vm<0, true>();
+    } else {
+        if (c < sp.nseg) {
+            constexpr int part = SS::v_part(M);
+            // outstanding: the slabs of chunks c and (if any) c + 1, in issue order
+            if (c + 1 < sp.nseg)
+                wait_vm<SS::SLAB_PIECES>();
+            else
+                wait_vm<0>();
+            const int64_t local0 = (sp.k0 + c) * kC - sp.p.start_pos;
+            if (local0 >= 3 && local0 + kC <= sp.p.seq_len)
+                v_front<NW, true, PRECISE>(sp.p, cx, Wv, slab, vbuf, local0, part, lane);
+            else
+                v_front<NW, false, PRECISE>(sp.p, cx, Wv, slab, vbuf, local0, part, lane);
+            if (c + 2 < sp.nseg) {
+                // the front end's reads of this region have returned
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int pc = 0; pc < SS::SLAB_PIECES; ++pc)
+                    issue_slab<NW>(sp.p, cx, slab, local0 + 2 * kC, part, pc, lane);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the V^T writes are done
+    }
+}
+
+// NW = 2: memory wave M over the whole segment, with the compute waves'
+// barriers (two in the prologue, one per chunk).  Chunk c's buffer is
+// buf[c % NB] and a V wave's slab of chunk c is slab[c % 2]; the loop is
+// unrolled over a whole period of both so that every buffer and slab region
+// is a distinct object at each step.
+template <int NW, int M, bool PRECISE>
+__device__ __forceinline__ void mem_role2(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
+                                          char* buf1, char* buf2, char* slab0, char* slab1, int lane) {
+    using SS = StateShape<NW, PRECISE>;
+    constexpr int NB = SS::NB, LO = SS::rec_lo(M), HI = SS::rec_hi(M);
+    constexpr int PERIOD = NB == 3 ? 6 : 2;
+    char* const bufs[3] = {buf0, buf1, buf2};
+    char* const slabs[2] = {slab0, slab1};
+    if constexpr (SS::is_v(M)) {
+        const int64_t l0 = sp.k0 * kC - sp.p.start_pos;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            if (c < sp.nseg)
+#pragma unroll
+                for (int pc = 0; pc < SS::SLAB_PIECES; ++pc)
+                    issue_slab<NW>(sp.p, cx, slabs[c], l0 + c * kC, SS::v_part(M), pc, lane);
+    } else if constexpr (NB == 3) {
+        if (sp.nseg > 0) {   // chunk 0's pieces; step 0 requests chunk 1's
+            const char* krec = key_rec(sp, cx.rb, cx.kh, 0);
+            const char* vrec = val_rec(sp, cx.rb, cx.h, 0);
+#pragma unroll
+            for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(buf0, krec, vrec, pc, lane);
+        }
+    }
+    wait_vm<0>();
+    __syncthreads();
+    mem_step2<NW, M, PRECISE>(sp, cx, Wv, bufs[(NB - 2) % NB], buf0, slab0, 0, lane);
+    __syncthreads();
+    for (int c = 1; c <= sp.nseg; c += PERIOD) {
+#pragma unroll
+        for (int i = 0; i < PERIOD; ++i) {
+            if (c + i <= sp.nseg) {
+                mem_step2<NW, M, PRECISE>(sp, cx, Wv, bufs[(1 + i + NB - 2) % NB], bufs[(1 + i) % NB],
+                                          slabs[(1 + i) % 2], c + i, lane);
+                lds_barrier();
+            }
+        }
+    }
+    wait_vm<0>();
+}
+
 template <int NW, int M, bool PRECISE>
 __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
                                          char* buf1, char* slab0, char* slab1, int lane) {
@@ -995,6 +1099,7 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
     // with computed offsets measured 10% slower)
     __shared__ __attribute__((aligned(16))) char buf0[SS::BUF];
     __shared__ __attribute__((aligned(16))) char buf1[SS::BUF];
+    __shared__ __attribute__((aligned(16))) char buf2[SS::NB == 3 ? SS::BUF : 16];
     __shared__ __attribute__((aligned(16))) char slab0[SS::NV * SS::SLAB];   // raw v slabs of the V waves,
     __shared__ __attribute__((aligned(16))) char slab1[SS::NV * SS::SLAB];   // per chunk parity
     __shared__ float Wv[4 * N];                                     // conv taps of the slice's v channels
@@ -1066,8 +1171,8 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         uint16_t* obase = static_cast<uint16_t*>(p.out) + ((int64_t)cx.b * p.seq_len * p.num_v_heads + cx.h) * kD +
                           cx.zcol0 + 16 * wave + 4 * lq + (int64_t)li * p.num_v_heads * kD;
         bf16x4 Ob[4];   // O of the previous chunk, stored during the next one
-        for (int j = 0; j < sp.nseg; ++j) {
-            const char* cur = (j & 1) ? buf1 : buf0;
+        for (int j = 0, jb = 0; j < sp.nseg; ++j, jb = jb + 1 == SS::NB ? 0 : jb + 1) {
+            const char* cur = jb == 0 ? buf0 : jb == 1 ? buf1 : buf2;
             bf16x4 vv[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
@@ -1099,17 +1204,22 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         const int vo = SS::is_v(m) ? SS::v_part(m) * SS::SLAB : 0;
         char* s0 = slab0 + vo;
         char* s1 = slab1 + vo;
-        switch (m) {
-            case 0: mem_role<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 1: mem_role<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 2: mem_role<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            case 3: mem_role<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            default:
-                if constexpr (NW == 2) {
-                    if (m == 4) mem_role<NW, 4, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
-                    else mem_role<NW, 5, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane);
-                }
-                break;
+        if constexpr (NW == 2) {
+            switch (m) {
+                case 0: mem_role2<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+                case 1: mem_role2<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+                case 2: mem_role2<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+                case 3: mem_role2<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+                case 4: mem_role2<NW, 4, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+                default: mem_role2<NW, 5, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+            }
+        } else {
+            switch (m) {
+                case 0: mem_role<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+                case 1: mem_role<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+                case 2: mem_role<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+                default: mem_role<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
+            }
         }
     }
     if (sp.last_seg) {
