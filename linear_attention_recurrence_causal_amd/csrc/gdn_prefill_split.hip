@@ -1194,10 +1194,11 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         }
         if (sp.nseg > 0) store_o(p, obase, Ob, sp.k0 + sp.nseg - 1, li);
         const int64_t sb = opaque(cx.s_base);
+        const int64_t lq4 = opaque(4 * lq);   // the offsets of the state load are not kept across the loop
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p.rec_out[sb + (int64_t)(16 * t + 4 * lq + e) * kD] = S[t][e];
+            for (int e = 0; e < 4; ++e) p.rec_out[sb + (16 * t + lq4 + e) * kD] = S[t][e];
     } else {
         // each V wave's slab region: part v_part(m) of the slab arrays
         const int m = wave - NW;
