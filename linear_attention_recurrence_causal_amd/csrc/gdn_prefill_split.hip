@@ -17,11 +17,12 @@
 //         only the state-dependent products of each chunk -- K S0, Q S0, R,
 //         Delta by blocked forward substitution, the state update, O, which
 //         they store straight from registers -- while 8 - NW memory waves
-//         fill the other LDS buffer with the next chunk: its records by
-//         global_load_lds and the front end of the slice's v channels (conv +
-//         SiLU from a raw slab copied one chunk earlier; the slice's own
-//         columns, so no value-head data goes through the workspace).  K^T
-//         is read from K with the transposing LDS reads.
+//         fill the LDS buffers of the next chunks (three buffers, records
+//         requested two chunks ahead, where LDS allows; two otherwise): the
+//         records by global_load_lds and the front end of the slice's v
+//         channels (conv + SiLU from a raw slab the same wave copied ahead;
+//         the slice's own columns, so no value-head data goes through the
+//         workspace).  K^T is read from K with the transposing LDS reads.
 //
 // A workspace smaller than the whole call is used segment by segment (prep
 // then state for each run of chunks that fits); the state travels between
@@ -1075,9 +1076,6 @@ __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& 
     wait_vm<0>();
 }
 
-// Waves 0..NW-1 own 16 state columns each; waves NW..7 move data.  One
-// barrier per chunk: the chunk's products are done (its buffer may be
-// refilled) and the next chunk's buffer is filled.
 __device__ __forceinline__ const SplitParams& base_of(const SplitParams& s) { return s; }
 __device__ __forceinline__ const SplitParams& base_of(const VarlenParams& v) { return v.sp; }
 
