@@ -146,15 +146,23 @@ void decode_step_kernel(DecodeParams p) {
     // flight; the multi-token build requests it after its tokens' conv
     // (below), so that the tokens' inputs and the state are not in registers
     // together.
+    // This thread's state elements: the head's d_k x d_v slice (a uniform
+    // base) plus a 32-bit offset inside it, row i at + i NRG dv.
     const int64_t head_base = ((int64_t)b * p.num_v_heads + h) * DK * dv;
-    const int64_t s_base = head_base + col0 + cq * 4;
+    const int lane_off = col0 + cq * 4 + rg * dv;
     const int64_t state_elems = (int64_t)p.batch * p.num_v_heads * DK * dv;
     float4 S[RPT];
+    // the one-token build keeps a per-lane 64-bit base (fewer registers
+    // there); the multi-token build a uniform base and 32-bit offsets
+    const int64_t s_base = head_base + col0 + cq * 4;
+    auto elem = [&](const float* base, int i) {
+        return MAXT == 1 ? base + s_base + (int64_t)(rg + i * NRG) * dv
+                         : (base + head_base) + (lane_off + i * NRG * dv);
+    };
     auto load_state = [&] {
         if (p.rec_in) {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i)
-                S[i] = *reinterpret_cast<const float4*>(p.rec_in + s_base + (int64_t)(rg + i * NRG) * dv);
+            for (int i = 0; i < RPT; ++i) S[i] = *reinterpret_cast<const float4*>(elem(p.rec_in, i));
         } else {
 #pragma unroll
             for (int i = 0; i < RPT; ++i) S[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -305,18 +313,16 @@ void decode_step_kernel(DecodeParams p) {
             // snapshot t through a buffer resource: a uniform base and one
             // 32-bit offset per lane, rather than a 64-bit address per row
             const __amdgpu_buffer_rsrc_t rs = snap_rsrc(rec_snap + t * state_elems + head_base, DK * dv * 4);
-            const int32_t off0 = (int32_t)((s_base - head_base + (int64_t)rg * dv) * 4);
 #pragma unroll
             for (int i = 0; i < RPT; ++i)
                 __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4u32*>(&S[i]), rs,
-                                                       off0 + i * NRG * dv * 4, 0, 0);
+                                                       (lane_off + i * NRG * dv) * 4, 0, 0);
         }
     }
 
     // ---- 7. the state, once
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<float4*>(p.rec_out + s_base + (int64_t)(rg + i * NRG) * dv) = S[i];
+    for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(const_cast<float*>(elem(p.rec_out, i))) = S[i];
 }
 
 // 128-column workgroups (the gated step's, and GDN_DECODE_COLS=128) take 512
