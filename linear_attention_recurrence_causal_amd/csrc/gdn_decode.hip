@@ -49,6 +49,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t snap_rsrc(const float* base, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
 }
 
+// A wave-uniform 64-bit value in scalar registers (the compiler forms some
+// 64-bit products of uniform values on the vector unit, one copy per lane)
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // MAXT: tokens per call the kernel is built for (1: the one-token step,
 // whose 64-column split fits seven waves per SIMD; kMaxDecodeTokens: the
 // multi-token step, four waves per SIMD).  Every token's conv, norms and
@@ -148,7 +156,7 @@ void decode_step_kernel(DecodeParams p) {
     // together.
     // This thread's state elements: the head's d_k x d_v slice (a uniform
     // base) plus a 32-bit offset inside it, row i at + i NRG dv.
-    const int64_t head_base = ((int64_t)b * p.num_v_heads + h) * DK * dv;
+    const int64_t head_base = uniform64(((int64_t)b * p.num_v_heads + h) * DK * dv);
     const int lane_off = col0 + cq * 4 + rg * dv;
     const int64_t state_elems = (int64_t)p.batch * p.num_v_heads * DK * dv;
     float4 S[RPT];
