@@ -135,7 +135,7 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     t = time_events(lambda: step(ws), args.steps, args.warmup)
     t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
-    # the precise mode (bf16 hi + lo on every state-path product), both paths
+    # the precise mode (bf16 hi + lo on the solve's and P Delta's products), both paths
     cfg_p = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads,
                        precision=gdn.GDN_PRECISION_HILO)
     ws_p = torch.empty(gdn.prefill_workspace_bytes(cfg_p, w.seq_len), dtype=torch.uint8, device="cuda")
@@ -543,8 +543,8 @@ def main():
                            "frac": flops / t_fused / BF16_PEAK_FLOPS,
                            "traffic": profiled_traffic("prefill_kernel_qwen36-27b_prefill_16k.md",
                                                        FUSED_SOURCES)},
-            "precise_mode": {"what": "gdn_config.precision = GDN_PRECISION_HILO (bf16 hi + lo on every "
-                                     "state-path product) on the same prefill",
+            "precise_mode": {"what": "gdn_config.precision = GDN_PRECISION_HILO (bf16 hi + lo on the "
+                                     "triangular solve's and P Delta's products) on the same prefill",
                              "two_pass_ms_per_call": t_p * 1e3, "two_pass_vs_default": t_p / t,
                              "fused_ms_per_call": t_pf * 1e3, "fused_vs_default": t_pf / t_fused},
         })

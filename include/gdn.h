@@ -87,11 +87,13 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *     takes Delta as bf16 hi + lo; the other state-path operands (S0 in K S0
  *     and Q S0, the triangular solve's coupling and diagonal blocks, P and
  *     Delta in P Delta) are single bf16.
- *   GDN_PRECISION_HILO: every one of those operands as bf16 hi + lo (about
- *     16 significant bits; three MFMAs per product), for inputs where the
+ *   GDN_PRECISION_HILO: the triangular solve's coupling and diagonal
+ *     blocks and P and Delta in P Delta as bf16 hi + lo (about 16
+ *     significant bits; three MFMAs per product), for inputs where the
  *     triangular solve cancels heavily (keys that nearly coincide, beta near
- *     1, slow decay).  About 1.7x the state-path MFMA work, and 12.75 KiB
- *     more workspace per value head and chunk.
+ *     1, slow decay); S0 stays single bf16, as in the default, which measured
+ *     no worse on those inputs.  About 1.4x the state-path MFMA work, and
+ *     12.75 KiB more workspace per value head and chunk.
  * The solve is the stable direct one of the Qwen3.6-27B PR ("Known
  * limitations and follow-ups") in both. */
 typedef enum { GDN_PRECISION_DEFAULT = 0, GDN_PRECISION_HILO = 1 } gdn_precision;

@@ -79,14 +79,6 @@ __device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     lo = __builtin_convertvector(x - back, bf16x4);
 }
 
-__device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
-    hi = to_bf16x8(a, b);
-    const f32x8 back = to_f32x8(hi);
-    const f32x4 la = {a[0] - back[0], a[1] - back[1], a[2] - back[2], a[3] - back[3]};
-    const f32x4 lb = {b[0] - back[4], b[1] - back[5], b[2] - back[6], b[3] - back[7]};
-    lo = to_bf16x8(la, lb);
-}
-
 // Column order inside Q, K (d_k columns) and K^T, P, AN (token columns).  An
 // index x = 32a + 16h + 4q + e is stored at 32a + 8q + 4h + e, so the eight
 // reduction slots that lane group q of v_mfma_f32_16x16x32_bf16 needs for

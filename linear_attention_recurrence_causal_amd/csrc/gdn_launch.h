@@ -52,7 +52,7 @@ struct PrefillParams {
     int32_t batch, num_k_heads, num_v_heads;
     float q_scale, l2_eps;
     int32_t diag_neumann;   // two-pass path: diagonal-block inverses by the Neumann product
-    int32_t precise;        // bf16 hi + lo operands on every state-path product (GDN_PRECISION_HILO)
+    int32_t precise;        // bf16 hi + lo operands on the solve's and P Delta's products (GDN_PRECISION_HILO)
 };
 
 // Output gate: rows = tokens x H_v rows of d_v elements.

@@ -298,19 +298,20 @@ __device__ __forceinline__ void phase_state(SM& sm, int buf, f32x4 S[8], f32x4 Q
     }
 }
 
-// ---- B1 of the precise mode: the same products with S0, Q S0 and K S0,
-// the substitution (delta_substitution_hl) and Delta on bf16 hi + lo
-// operands (three MFMAs per product, the lo x lo term dropped).  Returns
-// Delta's hi and lo parts for B2.
+// ---- B1 of the precise mode: the same products with the substitution
+// (delta_substitution_hl) and Delta on bf16 hi + lo operands (three MFMAs
+// per product, the lo x lo term dropped); Q S0 and K S0 take S0 rounded once
+// to bf16, as in the default precision.  Returns Delta's hi and lo parts for
+// B2.
 template <class SM>
 __device__ __forceinline__ void phase_state_hl(SM& sm, int buf, f32x4 S[8], f32x4 QS[4], bf16x8 BD[2],
                                                bf16x8 BDl[2], int wave, int li, int lq) {
     const int cw = 16 * wave + li;
     const __bf16* Ks = sm.Ks[buf];
     const __bf16* Qs = sm.Qs[buf];
-    bf16x8 Bh[4], Bl[4];
+    bf16x8 Bh[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) split_bf16x8(S[2 * ks], S[2 * ks + 1], Bh[ks], Bl[ks]);
+    for (int ks = 0; ks < 4; ++ks) Bh[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
     f32x4 KS[4];
 #pragma unroll
     for (int mh = 0; mh < 4; mh += 2) {
@@ -331,8 +332,6 @@ __device__ __forceinline__ void phase_state_hl(SM& sm, int buf, f32x4 S[8], f32x
             for (int ks = 0; ks < 4; ++ks) {
                 k = mfma16(ak[mm][ks], Bh[ks], k);
                 q = mfma16(aq[mm][ks], Bh[ks], q);
-                k = mfma16(ak[mm][ks], Bl[ks], k);
-                q = mfma16(aq[mm][ks], Bl[ks], q);
             }
             KS[mh + mm] = k;
             QS[mh + mm] = q;

@@ -616,18 +616,18 @@ __device__ __forceinline__ void chunk_products(const char* buf, f32x4 S[8], cons
         for (int t = 0; t < 8; ++t) S[t] = mfma16(akt[t][st / 2], (st % 2 ? BL : BH)[st / 2], S[t]);
 }
 
-// The precise mode's chunk (bf16 hi + lo on every state-path operand): K S0
-// and (Q S0)^T with S0 as hi + lo, the substitution with the coupling and
-// diagonal products on hi + lo (delta_substitution_hl), O's P Delta on hi +
-// lo, and the state update as in chunk_products.  About 1.7x the MFMAs of
-// the default; the operands are loaded in smaller batches (fewer registers,
-// more exposed LDS latency).
+// The precise mode's chunk: the substitution with the coupling and diagonal
+// products on bf16 hi + lo (delta_substitution_hl), O's P Delta on hi + lo,
+// and the state update as in chunk_products; K S0 and (Q S0)^T take S0
+// rounded once to bf16, as in the default precision.  About 1.4x the MFMAs
+// of the default; the operands are loaded in smaller batches (fewer
+// registers, more exposed LDS latency).
 template <class StorePrev>
 __device__ __forceinline__ void chunk_products_hl(const char* buf, f32x4 S[8], const bf16x4 vv[4], bf16x4 Ob[4],
                                                   int li, int lq, StorePrev&& store_prev) {
-    bf16x8 Bh[4], Bl[4];
+    bf16x8 Bh[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) split_bf16x8(S[2 * ks], S[2 * ks + 1], Bh[ks], Bl[ks]);
+    for (int ks = 0; ks < 4; ++ks) Bh[ks] = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
     // K S0 in two halves of row tiles
     f32x4 KS[4];
 #pragma unroll
@@ -644,7 +644,6 @@ __device__ __forceinline__ void chunk_products_hl(const char* buf, f32x4 S[8], c
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 acc = mfma16(ak[mm][ks], Bh[ks], acc);
-                acc = mfma16(ak[mm][ks], Bl[ks], acc);
             }
             KS[mh + mm] = acc;
         }
@@ -695,7 +694,6 @@ __device__ __forceinline__ void chunk_products_hl(const char* buf, f32x4 S[8], c
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 acc = mfma16(Bh[k], aq[mm][k], acc);
-                acc = mfma16(Bl[k], aq[mm][k], acc);
             }
             QT[mh + mm] = acc;
         }
