@@ -762,8 +762,7 @@ __device__ __forceinline__ int64_t state_channel(const PrefillParams& p, const S
 // without a compute wave, which copy none) run the front end of the slice's
 // v channels, part v_part(m) of the chunk's rows, one 4-channel x 4-row item
 // per lane, from a raw slab of exactly those rows (+ 3 rows of conv history)
-// that the same wave copied into its own slab region one chunk (NW = 4) or
-// two chunks (NW = 2) earlier.
+// that the same wave copied into its own slab region two chunks earlier.
 template <int NW, bool PRECISE = false>
 struct StateShape {
     static constexpr int NM = 8 - NW;
@@ -895,8 +894,9 @@ __device__ __forceinline__ void checkpoint(const PrefillParams& p, const StateCt
 // operation.
 template <int n, bool LGKM = false>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(n >= 0 && n < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((LGKM ? 0x0070 : 0x0f70) | n);   // expcnt: no wait
+    static_assert(n >= 0 && n < 64, "vmcnt field");
+    // vmcnt bits 3:0 and 15:14; expcnt: no wait
+    __builtin_amdgcn_s_waitcnt((LGKM ? 0x0070 : 0x0f70) | (n & 15) | ((n >> 4) << 14));
 }
 
 // Workgroup barrier without the memory fences of __syncthreads: each wave
@@ -910,57 +910,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Memory wave M's share of filling buf with chunk jn: its record pieces; for
-// a V wave then the v front end from slab_cur (this wave's raw slab of chunk
-// jn, copied in the previous step) and the copy of chunk jn + 1's slab into
-// slab_next, which may stay in flight across the barrier that follows.
+// Memory wave M's step c, run while the compute waves work on chunk c - 1
+// (c = 0: before the first chunk).  It completes chunk c's buffer vbuf.  A
+// copy wave requests its pieces of chunk c + NB - 2 into rbuf and waits for
+// those of chunk c.  A V wave requests its pieces of chunk c, if it copies
+// any (NW = 4), waits for chunk c's slab (in `slab`, requested two steps
+// earlier), runs the front end into vbuf, then requests chunk c + 2's slab
+// into the same region, which stays in flight across the barrier that
+// follows.
 template <int NW, int M, bool PRECISE>
-__device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf,
-                                         const char* slab_cur, char* slab_next, int jn, int lane) {
-    using SS = StateShape<NW, PRECISE>;
-    constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M);
-    if (jn >= sp.nseg) {
-        wait_vm<0, true>();
-        return;
-    }
-    const char* krec = key_rec(sp, cx.rb, cx.kh, jn);
-    const char* vrec = val_rec(sp, cx.rb, cx.h, jn);
-#pragma unroll
-    for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(buf, krec, vrec, pc, lane);
-    if constexpr (SS::is_v(M)) {
-        constexpr int part = SS::v_part(M);
-        wait_vm<HI - LO>();   // the slab copies issued before these pieces have landed
-        const int64_t local0 = (sp.k0 + jn) * kC - sp.p.start_pos;
-        if (local0 >= 3 && local0 + kC <= sp.p.seq_len)
-            v_front<NW, true, PRECISE>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
-        else
-            v_front<NW, false, PRECISE>(sp.p, cx, Wv, slab_cur, buf, local0, part, lane);
-        if (jn + 1 < sp.nseg) {
-#pragma unroll
-            for (int pc = 0; pc < SS::SLAB_PIECES; ++pc) issue_slab<NW>(sp.p, cx, slab_next, local0 + kC, part, pc, lane);
-            wait_vm<SS::SLAB_PIECES, true>();
-        } else {
-            wait_vm<0, true>();
-        }
-    } else {
-        wait_vm<0, true>();
-    }
-}
-
-// Memory wave M over the whole segment: the same barriers as the compute
-// waves (two in the prologue, one per chunk).  Two chunks per trip so that
-// each LDS buffer and slab region is a distinct object: the compiler then
-// orders reads of one only after its own copies.  Chunk c's buffer is
-// buf[c % 2] and its raw slab slab[c % 2].
-// NW = 2: memory wave M's step c, run while the compute waves work on chunk
-// c - 1 (c = 0: before the first chunk).  It completes chunk c's buffer
-// vbuf.  A copy wave requests its pieces of chunk c + NB - 2 into rbuf and
-// waits for those of chunk c.  A V wave waits for chunk c's slab (in `slab`,
-// requested two steps earlier), runs the front end into vbuf, then requests
-// chunk c + 2's slab into the same region, which stays in flight across the
-// barrier that follows.
-template <int NW, int M, bool PRECISE>
-__device__ __forceinline__ void mem_step2(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* rbuf,
+__device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* rbuf,
                                           char* vbuf, char* slab, int c, int lane) {
     using SS = StateShape<NW, PRECISE>;
     constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M), AHEAD = SS::NB - 2;
@@ -978,13 +937,22 @@ __device__ __forceinline__ void mem_step2(const SplitParams& sp, const StateCtx&
         }
         wait_vm<0, true>();
     } else {
+        constexpr int P = HI - LO;   // record pieces a V wave copies (NW = 4; none at NW = 2)
+        static_assert(P == 0 || AHEAD == 0, "V waves copy pieces only with two buffers");
         if (c < sp.nseg) {
             constexpr int part = SS::v_part(M);
-            // outstanding: the slabs of chunks c and (if any) c + 1, in issue order
+            if constexpr (P > 0) {
+                const char* krec = key_rec(sp, cx.rb, cx.kh, c);
+                const char* vrec = val_rec(sp, cx.rb, cx.h, c);
+#pragma unroll
+                for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(rbuf, krec, vrec, pc, lane);
+            }
+            // outstanding, in issue order: the slabs of chunks c and (if any)
+            // c + 1, then this step's pieces
             if (c + 1 < sp.nseg)
-                wait_vm<SS::SLAB_PIECES>();
+                wait_vm<SS::SLAB_PIECES + P>();
             else
-                wait_vm<0>();
+                wait_vm<P>();
             const int64_t local0 = (sp.k0 + c) * kC - sp.p.start_pos;
             if (local0 >= 3 && local0 + kC <= sp.p.seq_len)
                 v_front<NW, true, PRECISE>(sp.p, cx, Wv, slab, vbuf, local0, part, lane);
@@ -998,18 +966,25 @@ __device__ __forceinline__ void mem_step2(const SplitParams& sp, const StateCtx&
                 for (int pc = 0; pc < SS::SLAB_PIECES; ++pc)
                     issue_slab<NW>(sp.p, cx, slab, local0 + 2 * kC, part, pc, lane);
             }
+            // this step's pieces have landed (chunk c + 2's slab may not have)
+            if constexpr (P > 0) {
+                if (c + 2 < sp.nseg)
+                    wait_vm<SS::SLAB_PIECES>();
+                else
+                    wait_vm<0>();
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the V^T writes are done
     }
 }
 
-// NW = 2: memory wave M over the whole segment, with the compute waves'
-// barriers (two in the prologue, one per chunk).  Chunk c's buffer is
+// Memory wave M over the whole segment, with the compute waves' barriers
+// (two in the prologue, one per chunk).  Chunk c's buffer is
 // buf[c % NB] and a V wave's slab of chunk c is slab[c % 2]; the loop is
 // unrolled over a whole period of both so that every buffer and slab region
 // is a distinct object at each step.
 template <int NW, int M, bool PRECISE>
-__device__ __forceinline__ void mem_role2(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
+__device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
                                           char* buf1, char* buf2, char* slab0, char* slab1, int lane) {
     using SS = StateShape<NW, PRECISE>;
     constexpr int NB = SS::NB, LO = SS::rec_lo(M), HI = SS::rec_hi(M);
@@ -1034,41 +1009,16 @@ __device__ __forceinline__ void mem_role2(const SplitParams& sp, const StateCtx&
     }
     wait_vm<0>();
     __syncthreads();
-    mem_step2<NW, M, PRECISE>(sp, cx, Wv, bufs[(NB - 2) % NB], buf0, slab0, 0, lane);
+    mem_step<NW, M, PRECISE>(sp, cx, Wv, bufs[(NB - 2) % NB], buf0, slab0, 0, lane);
     __syncthreads();
     for (int c = 1; c <= sp.nseg; c += PERIOD) {
 #pragma unroll
         for (int i = 0; i < PERIOD; ++i) {
             if (c + i <= sp.nseg) {
-                mem_step2<NW, M, PRECISE>(sp, cx, Wv, bufs[(1 + i + NB - 2) % NB], bufs[(1 + i) % NB],
+                mem_step<NW, M, PRECISE>(sp, cx, Wv, bufs[(1 + i + NB - 2) % NB], bufs[(1 + i) % NB],
                                           slabs[(1 + i) % 2], c + i, lane);
                 lds_barrier();
             }
-        }
-    }
-    wait_vm<0>();
-}
-
-template <int NW, int M, bool PRECISE>
-__device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* buf0,
-                                         char* buf1, char* slab0, char* slab1, int lane) {
-    using SS = StateShape<NW, PRECISE>;
-    if constexpr (SS::is_v(M)) {
-        if (sp.nseg > 0)
-#pragma unroll
-            for (int pc = 0; pc < SS::SLAB_PIECES; ++pc)
-                issue_slab<NW>(sp.p, cx, slab0, sp.k0 * kC - sp.p.start_pos, SS::v_part(M), pc, lane);
-    }
-    wait_vm<0>();
-    __syncthreads();
-    mem_step<NW, M, PRECISE>(sp, cx, Wv, buf0, slab0, slab1, 0, lane);
-    __syncthreads();
-    for (int j = 0; j < sp.nseg; j += 2) {
-        mem_step<NW, M, PRECISE>(sp, cx, Wv, buf1, slab1, slab0, j + 1, lane);
-        lds_barrier();
-        if (j + 1 < sp.nseg) {
-            mem_step<NW, M, PRECISE>(sp, cx, Wv, buf0, slab0, slab1, j + 2, lane);
-            lds_barrier();
         }
     }
     wait_vm<0>();
@@ -1201,22 +1151,17 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         const int vo = SS::is_v(m) ? SS::v_part(m) * SS::SLAB : 0;
         char* s0 = slab0 + vo;
         char* s1 = slab1 + vo;
-        if constexpr (NW == 2) {
-            switch (m) {
-                case 0: mem_role2<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-                case 1: mem_role2<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-                case 2: mem_role2<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-                case 3: mem_role2<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-                case 4: mem_role2<NW, 4, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-                default: mem_role2<NW, 5, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
-            }
-        } else {
-            switch (m) {
-                case 0: mem_role<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-                case 1: mem_role<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-                case 2: mem_role<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-                default: mem_role<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, s0, s1, lane); break;
-            }
+        switch (m) {
+            case 0: mem_role<NW, 0, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+            case 1: mem_role<NW, 1, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+            case 2: mem_role<NW, 2, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+            case 3: mem_role<NW, 3, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane); break;
+            default:
+                if constexpr (NW == 2) {
+                    if (m == 4) mem_role<NW, 4, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane);
+                    else mem_role<NW, 5, PRECISE>(sp, cx, Wv, buf0, buf1, buf2, s0, s1, lane);
+                }
+                break;
         }
     }
     if (sp.last_seg) {
