@@ -112,10 +112,11 @@ def time_events(fn, steps, warmup):
 
 
 def bench_prefill(args):
-    """The prefill call as a user makes it for this shape: with a workspace
-    (allocated once, outside the timed region), which selects the two-pass
-    path.  The fused single-pass kernel (no workspace) is timed beside it for
-    reference."""
+    """The prefill call as a serving loop makes it for this shape: on a stream
+    of its own, with a workspace (allocated once, outside the timed region),
+    which selects the two-pass path with the tail of the prep overlapped with
+    the state kernel.  Beside it: the same call on the NULL stream (the serial
+    two-pass path) and the fused single-pass kernel (no workspace)."""
     import torch
     from linear_attention_recurrence_causal_amd import gdn, inputs as I
     w = I.WORKLOADS[2]
@@ -132,8 +133,12 @@ def bench_prefill(args):
                             None, None, out=out, conv_state_out=conv, rec_state_out=S,
                             workspace=workspace)
 
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    t = time_events(lambda: step(ws), args.steps, args.warmup)
+    with torch.cuda.stream(side):
+        t = time_events(lambda: step(ws), args.steps, args.warmup)
+    t_null = time_events(lambda: step(ws), max(2, args.steps // 2), 2)
     t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
     # the precise mode (bf16 hi + lo on the solve's and P Delta's products), both paths
     cfg_p = gdn.Config(batch=w.batch, num_k_heads=w.num_k_heads, num_v_heads=w.num_v_heads,
@@ -144,13 +149,15 @@ def bench_prefill(args):
         gdn.prefill_chunked(cfg_p, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"],
                             None, None, out=out, conv_state_out=conv, rec_state_out=S, workspace=workspace)
 
-    t_p = time_events(lambda: step_p(ws_p), max(2, args.steps // 2), 5)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        t_p = time_events(lambda: step_p(ws_p), max(2, args.steps // 2), 5)
     t_pf = time_events(lambda: step_p(None), 2, 1)
     del ws_p
     tokens = w.batch * w.seq_len
     flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
     byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads)
-    return w, t, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws.numel()
+    return w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws.numel()
 
 
 def bench_decode(args):
@@ -355,6 +362,10 @@ def bench_varlen(args):
             "single_calls_us": t1 * 1e6, "speedup_vs_single_calls": t1 / t}
 
 
+OVERLAPPED = ("two-pass prefill, overlapped: prep_kernel (head chunks), then state_kernel<2> beside "
+              "prep_kernel_tail (the other chunks) on disjoint CUs (one call)")
+
+
 def prefill_roofline(kernel, flops, t, byts, profile):
     return {"kernel": kernel, "bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_FLOPS / 1e12,
             "unit": "TFLOP/s", "frac": flops / t / BF16_PEAK_FLOPS,
@@ -443,19 +454,21 @@ def bench_long(args):
     conv = torch.empty(w.batch, w.conv_dim, 3, dtype=torch.bfloat16, device="cuda")
     S = torch.empty(w.batch, w.num_v_heads, 128, 128, device="cuda")
     ws = torch.empty(gdn.prefill_workspace_bytes(cfg, w.seq_len), dtype=torch.uint8, device="cuda")
-    t = time_events(lambda: gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"],
-                                                d["dt_bias"], None, None, ckpt_interval=w.ckpt_interval,
-                                                ckpt_buf=ck, out=out, conv_state_out=conv, rec_state_out=S,
-                                                workspace=ws),
-                    max(2, args.steps // 4), 2)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        t = time_events(lambda: gdn.prefill_chunked(cfg, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"],
+                                                    d["dt_bias"], None, None, ckpt_interval=w.ckpt_interval,
+                                                    ckpt_buf=ck, out=out, conv_state_out=conv, rec_state_out=S,
+                                                    workspace=ws),
+                        max(2, args.steps // 4), 2)
     tokens = w.batch * w.seq_len
     flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
     byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads) + len(ents) * (nb // len(ents))
     return {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill of 262,144 tokens (B=1, 16/48 heads) "
                         "with a checkpoint slot every 4096 tokens (64 slots)",
             "ms_per_call": t * 1e3, "tokens_per_s": tokens / t, "checkpoint_slots": len(ents),
-            "roofline": prefill_roofline("two-pass prefill: prep_kernel + state_kernel<2> (one call)", flops, t,
-                                         byts, "prefill_two_pass_qwen36-27b_prefill_256k.md")}
+            "roofline": prefill_roofline(OVERLAPPED, flops, t, byts, "prefill_two_pass_qwen36-27b_prefill_256k.md")}
 
 
 def cpu_baseline(inp, tokens):
@@ -520,7 +533,7 @@ def main():
     inp = None
     if "prefill" in sections:
         print("bench: prefill", file=sys.stderr, flush=True)
-        w, t, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
+        w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
         achieved = flops / t
         rec.update({
             "value": tokens / t,
@@ -529,7 +542,8 @@ def main():
                        "seq_len": w.seq_len, "num_k_heads": w.num_k_heads,
                        "num_v_heads": w.num_v_heads, "head_dim": 128, "chunk": 64,
                        "io": "bf16", "state": "fp32", "parallelism": "none (1 GPU)"},
-            "roofline": {"kernel": "two-pass prefill: prep_kernel + state_kernel<2> (one call)",
+            "stream": "a created (non-NULL) stream, as a serving loop runs",
+            "roofline": {"kernel": OVERLAPPED,
                          "bound": "mfma", "achieved": achieved / 1e12,
                          "peak": BF16_PEAK_FLOPS / 1e12, "unit": "TFLOP/s",
                          "frac": achieved / BF16_PEAK_FLOPS,
@@ -538,6 +552,10 @@ def main():
                          "flops_per_launch": flops, "hbm_floor_bytes_per_launch": byts,
                          "hbm_floor_frac": byts / t / HBM_PEAK_BYTES,
                          "workspace_bytes": ws_bytes},
+            "null_stream": {"what": "the same call on the NULL stream, where the prep runs before the state "
+                                    "kernel (serial two-pass path)",
+                            "ms_per_call": t_null * 1e3, "tokens_per_s": tokens / t_null,
+                            "frac": flops / t_null / BF16_PEAK_FLOPS},
             "fused_path": {"kernel": "prefill_kernel<8>", "ms_per_call": t_fused * 1e3,
                            "tokens_per_s": tokens / t_fused,
                            "frac": flops / t_fused / BF16_PEAK_FLOPS,

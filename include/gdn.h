@@ -146,7 +146,9 @@ gdn_status gdn_state_checkpoint(const gdn_config* cfg, int64_t start_pos, int64_
 
 /* Workspace for the two-pass prefill (host only): the bytes with which a call
  * of seq_len tokens per sequence (any start_pos) runs each pass once,
- *   B * (chunks the call can span) * (H_k * 32768 + H_v * 13568).
+ *   B * n * (H_k * 32768 + H_v * 13568)  (n: chunks the call can span)
+ * plus, from n = 2 on, 8 * (B * H_k * roundup(n, 32) + 1024) for the ready
+ * flags of the overlapped prep (see gdn_prefill_chunked).
  * The chunked form splits into per-chunk work that does not depend on the
  * state and a short recurrence over chunks that does ("Performance note");
  * with a workspace the first part runs for every chunk in parallel and only
@@ -188,7 +190,18 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
  * follow-ups").  On the two-pass path the environment variable
  * GDN_DIAG_SOLVE=neumann selects the product form of the Neumann series
  * instead (the faster-style variant the same passage names), read at each
- * call; it is less accurate where keys nearly coincide. */
+ * call; it is less accurate where keys nearly coincide.
+ * Overlapped prep: with the whole call in one segment plus the flag bytes
+ * above, a state kernel of 16-column waves on at most 24 workgroups per XCD,
+ * B * H_k a multiple of 8, 64 chunks or more, a GPU of 8 XCDs x 32 CUs, and
+ * a created stream (not the NULL, legacy or per-thread stream, not being
+ * captured), the call runs the prep of its later chunks concurrently with
+ * the state kernel, on two library-owned streams of the device with disjoint
+ * CU masks (24 and 8 CUs of every XCD), forked from `stream` at the call and
+ * joined back into it at the end; the results are bit for bit those of the
+ * serial path.  The library streams are blocking streams: work the caller
+ * puts on the NULL stream meanwhile waits for them.  GDN_PREFILL_OVERLAP=0
+ * turns this off, =1 takes it from 2 chunks on. */
 gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
                                const void* qkv, const void* a, const void* b, const void* conv_w,
                                const float* A_log, const float* dt_bias,

@@ -168,16 +168,19 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
     // floor((seq_len + chunk - 2) / chunk) + 1 chunks
     const int64_t chunks = seq_len == 0 ? 0 : (seq_len + cfg->chunk - 2) / cfg->chunk + 1;
     *bytes = (uint64_t)chunks * gdn::prefill_split_chunk_bytes(cfg->batch, cfg->num_k_heads, cfg->num_v_heads, cfg->precision == GDN_PRECISION_HILO);
+    // and, from two chunks on, the ready flags of the overlapped prep
+    if (chunks >= 2) *bytes += gdn::prefill_overlap_bytes(cfg->batch, cfg->num_k_heads, chunks);
     return GDN_OK;
 }
 
-gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
-                               const void* qkv, const void* a, const void* b, const void* conv_w,
-                               const float* A_log, const float* dt_bias,
-                               const void* conv_state_in, void* conv_state_out,
-                               const float* rec_state_in, float* rec_state_out, void* out,
-                               void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
-                               void* workspace, uint64_t workspace_bytes, void* stream) {
+static gdn_status prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                                  const void* qkv, const void* a, const void* b, const void* conv_w,
+                                  const float* A_log, const float* dt_bias,
+                                  const void* conv_state_in, void* conv_state_out,
+                                  const float* rec_state_in, float* rec_state_out, void* out,
+                                  void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                                  void* workspace, uint64_t workspace_bytes, void* stream,
+                                  bool allow_overlap) {
     if (gdn_status s = check_config(cfg)) return s;
     if (seq_len < 0 || start_pos < 0 || ckpt_interval < 0) return GDN_EINVAL;
     if (ckpt_interval > 0 && ckpt_interval % cfg->chunk != 0) return GDN_EINVAL;
@@ -239,7 +242,8 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
         // only the part a call can use is checked against the other buffers
         const int64_t k_first = start_pos / cfg->chunk;
         const int64_t chunks = L > 0 ? (start_pos + L - 1) / cfg->chunk + 1 - k_first : 0;
-        const uint64_t need = (uint64_t)chunks * chunk_ws;
+        const uint64_t need =
+            (uint64_t)chunks * chunk_ws + (chunks >= 2 ? gdn::prefill_overlap_bytes(cfg->batch, cfg->num_k_heads, chunks) : 0);
         const Range r_ws = range_of(workspace, need < workspace_bytes ? need : workspace_bytes);
         const Range r_ck = range_of(ckpt_buf, plan.count > 0 ? plan.buffer_bytes : 0);
         if (overlap(r_ws, r_qkv) || overlap(r_ws, r_out) || overlap(r_ws, r_rout) || overlap(r_ws, r_cout) ||
@@ -276,9 +280,22 @@ gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t s
     const char* solve_env = getenv("GDN_DIAG_SOLVE");
     p.diag_neumann = solve_env && solve_env[0] == 'n';
     p.precise = cfg->precision == GDN_PRECISION_HILO;
-    const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream))
+    const hipError_t e = two_pass ? gdn::launch_prefill_split(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                                                              allow_overlap)
                                   : gdn::launch_prefill(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
+                               const void* qkv, const void* a, const void* b, const void* conv_w,
+                               const float* A_log, const float* dt_bias,
+                               const void* conv_state_in, void* conv_state_out,
+                               const float* rec_state_in, float* rec_state_out, void* out,
+                               void* ckpt_buf, uint64_t ckpt_buf_bytes, int64_t ckpt_interval,
+                               void* workspace, uint64_t workspace_bytes, void* stream)  {
+    return prefill_chunked(cfg, seq_len, start_pos, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out,
+                           rec_state_in, rec_state_out, out, ckpt_buf, ckpt_buf_bytes, ckpt_interval, workspace,
+                           workspace_bytes, stream, true);
 }
 
 gdn_status gdn_prefill_chunked_noalloc(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
@@ -294,9 +311,10 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_config* cfg, int64_t seq_len, i
         return GDN_ESPACE;
     void* ws = nullptr;
     if (gdn_status s = scratch_of(stream, &ws)) return s;
-    return gdn_prefill_chunked(cfg, seq_len, start_pos, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in,
-                               conv_state_out, rec_state_in, rec_state_out, out, ckpt_buf, ckpt_buf_bytes,
-                               ckpt_interval, ws, kNoAllocScratchBytes, stream);
+    // no overlapped prep: its streams would be created on first use
+    return prefill_chunked(cfg, seq_len, start_pos, qkv, a, b, conv_w, A_log, dt_bias, conv_state_in, conv_state_out,
+                           rec_state_in, rec_state_out, out, ckpt_buf, ckpt_buf_bytes, ckpt_interval, ws,
+                           kNoAllocScratchBytes, stream, false);
 }
 
 // Output gate arguments of a decode call (y == NULL: no gate).

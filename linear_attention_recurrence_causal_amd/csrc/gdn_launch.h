@@ -77,10 +77,16 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Two-pass path: workspace bytes per chunk of every sequence, whether the
 // head grouping is supported, and the launcher (segments of
-// ws_bytes / prefill_split_chunk_bytes chunks; at least one must fit).
+// ws_bytes / prefill_split_chunk_bytes chunks; at least one must fit).  A
+// call in one segment with prefill_overlap_bytes more (ready flags and
+// counters after the records) runs the tail of its prep concurrently with
+// the state kernel on library-owned streams where allow_overlap is set and
+// the shape, the chip and the stream (not capturing) qualify.
 uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads, bool precise);
+uint64_t prefill_overlap_bytes(int batch, int num_k_heads, int64_t chunks);
 bool prefill_split_supported(const PrefillParams& p);
-hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream);
+hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream,
+                                bool allow_overlap);
 
 // Varlen two-pass path: p.batch sequences packed along the token axis
 // (cu_seqlens[p.batch + 1], start_pos[p.batch], host arrays; p.seq_len and

@@ -29,6 +29,10 @@
 // segments through rec_state_out.  Every value the state kernel consumes is
 // bit-identical to what the fused kernel computes in LDS, so the two paths
 // agree to the last bit up to the compiler's instruction choice.
+#include <chrono>
+#include <cmath>
+#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_chunk_common.h"
@@ -95,7 +99,54 @@ struct SplitParams {
     int32_t last_seg;    // write the final conv tail
     int32_t rec_stride;  // chunk records per (sequence, head) in the workspace
     int32_t rec_batch;   // sequences with records in the workspace
+    int32_t pj;          // chunks per (sequence, key head) in a prep grid
+    // Overlapped prep (null flags: off).  The prep launch on the caller's
+    // stream covers chunks [0, n1); prep_kernel_tail publishes chunks n1..
+    // one by one, concurrently with that launch and with the state kernel,
+    // which waits for each chunk's flag.  Flags, claim counters and error
+    // words carry the call's epoch, so nothing has to be cleared between
+    // calls.
+    uint64_t* flags;     // [B H_k][frow]: the epoch once a chunk's records are complete
+    uint64_t* hdr;       // kOvlHdrWords: epoch-tagged claim counters per XCD, error words
+    uint64_t epoch;      // this call's tag, never 0
+    int32_t frow;        // flag words per row (a multiple of 32)
+    int32_t n1;
 };
+
+// ---- overlap header (64-bit word offsets; each XCD's counter on a 256-byte
+// line of its own).  A counter holds a 40-bit epoch tag and a 24-bit count.
+// An error word holds the epoch of the call that met the error: kHdrErrXcd
+// an XCD id out of range, kHdrErrClaim more state workgroups on an XCD than
+// its share of the work, kHdrErrWait a wait for a chunk that timed out.
+constexpr int kOvlHdrWords = 1024;
+constexpr int kHdrState = 0, kHdrPrep = 256, kHdrErrXcd = 512, kHdrErrClaim = 544, kHdrErrWait = 576;
+constexpr int kOvlXcds = 8;
+// persistent tail workgroups: as many as the tail stream's 64 CUs hold at
+// once (two per CU; one in the precise mode, whose prep takes the LDS of two)
+constexpr int ovl_tail_blocks(bool precise) { return precise ? 64 : 128; }
+
+// The count before this claim of an epoch-tagged counter (0 for the call's
+// first claim, whatever an earlier call left there)
+__device__ __forceinline__ uint32_t claim_next(uint64_t* ctr, uint64_t epoch) {
+    const uint64_t tag = (epoch & 0xffffffffffull) << 24;
+    uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const bool cur = (old & ~0xffffffull) == tag;
+        uint64_t seen = old;
+        if (__hip_atomic_compare_exchange_strong(ctr, &seen, cur ? old + 1 : tag + 1, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return cur ? (uint32_t)(old & 0xffffff) : 0u;
+        old = seen;
+    }
+}
+
+__device__ __forceinline__ void ovl_error(uint64_t* hdr, int word, uint64_t epoch) {
+    __hip_atomic_store(hdr + word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// XCD (accelerator complex die) of the calling wave, from the XCC_ID
+// hardware register: the workgroups that share one XCD share its L2
+__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)); }
 
 // Records of record-sequence rb (the sequence's index among those of the
 // launch), head and chunk j of the segment
@@ -272,12 +323,12 @@ __device__ __forceinline__ void zero_upper(PrepHeadBuf<PRECISE>& hb, int tid) {
 
 // Chunk j of the segment for sequence b (record-sequence rb) and key head kh
 template <bool NEUMANN, bool PRECISE>
-__device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, int kh, int j) {
+__device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, int kh, int j, int tid) {
     const PrefillParams& p = sp.p;
     using HB = PrepHeadBuf<PRECISE>;
     __shared__ PrepSmem<PRECISE> sm;
     // wave index in a scalar register: branches on it are uniform
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
     const int li = lane % 16, lq = lane / 16;
     const int Hk = p.num_k_heads, r = p.num_v_heads / Hk;
     const int64_t local0 = (sp.k0 + j) * kC - p.start_pos;
@@ -420,10 +471,54 @@ __device__ __forceinline__ void prep_body(const SplitParams& sp, int b, int rb, 
 template <bool NEUMANN, bool PRECISE>
 __global__ __launch_bounds__(kPrepThreads)
 void prep_kernel(SplitParams sp) {
-    const int j = blockIdx.x % sp.rec_stride;
-    const int grp = blockIdx.x / sp.rec_stride;
+    const int j = blockIdx.x % sp.pj;
+    const int grp = blockIdx.x / sp.pj;
     const int b = grp / sp.p.num_k_heads, kh = grp % sp.p.num_k_heads;
-    prep_body<NEUMANN, PRECISE>(sp, b, b, kh, j);
+    prep_body<NEUMANN, PRECISE>(sp, b, b, kh, j, threadIdx.x);
+}
+
+// Tail of an overlapped call: persistent workgroups, as many as the tail
+// stream's CUs hold at once (so none waits to be dispatched, and nothing
+// dispatched after them waits behind them).  A workgroup takes the next item
+// -- (group, chunk) of chunks n1.. -- of its own XCD, groups g with
+// g % 8 == XCD, chunks in order, so that the state workgroups of the group,
+// on the same XCD, read its records from the L2 they were written to.  Once
+// every record store of an item has completed, its flag is set.
+template <bool NEUMANN, bool PRECISE>
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(PRECISE ? 2 : 4, PRECISE ? 2 : 4)))
+void prep_kernel_tail(SplitParams sp) {
+    __shared__ int next_item;
+    const int tid0 = threadIdx.x;
+    const unsigned x = xcd_id();
+    if (x >= kOvlXcds) {
+        if (tid0 == 0) ovl_error(sp.hdr, kHdrErrXcd, sp.epoch);
+        return;
+    }
+    const int Hk = sp.p.num_k_heads, gx = sp.p.batch * Hk / kOvlXcds;
+    const int items = gx * (sp.nseg - sp.n1);
+    uint64_t* ctr = sp.hdr + kHdrPrep + 32 * x;
+    if (tid0 == 0) next_item = (int)claim_next(ctr, sp.epoch);
+    __syncthreads();
+    int t = next_item;
+    while (t < items) {
+        // the thread index, opaque per item: the compiler cannot keep the
+        // body's per-lane addresses live across the loop
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        int nxt = 0;
+        if (tid0 == 0) nxt = (int)claim_next(ctr, sp.epoch);   // the next claim, during this item
+        const int c = sp.n1 + t / gx, grp = (int)x + kOvlXcds * (t % gx);
+        prep_body<NEUMANN, PRECISE>(sp, grp / Hk, grp / Hk, grp % Hk, c, tid);
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's record stores have completed
+        __syncthreads();                 // ... and every other thread's
+        if (tid0 == 0) {
+            __hip_atomic_store(sp.flags + (int64_t)grp * sp.frow + c, sp.epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            next_item = nxt;
+        }
+        __syncthreads();
+        t = next_item;
+    }
 }
 
 // Varlen: blockIdx = (entry i, key head, chunk j of the segment); entries
@@ -436,15 +531,18 @@ void prep_kernel_varlen(VarlenParams vp) {
     const int i = grp / vp.sp.p.num_k_heads, kh = grp % vp.sp.p.num_k_heads;
     const SplitParams sp = seq_view(vp, i, vp.b0 + i);
     if (j >= sp.nseg) return;
-    prep_body<NEUMANN, PRECISE>(sp, vp.b0 + i, i, kh, j);
+    prep_body<NEUMANN, PRECISE>(sp, vp.b0 + i, i, kh, j, threadIdx.x);
 }
 
 // ============================================================ state kernel
 // LDS pointer from a generic pointer into LDS by its low 32 bits (the LDS
 // offset): no address-space cast, whose null check costs a compare and a
 // select per copy
-#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(uintptr_t)(uint32_t)(uintptr_t)(x))
 
+// LDS pointer from a generic pointer into LDS by its low 32 bits (the LDS
+// offset): no address-space cast, whose null check costs a compare and a
+// select per copy
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(uintptr_t)(uint32_t)(uintptr_t)(x))
 
 // LDS buffer of one chunk: Q | K | P | AN | rows [| P_lo | AN_lo] | V^T (V^T
 // of the slice's columns, row stride kVtLd; the lo parts of P and AN in the
@@ -910,6 +1008,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Overlapped call: chunk cr's records are complete once its flag holds the
+// call's epoch.  `ready` holds the flag as loaded one step earlier; until it
+// matches, the wave polls.  A wait gives up after 0.1 s (the error word
+// kHdrErrWait, after which every wait of the call returns at once), so a
+// wave never waits without bound.
+__device__ __forceinline__ void await_chunk(const SplitParams& sp, const StateCtx& cx, int cr, uint64_t ready) {
+    wait_vm<0>();   // the flag load of the previous step has returned
+    if (__builtin_amdgcn_readfirstlane((uint32_t)(ready == sp.epoch))) return;
+    const uint64_t* f = sp.flags + (int64_t)(cx.rb * sp.p.num_k_heads + cx.kh) * sp.frow + cr;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.epoch) return;
+        if (__hip_atomic_load(sp.hdr + kHdrErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.epoch) return;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000u) {   // 100 MHz clock
+            ovl_error(sp.hdr, kHdrErrWait, sp.epoch);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+__device__ __forceinline__ uint64_t load_flag(const SplitParams& sp, const StateCtx& cx, int cr) {
+    asm volatile("" ::: "memory");   // issued after this step's record copies
+    return __hip_atomic_load(sp.flags + (int64_t)(cx.rb * sp.p.num_k_heads + cx.kh) * sp.frow + cr, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Memory wave M's step c, run while the compute waves work on chunk c - 1
 // (c = 0: before the first chunk).  It completes chunk c's buffer vbuf.  A
 // copy wave requests its pieces of chunk c + NB - 2 into rbuf and waits for
@@ -920,20 +1045,24 @@ __device__ __forceinline__ void lds_barrier() {
 // follows.
 template <int NW, int M, bool PRECISE>
 __device__ __forceinline__ void mem_step(const SplitParams& sp, const StateCtx& cx, const float* Wv, char* rbuf,
-                                          char* vbuf, char* slab, int c, int lane) {
+                                          char* vbuf, char* slab, int c, int lane, uint64_t& ready) {
     using SS = StateShape<NW, PRECISE>;
     constexpr int LO = SS::rec_lo(M), HI = SS::rec_hi(M), AHEAD = SS::NB - 2;
     if constexpr (!SS::is_v(M)) {
         const int cr = c + AHEAD;
         if (cr < sp.nseg) {
+            const bool ovl = sp.flags != nullptr;
+            if (ovl && cr >= sp.n1) await_chunk(sp, cx, cr, ready);
             const char* krec = key_rec(sp, cx.rb, cx.kh, cr);
             const char* vrec = val_rec(sp, cx.rb, cx.h, cr);
 #pragma unroll
             for (int pc = LO; pc < HI; ++pc) issue_piece<PRECISE>(rbuf, krec, vrec, pc, lane);
-            if constexpr (AHEAD > 0) {
+            if constexpr (AHEAD > 0)
                 wait_vm<HI - LO, true>();   // chunk c's pieces, requested one step earlier, have landed
-                return;
-            }
+            else
+                wait_vm<0, true>();
+            if (ovl && cr + 1 < sp.nseg && cr + 1 >= sp.n1) ready = load_flag(sp, cx, cr + 1);
+            return;
         }
         wait_vm<0, true>();
     } else {
@@ -991,6 +1120,7 @@ __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& 
     constexpr int PERIOD = NB == 3 ? 6 : 2;
     char* const bufs[3] = {buf0, buf1, buf2};
     char* const slabs[2] = {slab0, slab1};
+    uint64_t ready = 0;   // copy waves of an overlapped call: the next chunk's flag
     if constexpr (SS::is_v(M)) {
         const int64_t l0 = sp.k0 * kC - sp.p.start_pos;
 #pragma unroll
@@ -1009,14 +1139,14 @@ __device__ __forceinline__ void mem_role(const SplitParams& sp, const StateCtx& 
     }
     wait_vm<0>();
     __syncthreads();
-    mem_step<NW, M, PRECISE>(sp, cx, Wv, bufs[(NB - 2) % NB], buf0, slab0, 0, lane);
+    mem_step<NW, M, PRECISE>(sp, cx, Wv, bufs[(NB - 2) % NB], buf0, slab0, 0, lane, ready);
     __syncthreads();
     for (int c = 1; c <= sp.nseg; c += PERIOD) {
 #pragma unroll
         for (int i = 0; i < PERIOD; ++i) {
             if (c + i <= sp.nseg) {
                 mem_step<NW, M, PRECISE>(sp, cx, Wv, bufs[(1 + i + NB - 2) % NB], bufs[(1 + i) % NB],
-                                          slabs[(1 + i) % 2], c + i, lane);
+                                          slabs[(1 + i) % 2], c + i, lane, ready);
                 lds_barrier();
             }
         }
@@ -1068,7 +1198,26 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
         entries = p0.batch;
     }
     const int NG = entries * p0.num_k_heads;
-    const int bid = blockIdx.x;
+    int bid = blockIdx.x;
+    if constexpr (!VARLEN) {
+        if (kp.flags) {
+            // overlapped call: take the next of this XCD's (group, member)
+            // slots, groups g with g % 8 == XCD (those whose records the tail
+            // prep writes into this XCD's L2); the slot count per XCD equals
+            // the workgroups the round-robin dispatch puts there
+            __shared__ int claim;
+            if (tid == 0) {
+                const unsigned x = xcd_id();
+                const int share = NG / kOvlXcds * M;
+                const int sl = x < kOvlXcds ? (int)claim_next(kp.hdr + kHdrState + 32 * x, kp.epoch) : share;
+                if (sl >= share) ovl_error(kp.hdr, x < kOvlXcds ? kHdrErrClaim : kHdrErrXcd, kp.epoch);
+                claim = sl < share ? kOvlXcds * sl + (int)x : -1;
+            }
+            __syncthreads();
+            bid = claim;
+            if (bid < 0) return;
+        }
+    }
     const int grp = (bid / 8 / M) * 8 + bid % 8;
     const int member = (bid / 8) % M;
     if (grp >= NG) return;
@@ -1209,6 +1358,63 @@ hipError_t launch_state_varlen(const VarlenParams& vp, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <class KP>
+hipError_t launch_prep_any(const PrefillParams& p, const KP& kp, dim3 grid, hipStream_t stream);
+
+template <bool NEUMANN, bool PRECISE>
+hipError_t launch_tail(const SplitParams& sp, hipStream_t stream) {
+    hipLaunchKernelGGL((prep_kernel_tail<NEUMANN, PRECISE>), dim3(ovl_tail_blocks(PRECISE)), dim3(kPrepThreads), 0,
+                       stream, sp);
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_any(const SplitParams& sp, hipStream_t stream) {
+    if (sp.p.precise) return sp.p.diag_neumann ? launch_tail<true, true>(sp, stream) : launch_tail<false, true>(sp, stream);
+    return sp.p.diag_neumann ? launch_tail<true, false>(sp, stream) : launch_tail<false, false>(sp, stream);
+}
+
+// ---- overlapped calls.  Two library streams per device with disjoint CU
+// masks: 24 of the 32 CUs of every XCD run the head prep and the state
+// kernel, the other 8 the tail prep.  Bit i of a mask is CU i; under either
+// order of CUs over XCDs (32 consecutive CUs per XCD, or CU i on XCD i % 8)
+// the pattern (i / 8) % 4 splits every XCD 24 : 8, so the round-robin
+// dispatch finds CUs on every XCD.  (An unmasked dispatch does not place its
+// workgroups around a masked queue's: it waits for the CUs that queue holds,
+// so the state kernel needs a mask of its own.)
+struct OvlStreams {
+    bool tried = false, ok = false;
+    hipStream_t main = nullptr, tail = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kOvlMaxDevices = 64;
+std::mutex ovl_mutex;
+OvlStreams ovl_dev[kOvlMaxDevices];
+uint64_t ovl_epoch = 0;   // last epoch handed out (under ovl_mutex)
+
+// The streams of device `dev` (the current device; created on first use,
+// kept until the process ends), or null where the chip is not 8 XCDs of 32
+// CUs.  Call with ovl_mutex held.
+OvlStreams* ovl_streams(int dev) {
+    if (dev < 0 || dev >= kOvlMaxDevices) return nullptr;
+    OvlStreams& o = ovl_dev[dev];
+    if (!o.tried) {
+        o.tried = true;
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus != 256)
+            return nullptr;
+        uint32_t mm[8], mt[8];
+        for (int w = 0; w < 8; ++w) {
+            mm[w] = mt[w] = 0;
+            for (int bit = 0; bit < 32; ++bit) ((((32 * w + bit) / 8) % 4 == 3) ? mt[w] : mm[w]) |= 1u << bit;
+        }
+        o.ok = hipExtStreamCreateWithCUMask(&o.main, 8, mm) == hipSuccess &&
+               hipExtStreamCreateWithCUMask(&o.tail, 8, mt) == hipSuccess &&
+               hipEventCreateWithFlags(&o.fork, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&o.join, hipEventDisableTiming) == hipSuccess;
+    }
+    return o.ok ? &o : nullptr;
+}
+
 // prep launch for (Neumann diagonal solve, precise mode)
 template <class KP>
 hipError_t launch_prep_any(const PrefillParams& p, const KP& kp, dim3 grid, hipStream_t stream) {
@@ -1244,7 +1450,91 @@ uint64_t prefill_split_chunk_bytes(int batch, int num_k_heads, int num_v_heads, 
     return (uint64_t)batch * ((uint64_t)num_k_heads * kKeyRec + (uint64_t)num_v_heads * val_rec_bytes(precise));
 }
 
-hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream) {
+uint64_t prefill_overlap_bytes(int batch, int num_k_heads, int64_t chunks) {
+    return 8 * ((uint64_t)batch * num_k_heads * (uint64_t)((chunks + 31) / 32 * 32) + kOvlHdrWords);
+}
+
+namespace {
+
+// Chunks of an overlapped call that the head prep launch covers: enough that
+// the tail prep, on a quarter of the CUs, stays ahead of the state kernel.
+// GDN_PREFILL_OVERLAP_HEAD (a fraction) overrides the default.
+int64_t overlap_head(int64_t n) {
+    double f = 0.27;
+    if (const char* env = getenv("GDN_PREFILL_OVERLAP_HEAD")) {
+        const double v = atof(env);
+        if (v > 0.0 && v < 1.0) f = v;
+    }
+    int64_t n1 = (int64_t)std::ceil(f * (double)n);
+    if (n1 < 1) n1 = 1;
+    if (n1 > n - 1) n1 = n - 1;
+    return n1;
+}
+
+// One segment of n chunks with the tail of the prep concurrent with the head
+// prep and the state kernel (see SplitParams).  Both library streams wait for
+// the caller's stream to reach this call (earlier calls on it may still read
+// the workspace); the caller's stream then waits for the main stream's state
+// kernel, which cannot finish before every tail item has published its
+// records, the last thing a tail workgroup does.  The tail is persistent
+// (one workgroup per slot of its CUs), so no later dispatch waits behind
+// unplaced tail workgroups.  Returns hipErrorNotSupported, with nothing
+// enqueued, where the call does not qualify.
+hipError_t launch_overlapped(SplitParams sp, int64_t n, uint64_t per, uint64_t ws_bytes, hipStream_t stream) {
+    const PrefillParams& p = sp.p;
+    const char* env = getenv("GDN_PREFILL_OVERLAP");
+    if (env && env[0] == '0') return hipErrorNotSupported;
+    const bool forced = env && env[0] == '1';
+    const int64_t ng = (int64_t)p.batch * p.num_k_heads;
+    const int r = p.num_v_heads / p.num_k_heads;
+    // the state grid (24 workgroups per XCD at most, one per CU, beside the
+    // tail's 8) and the per-XCD shares must come out even; short calls gain
+    // nothing
+    if (state_waves(p) != 2 || ng % kOvlXcds != 0 || ng * r * StateShape<2>::SPLIT > 24 * kOvlXcds || n < 2 ||
+        (!forced && n < 64) || n > (1 << 20))
+        return hipErrorNotSupported;
+    if (ws_bytes < (uint64_t)n * per + prefill_overlap_bytes(p.batch, p.num_k_heads, n)) return hipErrorNotSupported;
+    // The tail stream is a blocking stream (the only kind a CU mask comes
+    // with): work on the NULL stream waits for it, so a call on the NULL
+    // (legacy) stream would run the tail alone before its head and state
+    // kernels.  Such calls, and calls being captured, take the serial path.
+    if (stream == nullptr || stream == hipStreamLegacy || stream == hipStreamPerThread) return hipErrorNotSupported;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return hipErrorNotSupported;
+    int dev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess || dev != cur)
+        return hipErrorNotSupported;
+    std::lock_guard<std::mutex> lock(ovl_mutex);
+    OvlStreams* o = ovl_streams(dev);
+    if (!o) return hipErrorNotSupported;
+    if (ovl_epoch == 0) {
+        // start from the clock, so that calls of different processes on one
+        // workspace are unlikely to share an epoch
+        ovl_epoch = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() & 0xffffffffffull;
+    }
+    ovl_epoch = ovl_epoch + 1 > 0xffffffffffull ? 1 : ovl_epoch + 1;
+    sp.epoch = ovl_epoch;
+    sp.frow = (int32_t)((n + 31) / 32 * 32);
+    sp.flags = reinterpret_cast<uint64_t*>(sp.ws + (uint64_t)n * per);
+    sp.hdr = sp.flags + ng * sp.frow;
+    sp.n1 = (int32_t)overlap_head(n);
+    sp.pj = sp.n1;
+    hipError_t e = hipEventRecord(o->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(o->tail, o->fork, 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(o->main, o->fork, 0);
+    if (e == hipSuccess) e = launch_prep_any(p, sp, dim3((unsigned)(ng * sp.n1)), o->main);
+    if (e == hipSuccess) e = launch_tail_any(sp, o->tail);
+    if (e == hipSuccess) e = p.precise ? launch_state<2, true>(sp, o->main) : launch_state<2, false>(sp, o->main);
+    if (e == hipSuccess) e = hipEventRecord(o->join, o->main);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, o->join, 0);
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_bytes, hipStream_t stream,
+                                bool allow_overlap) {
     if (p.batch == 0) return hipSuccess;
     const uint64_t per = prefill_split_chunk_bytes(p.batch, p.num_k_heads, p.num_v_heads, p.precise);
     const int64_t k_first = p.start_pos / kC;
@@ -1267,11 +1557,21 @@ hipError_t launch_prefill_split(const PrefillParams& p, void* ws, uint64_t ws_by
         return launch_state_any(sp, stream);
     }
     sp.rec_batch = p.batch;
+    if (allow_overlap && k_end - k_first <= max_seg) {
+        const int64_t n = k_end - k_first;
+        sp.k0 = k_first;
+        sp.nseg = (int32_t)n;
+        sp.rec_stride = (int32_t)n;
+        sp.last_seg = 1;
+        const hipError_t e = launch_overlapped(sp, n, per, ws_bytes, stream);
+        if (e != hipErrorNotSupported) return e;
+    }
     for (int64_t k0 = k_first; k0 < k_end; k0 += max_seg) {
         const int64_t n = k_end - k0 < max_seg ? k_end - k0 : max_seg;
         sp.k0 = k0;
         sp.nseg = (int32_t)n;
         sp.rec_stride = (int32_t)n;
+        sp.pj = (int32_t)n;
         sp.last_seg = k0 + n == k_end;
         const dim3 grid((unsigned)(p.batch * p.num_k_heads * n));
         hipError_t e = launch_prep_any(p, sp, grid, stream);

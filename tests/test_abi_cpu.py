@@ -86,11 +86,19 @@ def test_checkpoint_plan_errors(G):
     assert f(ctypes.byref(bad.c()), 0, 100, 64, None, 0, ctypes.byref(count), ctypes.byref(nb)) == G.GDN_EINVAL
 
 
+def overlap_bytes(B, Hk, chunks):
+    """Ready flags of the overlapped prep, one 8-byte word per (sequence, key
+    head, chunk) in rows rounded up to 32 words, and an 8 KiB header; only
+    where a call spans two chunks or more."""
+    return 8 * (B * Hk * -(-chunks // 32) * 32 + 1024) if chunks >= 2 else 0
+
+
 def test_workspace_bytes(G):
     """B x (chunks a call of L tokens can span, from any start) x per-chunk
-    records (H_k x (Q, K) + H_v x (P, AN, row scales)); P and AN keep the
-    first 32 columns of rows 0..31 and all of rows 32..63 (their lower 16x16
-    tiles, with two upper ones to keep rows 0..31 equal)."""
+    records (H_k x (Q, K) + H_v x (P, AN, row scales)), plus the overlap
+    flags; P and AN keep the first 32 columns of rows 0..31 and all of rows
+    32..63 (their lower 16x16 tiles, with two upper ones to keep rows 0..31
+    equal)."""
     for B, Hk, Hv in ((1, 16, 48), (8, 16, 32), (2, 2, 6)):
         lower = 32 * 64 + 32 * 128      # rows 0..31 keep 32 columns, rows 32..63 all 64
         per = B * (Hk * 2 * 64 * 128 * 2 + Hv * (2 * lower + 5 * 64 * 4))
@@ -98,8 +106,8 @@ def test_workspace_bytes(G):
         for L in (0, 1, 2, 63, 64, 65, 127, 128, 16384):
             # brute force over the start offset inside a chunk
             span = max((((s + L - 1) // 64) - s // 64 + 1) if L else 0 for s in range(64))
-            assert G.prefill_workspace_bytes(c, L) == span * per, (B, Hk, Hv, L)
-    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 13568)
+            assert G.prefill_workspace_bytes(c, L) == span * per + overlap_bytes(B, Hk, span), (B, Hk, Hv, L)
+    assert G.prefill_workspace_bytes(cfg(G), 16384) == 257 * (16 * 32768 + 48 * 13568) + 8 * (16 * 288 + 1024)
 
 
 def test_workspace_bytes_precise(G):
@@ -107,7 +115,8 @@ def test_workspace_bytes_precise(G):
     (two more 6144-byte triangles) and pads the row scales to 2 KiB: 26624
     bytes per value head and chunk; key records are unchanged."""
     c = cfg(G, precision=G.GDN_PRECISION_HILO)
-    assert G.prefill_workspace_bytes(c, 16384) == 257 * (16 * 32768 + 48 * (2 * 6144 + 2048 + 2 * 6144))
+    assert G.prefill_workspace_bytes(c, 16384) == (257 * (16 * 32768 + 48 * (2 * 6144 + 2048 + 2 * 6144))
+                                                   + overlap_bytes(1, 16, 257))
     for L in (1, 64, 65, 1000):
         assert G.prefill_workspace_bytes(c, L) > G.prefill_workspace_bytes(cfg(G), L)
     for p in (-1, 2, 7):
