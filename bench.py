@@ -111,6 +111,24 @@ def time_events(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3 / steps   # seconds per call
 
 
+def settle_clocks(fn, seconds):
+    """Untimed calls of fn for `seconds` of wall time, before the warm-up
+    calls: the process starts with the GPU idle, and its clocks take longer
+    than a few calls to come up (the 16k prefill ran at 0.500 ms per call
+    after 5 untimed calls and at 0.464 ms after 200).  Returns the calls made."""
+    import torch
+    n = 0
+    if seconds <= 0:
+        return n
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def bench_prefill(args):
     """The prefill call as a serving loop makes it for this shape: on a stream
     of its own, with a workspace (allocated once, outside the timed region),
@@ -137,6 +155,7 @@ def bench_prefill(args):
     side.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
+        settle = settle_clocks(lambda: step(ws), args.settle)
         t = time_events(lambda: step(ws), args.steps, args.warmup)
     t_null = time_events(lambda: step(ws), max(2, args.steps // 2), 2)
     t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
@@ -157,7 +176,7 @@ def bench_prefill(args):
     tokens = w.batch * w.seq_len
     flops = prefill_flops_per_token_head() * tokens * w.num_v_heads
     byts = prefill_bytes(w.batch, w.seq_len, w.num_k_heads, w.num_v_heads)
-    return w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws.numel()
+    return w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws.numel(), settle
 
 
 def bench_decode(args):
@@ -493,6 +512,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed calls before each timed region (the clocks settle within them)")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed prefill calls before the first warm-up call (the GPU starts idle)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -533,9 +554,12 @@ def main():
     inp = None
     if "prefill" in sections:
         print("bench: prefill", file=sys.stderr, flush=True)
-        w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes = bench_prefill(args)
+        w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes, settled = bench_prefill(args)
         achieved = flops / t
         rec.update({
+            "clock_settle": {"seconds": args.settle, "calls": settled,
+                             "what": "untimed calls of the same prefill before the warm-up calls, so that the "
+                                     "timed calls run at the clocks a busy serving loop holds"},
             "value": tokens / t,
             "ms_per_step": t * 1e3,
             "config": {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill", "batch": w.batch,

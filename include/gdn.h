@@ -200,8 +200,13 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
  * CU masks (24 and 8 CUs of every XCD), forked from `stream` at the call and
  * joined back into it at the end; the results are bit for bit those of the
  * serial path.  The library streams are blocking streams: work the caller
- * puts on the NULL stream meanwhile waits for them.  GDN_PREFILL_OVERLAP=0
- * turns this off, =1 takes it from 2 chunks on. */
+ * puts on the NULL stream meanwhile waits for them.  The state kernel waits
+ * for each later chunk's records with a bound of 2 s: if the concurrent prep
+ * cannot run that long (its CUs held by other work), the call fails loudly
+ * rather than returning wrong values: rec_state_out and every out row of the
+ * call are NaN (checkpoint slots it wrote are then invalid too), and the
+ * caller's stream sees no error code.  GDN_PREFILL_OVERLAP=0 turns the
+ * overlap off, =1 takes it from 2 chunks on. */
 gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
                                const void* qkv, const void* a, const void* b, const void* conv_w,
                                const float* A_log, const float* dt_bias,

@@ -111,6 +111,7 @@ struct SplitParams {
     uint64_t epoch;      // this call's tag, never 0
     int32_t frow;        // flag words per row (a multiple of 32)
     int32_t n1;
+    uint64_t wait_ticks; // bound of one wait, in ticks of the 100 MHz s_memrealtime clock
 };
 
 // ---- overlap header (64-bit word offsets; each XCD's counter on a 256-byte
@@ -1010,9 +1011,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Overlapped call: chunk cr's records are complete once its flag holds the
 // call's epoch.  `ready` holds the flag as loaded one step earlier; until it
-// matches, the wave polls.  A wait gives up after 0.1 s (the error word
+// matches, the wave polls.  A wait gives up after 2 s (the error word
 // kHdrErrWait, after which every wait of the call returns at once), so a
-// wave never waits without bound.
+// wave never waits without bound; the compute waves then poison their
+// slice of the call's outputs (ovl_failed).
 __device__ __forceinline__ void await_chunk(const SplitParams& sp, const StateCtx& cx, int cr, uint64_t ready) {
     wait_vm<0>();   // the flag load of the previous step has returned
     if (__builtin_amdgcn_readfirstlane((uint32_t)(ready == sp.epoch))) return;
@@ -1021,12 +1023,23 @@ __device__ __forceinline__ void await_chunk(const SplitParams& sp, const StateCt
     for (;;) {
         if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.epoch) return;
         if (__hip_atomic_load(sp.hdr + kHdrErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.epoch) return;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000u) {   // 100 MHz clock
+        if (__builtin_amdgcn_s_memrealtime() - t0 > sp.wait_ticks) {
             ovl_error(sp.hdr, kHdrErrWait, sp.epoch);
             return;
         }
         __builtin_amdgcn_s_sleep(8);
     }
+}
+
+// Whether an overlapped call met an error (a wait that timed out, or a
+// workgroup placed outside its XCD's share): its outputs cannot be trusted
+__device__ __forceinline__ bool ovl_failed(const SplitParams& sp) {
+    if (!sp.flags) return false;
+    bool bad = false;
+#pragma unroll
+    for (int w : {kHdrErrXcd, kHdrErrClaim, kHdrErrWait})
+        bad |= __hip_atomic_load(sp.hdr + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.epoch;
+    return bad;
 }
 
 __device__ __forceinline__ uint64_t load_flag(const SplitParams& sp, const StateCtx& cx, int cr) {
@@ -1288,6 +1301,24 @@ __global__ __launch_bounds__(512) void state_kernel(KP kp) {
             }
         }
         if (sp.nseg > 0) store_o(p, obase, Ob, sp.k0 + sp.nseg - 1, li);
+        // an overlapped call whose prep did not keep up (its CUs held by
+        // other work for the whole wait bound) computed from records that
+        // were not complete: it fails loudly, with NaN in this wave's
+        // columns of every output row of the segment and of the final state
+        if (__builtin_amdgcn_readfirstlane((uint32_t)ovl_failed(sp))) {
+            __builtin_amdgcn_s_waitcnt(0);
+            const int64_t t_lo = std::max<int64_t>(sp.k0 * kC - p.start_pos, 0);
+            const int64_t t_hi = std::min<int64_t>((sp.k0 + sp.nseg) * kC - p.start_pos, p.seq_len);
+            uint16_t* ocol = static_cast<uint16_t*>(p.out) + ((int64_t)cx.b * p.seq_len * p.num_v_heads + cx.h) * kD +
+                             cx.zcol0 + 16 * wave + 4 * (lane % 4);
+            const bf16x4 qnan = {(__bf16)__builtin_nanf(""), (__bf16)__builtin_nanf(""), (__bf16)__builtin_nanf(""),
+                                 (__bf16)__builtin_nanf("")};
+            for (int64_t t = t_lo + lane / 4; t < t_hi; t += 16)
+                *reinterpret_cast<bf16x4*>(ocol + t * p.num_v_heads * kD) = qnan;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) S[t] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                     __builtin_nanf("")};
+        }
         const int64_t sb = opaque(cx.s_base);
         const int64_t lq4 = opaque(4 * lq);   // the offsets of the state load are not kept across the loop
 #pragma unroll
@@ -1520,11 +1551,22 @@ hipError_t launch_overlapped(SplitParams sp, int64_t n, uint64_t per, uint64_t w
     sp.hdr = sp.flags + ng * sp.frow;
     sp.n1 = (int32_t)overlap_head(n);
     sp.pj = sp.n1;
+    // 2 s by default; GDN_PREFILL_OVERLAP_WAIT_US sets another bound (tests)
+    sp.wait_ticks = 200000000ull;
+    if (const char* w = getenv("GDN_PREFILL_OVERLAP_WAIT_US")) {
+        const long long us = atoll(w);
+        if (us > 0) sp.wait_ticks = (uint64_t)us * 100;
+    }
+    // GDN_PREFILL_OVERLAP_SKIP_TAIL=1 leaves the tail prep out, so that its
+    // chunks are never published: a test of the failure path (every wait
+    // runs into its bound, the outputs come back NaN)
+    const char* skip = getenv("GDN_PREFILL_OVERLAP_SKIP_TAIL");
+    const bool skip_tail = skip && skip[0] == '1';
     hipError_t e = hipEventRecord(o->fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(o->tail, o->fork, 0);
     if (e == hipSuccess) e = hipStreamWaitEvent(o->main, o->fork, 0);
     if (e == hipSuccess) e = launch_prep_any(p, sp, dim3((unsigned)(ng * sp.n1)), o->main);
-    if (e == hipSuccess) e = launch_tail_any(sp, o->tail);
+    if (e == hipSuccess && !skip_tail) e = launch_tail_any(sp, o->tail);
     if (e == hipSuccess) e = p.precise ? launch_state<2, true>(sp, o->main) : launch_state<2, false>(sp, o->main);
     if (e == hipSuccess) e = hipEventRecord(o->join, o->main);
     if (e == hipSuccess) e = hipStreamWaitEvent(stream, o->join, 0);

@@ -182,3 +182,31 @@ def test_null_stream_takes_serial_path(G):
     b = run(G, w, d, torch.zeros_like(ws), overlap=0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_overlap_starved_prep_fails_loudly(G):
+    """The failure path of the overlap, forced from the host: with the tail
+    prep left out (GDN_PREFILL_OVERLAP_SKIP_TAIL=1, so its chunks are never
+    published) and a 200 us wait bound, the first wait for a tail chunk runs
+    into its bound and every later wait returns at once; the wait error word
+    holds the call's epoch and the call's final state and every output row
+    come back NaN.  The next call on the same workspace, with its prep, is
+    bit for bit the serial one."""
+    w = I.Workload("ovl starved", batch=1, seq_len=1000, num_k_heads=8, num_v_heads=24, init_state=True, seed=207)
+    inp = I.generate(w)
+    d = to_dev(inp)
+    c = cfg_of(G, w)
+    ws = torch.zeros(G.prefill_workspace_bytes(c, w.seq_len), dtype=torch.uint8, device="cuda")
+    with env(GDN_PREFILL_OVERLAP_SKIP_TAIL=1, GDN_PREFILL_OVERLAP_WAIT_US=200):
+        out, conv, S = run(G, w, d, ws, overlap=1)
+    assert bool(torch.isnan(S).all()), "final state not poisoned"
+    assert bool(torch.isnan(out.float()).all()), "output rows not poisoned"
+    n, n1, off, frow = layout(G, c, w, 0, w.seq_len)
+    ng = w.batch * w.num_k_heads
+    hdr = ws[off:off + 8 * (ng * frow + 1024)].view(torch.int64).cpu()[ng * frow:]
+    assert int(hdr[576]) != 0, "wait error word not set"
+    a = run(G, w, d, ws, overlap=1)
+    check_flags(G, c, w, ws, 0, w.seq_len, 0.27)
+    b = run(G, w, d, torch.zeros_like(ws), overlap=0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
