@@ -1489,9 +1489,12 @@ namespace {
 
 // Chunks of an overlapped call that the head prep launch covers: enough that
 // the tail prep, on a quarter of the CUs, stays ahead of the state kernel.
-// GDN_PREFILL_OVERLAP_HEAD (a fraction) overrides the default.
-int64_t overlap_head(int64_t n) {
-    double f = 0.27;
+// A quarter of the chunks in the default precision; 30% in the precise mode,
+// whose tail holds one prep workgroup per CU instead of two (both measured
+// best on the 16k prefill).  GDN_PREFILL_OVERLAP_HEAD (a fraction)
+// overrides the default.
+int64_t overlap_head(int64_t n, bool precise) {
+    double f = precise ? 0.30 : 0.25;
     if (const char* env = getenv("GDN_PREFILL_OVERLAP_HEAD")) {
         const double v = atof(env);
         if (v > 0.0 && v < 1.0) f = v;
@@ -1549,7 +1552,7 @@ hipError_t launch_overlapped(SplitParams sp, int64_t n, uint64_t per, uint64_t w
     sp.frow = (int32_t)((n + 31) / 32 * 32);
     sp.flags = reinterpret_cast<uint64_t*>(sp.ws + (uint64_t)n * per);
     sp.hdr = sp.flags + ng * sp.frow;
-    sp.n1 = (int32_t)overlap_head(n);
+    sp.n1 = (int32_t)overlap_head(n, p.precise);
     sp.pj = sp.n1;
     // 2 s by default; GDN_PREFILL_OVERLAP_WAIT_US sets another bound (tests)
     sp.wait_ticks = 200000000ull;
