@@ -583,6 +583,24 @@ def test_workload_qwen36_prefill_256k_checkpoints(G):
         assert worst <= TOL_BF16_STATE
 
     check_run("256k two-pass", out, conv, S, buf)
+    # the same call on a created stream takes the overlapped prep (head chunks
+    # first, the rest beside the state kernel): bit for bit the serial run,
+    # checkpoint slots included
+    print("[256k] GPU prefill, two-pass path with the overlapped prep (side stream)", flush=True)
+    buf_o = torch.zeros_like(buf)
+    ws = torch.zeros(G.prefill_workspace_bytes(c, w.seq_len), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out_o, conv_o, S_o = gpu_prefill(G, w, d, ckpt_interval=4096, ckpt_buf=buf_o, workspace=ws)
+    torch.cuda.synchronize()
+    n = w.seq_len // 64
+    per = G.prefill_workspace_bytes(c, 1)
+    flags = ws[n * per:n * per + 8 * w.num_k_heads * n].view(torch.int64).view(w.num_k_heads, n)
+    assert bool((flags[:, n - 1] != 0).all()), "the tail prep did not publish the last chunk"
+    assert torch.equal(out_o, out) and torch.equal(conv_o, conv) and torch.equal(S_o, S)
+    assert torch.equal(buf_o, buf), "checkpoint slots differ between the overlapped and the serial run"
+    del out_o, conv_o, S_o, buf_o, ws, flags
     print("[256k] GPU prefill, fused path", flush=True)
     buf_f = torch.zeros_like(buf)
     out_f, conv_f, S_f = gpu_prefill(G, w, d, ckpt_interval=4096, ckpt_buf=buf_f, path="fused")
