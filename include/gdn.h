@@ -203,9 +203,11 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_config* cfg, int64_t seq_len, u
  * puts on the NULL stream meanwhile waits for them.  The state kernel waits
  * for each later chunk's records with a bound of 2 s: if the concurrent prep
  * cannot run that long (its CUs held by other work), the call fails loudly
- * rather than returning wrong values: rec_state_out and every out row of the
- * call are NaN (checkpoint slots it wrote are then invalid too), and the
- * caller's stream sees no error code.  GDN_PREFILL_OVERLAP=0 turns the
+ * rather than returning wrong values: every state workgroup that met the
+ * timeout or started waiting after it writes NaN into its columns of
+ * rec_state_out and of every out row of the call, so the final state of at
+ * least the affected heads is NaN (the checkpoint slots the call wrote are
+ * then invalid too); the caller's stream sees no error code.  GDN_PREFILL_OVERLAP=0 turns the
  * overlap off, =1 takes it from 2 chunks on. */
 gdn_status gdn_prefill_chunked(const gdn_config* cfg, int64_t seq_len, int64_t start_pos,
                                const void* qkv, const void* a, const void* b, const void* conv_w,

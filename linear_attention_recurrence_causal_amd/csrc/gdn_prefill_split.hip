@@ -1415,7 +1415,7 @@ hipError_t launch_tail_any(const SplitParams& sp, hipStream_t stream) {
 struct OvlStreams {
     bool tried = false, ok = false;
     hipStream_t main = nullptr, tail = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, join_tail = nullptr;
 };
 constexpr int kOvlMaxDevices = 64;
 std::mutex ovl_mutex;
@@ -1441,7 +1441,8 @@ OvlStreams* ovl_streams(int dev) {
         o.ok = hipExtStreamCreateWithCUMask(&o.main, 8, mm) == hipSuccess &&
                hipExtStreamCreateWithCUMask(&o.tail, 8, mt) == hipSuccess &&
                hipEventCreateWithFlags(&o.fork, hipEventDisableTiming) == hipSuccess &&
-               hipEventCreateWithFlags(&o.join, hipEventDisableTiming) == hipSuccess;
+               hipEventCreateWithFlags(&o.join, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&o.join_tail, hipEventDisableTiming) == hipSuccess;
     }
     return o.ok ? &o : nullptr;
 }
@@ -1508,12 +1509,11 @@ int64_t overlap_head(int64_t n, bool precise) {
 // One segment of n chunks with the tail of the prep concurrent with the head
 // prep and the state kernel (see SplitParams).  Both library streams wait for
 // the caller's stream to reach this call (earlier calls on it may still read
-// the workspace); the caller's stream then waits for the main stream's state
-// kernel, which cannot finish before every tail item has published its
-// records, the last thing a tail workgroup does.  The tail is persistent
-// (one workgroup per slot of its CUs), so no later dispatch waits behind
-// unplaced tail workgroups.  Returns hipErrorNotSupported, with nothing
-// enqueued, where the call does not qualify.
+// the workspace); the caller's stream then waits for both library streams.
+// The tail is persistent (one workgroup per slot of its CUs), so no later
+// dispatch waits behind unplaced tail workgroups.  Returns
+// hipErrorNotSupported, with nothing enqueued, where the call does not
+// qualify.
 hipError_t launch_overlapped(SplitParams sp, int64_t n, uint64_t per, uint64_t ws_bytes, hipStream_t stream) {
     const PrefillParams& p = sp.p;
     const char* env = getenv("GDN_PREFILL_OVERLAP");
@@ -1566,14 +1566,22 @@ hipError_t launch_overlapped(SplitParams sp, int64_t n, uint64_t per, uint64_t w
     const char* skip = getenv("GDN_PREFILL_OVERLAP_SKIP_TAIL");
     const bool skip_tail = skip && skip[0] == '1';
     hipError_t e = hipEventRecord(o->fork, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(o->tail, o->fork, 0);
+    if (e != hipSuccess) return e;   // nothing enqueued
+    e = hipStreamWaitEvent(o->tail, o->fork, 0);
     if (e == hipSuccess) e = hipStreamWaitEvent(o->main, o->fork, 0);
     if (e == hipSuccess) e = launch_prep_any(p, sp, dim3((unsigned)(ng * sp.n1)), o->main);
     if (e == hipSuccess && !skip_tail) e = launch_tail_any(sp, o->tail);
     if (e == hipSuccess) e = p.precise ? launch_state<2, true>(sp, o->main) : launch_state<2, false>(sp, o->main);
-    if (e == hipSuccess) e = hipEventRecord(o->join, o->main);
-    if (e == hipSuccess) e = hipStreamWaitEvent(stream, o->join, 0);
-    return e;
+    // Join both library streams back into the caller's stream, after a failed
+    // launch too: whatever the call enqueued is then ordered before the
+    // caller's later work.  The tail stream is joined as well as the main
+    // one: a tail workgroup dispatched late (its CUs held by other work) may
+    // still claim from the workspace header after the state kernel is done.
+    hipError_t j = hipEventRecord(o->join, o->main);
+    if (j == hipSuccess) j = hipStreamWaitEvent(stream, o->join, 0);
+    if (j == hipSuccess) j = hipEventRecord(o->join_tail, o->tail);
+    if (j == hipSuccess) j = hipStreamWaitEvent(stream, o->join_tail, 0);
+    return e != hipSuccess ? e : j;
 }
 
 }  // namespace
