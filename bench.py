@@ -96,8 +96,16 @@ DECODE_SOURCES = ("gdn_decode.hip",)
 GATE_SOURCES = ("gdn_gate.hip",)
 
 
+# seconds of untimed calls before each timed region (set from --settle), and
+# the calls that made it for the headline region
+SETTLE = {"seconds": 0.0, "headline_calls": None}
+
+
 def time_events(fn, steps, warmup):
     import torch
+    calls = settle_clocks(fn, SETTLE["seconds"])
+    if SETTLE["headline_calls"] is None:
+        SETTLE["headline_calls"] = calls
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -112,10 +120,12 @@ def time_events(fn, steps, warmup):
 
 
 def settle_clocks(fn, seconds):
-    """Untimed calls of fn for `seconds` of wall time, before the warm-up
-    calls: the process starts with the GPU idle, and its clocks take longer
-    than a few calls to come up (the 16k prefill ran at 0.500 ms per call
-    after 5 untimed calls and at 0.464 ms after 200).  Returns the calls made."""
+    """Untimed calls of fn for `seconds` of wall time, before a timed region's
+    warm-up calls: the GPU idles while a section generates its inputs on the
+    CPU, and its clocks take longer than a few calls to come back (the 16k
+    prefill ran at 0.500 ms per call after 5 untimed calls and at 0.464 ms
+    after 200; the Coder-Next prefill at 0.61 ms after 5 and 0.52 ms after
+    50).  Returns the calls made."""
     import torch
     n = 0
     if seconds <= 0:
@@ -155,8 +165,8 @@ def bench_prefill(args):
     side.wait_stream(torch.cuda.current_stream())
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        settle = settle_clocks(lambda: step(ws), args.settle)
         t = time_events(lambda: step(ws), args.steps, args.warmup)
+    settle = SETTLE["headline_calls"]
     t_null = time_events(lambda: step(ws), max(2, args.steps // 2), 2)
     t_fused = time_events(lambda: step(None), max(2, args.steps // 4), 1)
     # the precise mode (bf16 hi + lo on the solve's and P Delta's products), both paths
@@ -524,6 +534,7 @@ def main():
                     help="also run a plain 1 GiB fp32 elementwise copy (read 1 GiB, write 1 GiB) "
                          "three times, the reference for scaling HBM byte counters")
     args = ap.parse_args()
+    SETTLE["seconds"] = args.settle
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the GDN core shards by (sequence, head) with no "
@@ -557,9 +568,10 @@ def main():
         w, t, t_null, t_fused, (t_p, t_pf), tokens, flops, byts, inp, ws_bytes, settled = bench_prefill(args)
         achieved = flops / t
         rec.update({
-            "clock_settle": {"seconds": args.settle, "calls": settled,
-                             "what": "untimed calls of the same prefill before the warm-up calls, so that the "
-                                     "timed calls run at the clocks a busy serving loop holds"},
+            "clock_settle": {"seconds": args.settle, "headline_calls": settled,
+                             "what": "before every timed region, untimed calls of the same call for this many "
+                                     "seconds, then the warm-up calls, so that the timed calls run at the clocks "
+                                     "a busy serving loop holds (headline_calls: those of the headline region)"},
             "value": tokens / t,
             "ms_per_step": t * 1e3,
             "config": {"workload": "Qwen3.6-27B-shaped GDN layer chunked prefill", "batch": w.batch,
