@@ -218,3 +218,33 @@ def test_overlap_starved_prep_fails_loudly(G):
     b = run(G, w, d, torch.zeros_like(ws), overlap=0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_overlap_two_streams_in_flight(G):
+    """Two overlapped calls on two created streams, enqueued back to back with
+    no synchronisation between them (each with its own workspace), share the
+    library's two streams: each must come out bit for bit equal to its serial
+    run, and each workspace's flags must carry its own call's epoch."""
+    w1 = I.Workload("ovl pair a", batch=1, seq_len=1000, num_k_heads=8, num_v_heads=24, init_state=True, seed=211)
+    w2 = I.Workload("ovl pair b", batch=1, seq_len=1000, num_k_heads=8, num_v_heads=24, init_state=True, seed=212)
+    ins = [I.generate(w) for w in (w1, w2)]
+    ds = [to_dev(x) for x in ins]
+    cs = [cfg_of(G, w) for w in (w1, w2)]
+    wss = [torch.zeros(G.prefill_workspace_bytes(c, w.seq_len), dtype=torch.uint8, device="cuda")
+           for c, w in zip(cs, (w1, w2))]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    res = []
+    with env(GDN_PREFILL_OVERLAP=1, GDN_PREFILL_STATE_WAVES=2):
+        for w, d, ws, s in zip((w1, w2), ds, wss, streams):
+            with torch.cuda.stream(s):
+                c = cfg_of(G, w)
+                res.append(G.prefill_chunked(c, d["qkv"], d["a"], d["b"], d["conv_w"], d["A_log"], d["dt_bias"],
+                                             d["conv_state"], d["rec_state"], workspace=ws))
+    torch.cuda.synchronize()
+    for (w, d, ws, c, r) in zip((w1, w2), ds, wss, cs, res):
+        check_flags(G, c, w, ws, 0, w.seq_len, None)
+        b = run(G, w, d, torch.zeros_like(ws), overlap=0)
+        for x, y in zip(r, b):
+            assert torch.equal(x, y), w.name
