@@ -20,7 +20,12 @@ from the states it produced, and the 262,144-token Qwen3.6-27B-shaped prefill
 that writes 64 checkpoint slots (one per 4096 tokens).  The precise mode
 (bf16 hi + lo operands) is timed on the 16k prefill beside the default.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only SECTIONS]
+Before every timed region the same call runs untimed for --settle seconds
+(default 0.3: the GPU idles while a section generates its inputs on the CPU,
+and its clocks take longer than a few calls to come back), then W warm-up
+calls, then K timed calls; the JSON line reports the settle as clock_settle.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--only SECTIONS]
 """
 from __future__ import annotations
 
