@@ -297,6 +297,37 @@ def test_prefill_then_decode(G, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_decode_stepped_equals_chunked_prefill(G, path):
+    """GPU against GPU on the same tokens: 200 one-token decode steps from
+    the initial states, and one chunked prefill over the 200 tokens.  The two
+    evaluate the same rule in different orders (per token in fp32; per chunk
+    on bf16 operands), so they agree within the bf16 bars (every 64-token
+    run, every head's state); the conv tails are copies of the same inputs,
+    bit for bit."""
+    w = small(seq_len=200, init_state=True, seed=31)
+    inp = I.generate(w)
+    d = to_dev(inp)
+    out_p, conv_p, S_p = gpu_prefill(G, w, d, path=path)
+    c = cfg_of(G, w)
+    conv, S = d["conv_state"], d["rec_state"]
+    outs = []
+    for t in range(w.seq_len):
+        o, conv, S = G.decode_step(c, d["qkv"][:, t].contiguous(), d["a"][:, t].contiguous(),
+                                   d["b"][:, t].contiguous(), d["conv_w"], d["A_log"], d["dt_bias"], conv, S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    out_d = torch.stack(outs, 1)
+    assert torch.equal(conv_p, conv), "conv tails differ"
+    e_run = local_rel(out_p.double().cpu().numpy(), out_d.double().cpu().numpy())
+    e_out = rel(out_p.double().cpu().numpy(), out_d.double().cpu().numpy())
+    e_st = state_rel_per_head(S_p.double().cpu().numpy(), S.double().cpu().numpy())
+    print(f"[stepped vs chunked {path}] out rel {e_out:.3e}, worst 64-token run {e_run:.3e}, "
+          f"worst head state {e_st:.3e}", flush=True)
+    assert finite(out_p) and finite(out_d)
+    assert e_run <= TOL_BF16_OUT and e_st <= TOL_BF16_STATE
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("stress", ["slowdecay", "extreme"])
 def test_prefill_stress(G, path, stress):
     """Not among the five workloads, held to the same bars: long
