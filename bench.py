@@ -51,10 +51,12 @@ def prefill_flops_per_token_head(C=64, d=128) -> float:
     return (C * (C - 1) * d + 4 * C * (C + 1) * d + 6 * C * d * d + C ** 3 / 3) / C
 
 
-def prefill_bytes(B, L, Hk, Hv, d=128) -> int:
-    """Fused-path HBM floor: read qkv, a, b, write o, read/write the state."""
+def prefill_bytes(B, L, Hk, Hv, d=128, state_in=False) -> int:
+    """Fused-path HBM floor: read qkv, a, b, write o and the final recurrent
+    state and conv tail; with state_in, also read the initial ones."""
     conv_dim = 2 * Hk * d + Hv * d
-    return B * L * (conv_dim * 2 + Hv * 2 * 2 + Hv * d * 2) + 2 * B * Hv * d * d * 4
+    states = B * (Hv * d * d * 4 + conv_dim * 3 * 2)
+    return B * L * (conv_dim * 2 + Hv * 2 * 2 + Hv * d * 2) + (2 if state_in else 1) * states
 
 
 def varlen_bytes(tokens, B, Hk, Hv, d=128) -> int:
